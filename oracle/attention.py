@@ -1,0 +1,98 @@
+"""Exact decode attention over the dequantized paged cache, and the split/merge
+(log-sum-exp) algebra.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+Decode attention (one query token per sequence) is the step whose memory
+traffic the 4-bit cache shrinks ([UQ] "這篇論文在解什麼痛點": KV cache fills
+HBM; "方法怎麼做，白話講": decode reads the compressed cache; [TQ-AMD]
+section 1: the aim is smaller KV with throughput kept).  The pages state no
+formula; the reading is standard softmax attention:
+
+  o[b, h] = sum_{t < T_b} softmax_t( scale * <q~[b,h], k_hat[b, h // g, t]> ) v_hat[b, h // g, t]
+
+* g = Hq / Hkv, query head h uses kv-head h // g (contiguous grouping);
+* keys are compared in the rotated domain: q~ = H_D q in fp64 for TQ4/4 (the
+  rotation is orthonormal, so this equals q . k for unrotated keys);
+  for MX-FP4 q~ is the query's own e4m3 code value (the rotated query as the
+  kernels store it);
+* T_b = 0 gives a zero row; no other mask (the new token is already cached).
+
+All arithmetic is fp64.  Pinned by tests/test_oracle_attention.py: weights sum
+to 1, brute-force loops on tiny inputs, T = 1, equal logits, merge of any
+partition equals the single pass, GQA with g = 1 equals per-head MHA, block
+table permutation invariance.
+"""
+import numpy as np
+
+from . import fpformats as fp
+from . import mxfp4, paged, wht
+
+
+def softmax_attention(q_rot, k_rot, v, scale):
+    """One query row against T cached rows, fp64.  Returns (o, weights)."""
+    q_rot = np.asarray(q_rot, dtype=np.float64)
+    k_rot = np.asarray(k_rot, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if k_rot.shape[0] == 0:
+        return np.zeros(v.shape[-1]), np.zeros(0)
+    logits = scale * (k_rot @ q_rot)
+    m = logits.max()
+    w = np.exp(logits - m)
+    w = w / w.sum()
+    return w @ v, w
+
+
+def decode(pool, q, block_table, context_lens, scale, rows=None):
+    """Decode attention for every (b, h) (or only ``rows``, a list of (b, h)).
+
+    ``pool`` is a ``paged.PagedPool``; ``q`` fp32 [B, Hq, D] holding bf16
+    values.  Returns fp64 [B, Hq, D] (rows not requested are NaN)."""
+    q = np.asarray(q, dtype=np.float32)
+    bsz, hq, d = q.shape
+    if hq % pool.hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    g = hq // pool.hkv
+    out = np.full((bsz, hq, d), np.nan)
+    want = rows if rows is not None else [(b, h) for b in range(bsz) for h in range(hq)]
+    cache = {}
+    for b, h in want:
+        kvh = h // g
+        key = (b, kvh)
+        if key not in cache:
+            cache[key] = pool.sequence_tokens(block_table[b], int(context_lens[b]), kvh)
+        k_rot, v_hat = cache[key]
+        out[b, h] = softmax_attention(rotated_query(pool, q[b, h]), k_rot, v_hat, scale)[0]
+    return out
+
+
+def rotated_query(pool, qrow):
+    if pool.fmt == paged.FORMAT_TQ4:
+        return wht.wht_f64(qrow)
+    return fp.e4m3_decode(mxfp4.query_fp8(qrow))
+
+
+# --- split / merge -----------------------------------------------------------
+
+def partial_state(logits, v):
+    """(m, l, acc) of one chunk: m = max logit, l = sum exp(logit - m),
+    acc = sum exp(logit - m) v.  An empty chunk is (-inf, 0, 0)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if logits.size == 0:
+        return -np.inf, 0.0, np.zeros(v.shape[-1])
+    m = logits.max()
+    e = np.exp(logits - m)
+    return m, e.sum(), e @ v
+
+
+def merge(states):
+    """Combine chunk states: M = max m_i, o = sum e^{m_i-M} acc_i / sum e^{m_i-M} l_i."""
+    ms = np.array([s[0] for s in states], dtype=np.float64)
+    if np.all(np.isneginf(ms)):
+        return np.zeros(len(states[0][2]))
+    big = ms.max()
+    wts = np.where(np.isneginf(ms), 0.0, np.exp(ms - big))
+    num = sum(w * s[2] for w, s in zip(wts, states))
+    den = sum(w * s[1] for w, s in zip(wts, states))
+    return num / den

@@ -1,0 +1,99 @@
+"""Pins for oracle.layout: hand bytes, bijections, round trips."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout
+
+HERE = os.path.dirname(__file__)
+G = json.load(open(os.path.join(HERE, "golden", "layout_hand.json")))
+
+
+def test_hand_pack():
+    b = layout.pack_nibbles(np.array(G["pack"]["codes"], np.uint8))
+    assert list(b) == G["pack"]["bytes"]
+
+
+def test_nibbles_all_bytes():
+    b = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(layout.pack_nibbles(layout.unpack_nibbles(b)), b)
+
+
+def test_record_sizes():
+    rb = G["record_bytes"]
+    assert layout.tq4_record_bytes(64) == rb["tq4_64"]
+    assert layout.tq4_record_bytes(128) == rb["tq4_128"]
+    assert layout.mxfp4_record_bytes(128) == rb["mxfp4_128"]
+    assert layout.tq4_sections(128)["end"] == rb["tq4_128"]
+    assert layout.mxfp4_sections(128)["end"] == rb["mxfp4_128"]
+
+
+def test_hand_offsets():
+    for e in G["kc"]:
+        assert int(layout.kc_offset(e["t"], e["p"], e["d"])) == e["off"]
+    for e in G["vc"]:
+        assert int(layout.vc_offset(e["t"], e["p"], e["d"])) == e["off"]
+    for e in G["vm"]:
+        so, mo = layout.vm_offsets(e["t"], e["gp"], e["d"])
+        assert (int(so), int(mo)) == (e["scale"], e["min"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_offset_maps_are_bijections(d):
+    t = np.arange(16)[:, None]
+    p = np.arange(d // 2)[None, :]
+    for off in (layout.kc_offset(t, p, d), layout.vc_offset(t, p, d)):
+        assert np.array_equal(np.sort(off.ravel()), np.arange(16 * d // 2))
+    gp = np.arange(d // 32)[None, :]
+    so, mo = layout.vm_offsets(t, gp, d)
+    allb = np.concatenate([so.ravel(), so.ravel() + 1, mo.ravel(), mo.ravel() + 1])
+    assert np.array_equal(np.sort(allb), np.arange(16 * (d // 32) * 4))
+    if d == 128:
+        assert np.array_equal(np.sort(layout.ks4_offset(t, gp).ravel()), np.arange(64))
+        assert np.array_equal(np.sort(layout.vs4_offset(t, gp, d).ravel()), np.arange(64))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_tq4_write_read_round_trip(d):
+    rng = np.random.default_rng(16)
+    n = 16
+    rec = np.zeros((n, layout.tq4_record_bytes(d)), np.uint8)
+    rows = rng.permutation(16)
+    kc = rng.integers(0, 16, (n, d)).astype(np.uint8)
+    vc = rng.integers(0, 16, (n, d)).astype(np.uint8)
+    ks = rng.standard_normal(n).astype(np.float16)
+    sc = rng.standard_normal((n, d // 32)).astype(np.float16)
+    mn = rng.standard_normal((n, d // 32)).astype(np.float16)
+    # all 16 rows of one block, written together into one record
+    one = np.zeros(rec.shape[1], np.uint8)
+    layout.tq4_write_rows(one, np.zeros(n, np.int64), rows, d, kc, ks, vc, sc, mn)
+    back = layout.tq4_read_block(one[None], d)
+    for i in range(n):
+        t = rows[i]
+        assert np.array_equal(back["kcode"][0, t], kc[i])
+        assert np.array_equal(back["vcode"][0, t], vc[i])
+        assert back["kscale"][0, t].view(np.uint16) == ks[i].view(np.uint16)
+        assert np.array_equal(back["vscale"][0, t].view(np.uint16), sc[i].view(np.uint16))
+        assert np.array_equal(back["vmin"][0, t].view(np.uint16), mn[i].view(np.uint16))
+
+
+def test_mxfp4_write_read_round_trip():
+    rng = np.random.default_rng(17)
+    d = 128
+    rec = np.zeros((16, layout.mxfp4_record_bytes(d)), np.uint8)
+    kc = rng.integers(0, 16, (16, d)).astype(np.uint8)
+    vc = rng.integers(0, 16, (16, d)).astype(np.uint8)
+    kx = rng.integers(-127, 128, (16, 4))
+    vx = rng.integers(-127, 128, (16, 4))
+    t = np.arange(16)
+    one = np.zeros((16, rec.shape[1]), np.uint8)
+    # row i goes to record i, token row i
+    layout.mxfp4_write_rows(one.reshape(-1), t * rec.shape[1], t, d, kc, kx, vc, vx)
+    back = layout.mxfp4_read_block(one, d)
+    for i in range(16):
+        assert np.array_equal(back["kcode"][i, i], kc[i])
+        assert np.array_equal(back["vcode"][i, i], vc[i])
+        assert np.array_equal(back["kexp"][i, i], kx[i])
+        assert np.array_equal(back["vexp"][i, i], vx[i])
