@@ -1,0 +1,56 @@
+"""Convenience wrapper: a cache whose pool and decode workspace are torch
+tensors on the current device.  Marshalling only."""
+import torch
+
+from . import binding as B
+
+
+class Cache:
+    def __init__(self, fmt, head_dim, num_kv_heads, num_blocks, key_table=None, device="cuda"):
+        self.fmt, self.head_dim, self.num_kv_heads, self.num_blocks = fmt, head_dim, num_kv_heads, num_blocks
+        nbytes = B.tq_pool_bytes(fmt, head_dim, num_kv_heads, num_blocks)
+        self.pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.handle = B.tq_create_cache(fmt, head_dim, num_kv_heads, num_blocks, key_table, self.pool)
+        self.record_bytes = B.tq_record_bytes(fmt, head_dim, num_kv_heads, num_blocks)
+        self._ws = None
+
+    def quantize_append(self, k, v, slot_mapping, stream=None):
+        assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int32
+        assert k.is_contiguous() and v.is_contiguous() and slot_mapping.is_contiguous()
+        assert k.shape == v.shape and k.shape[1:] == (self.num_kv_heads, self.head_dim)
+        assert slot_mapping.shape == (k.shape[0],)
+        B.tq_quantize_append(self.handle, k, v, slot_mapping, stream)
+
+    def workspace(self, batch, num_q_heads, max_context_len):
+        need = B.tq_decode_workspace_bytes(self.handle, batch, num_q_heads, max_context_len)
+        if need == 0:
+            return None
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.pool.device)
+        return self._ws
+
+    def decode(self, q, block_table, context_lens, max_context_len, softmax_scale, out=None,
+               out_dtype=torch.float32, stream=None):
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == self.head_dim
+        assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+        assert context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        ws = self.workspace(q.shape[0], q.shape[1], max_context_len)
+        B.tq_decode_attention(self.handle, q, out, block_table, context_lens, max_context_len, softmax_scale, ws,
+                              stream)
+        return out
+
+    def key_table_f16(self):
+        return B.tq_cache_info(self.handle)[2]
+
+    def close(self):
+        if self.handle is not None:
+            B.tq_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,272 @@
+// C-ABI of the 4-bit KV-cache library: argument checks, handle and table
+// management, launch planning.  Every compute step runs in the HIP kernels.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+struct tq_cache {
+  tq_cache_desc desc;
+  size_t record_bytes;
+  size_t pool_bytes;
+  uint8_t *pool;
+  bool owns_pool;
+  tq::DeviceTables *tables;  // device
+  tq::BinParams bins;
+  uint16_t table_f16[16];
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+tq_status hip_fail(hipError_t e, const char *what) {
+  return fail(TQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+tq_status check_desc(const tq_cache_desc *d, size_t *record) {
+  if (!d) return fail(TQ_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->block_size != 16) return fail(TQ_ERR_INVALID_ARG, "block_size must be 16");
+  if (d->num_kv_heads < 1) return fail(TQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (d->num_blocks < 1) return fail(TQ_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (d->format == TQ_FORMAT_TQ4) {
+    if (d->head_dim != 64 && d->head_dim != 128)
+      return fail(TQ_ERR_UNSUPPORTED, "TQ4/4 supports head_dim 64 and 128");
+    *record = tq::tq4_record_bytes(d->head_dim);
+  } else if (d->format == TQ_FORMAT_MXFP4) {
+    if (d->head_dim != 128) return fail(TQ_ERR_UNSUPPORTED, "MX-FP4 supports head_dim 128");
+    if (d->key_table) return fail(TQ_ERR_INVALID_ARG, "MX-FP4 takes no key table");
+    *record = tq::mxfp4_record_bytes(d->head_dim);
+  } else {
+    return fail(TQ_ERR_INVALID_ARG, "unknown format");
+  }
+  const double total = (double)*record * (double)d->num_blocks * (double)d->num_kv_heads;
+  if (total > 9.0e18) return fail(TQ_ERR_INVALID_ARG, "pool size overflows");
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported";
+    case TQ_ERR_OOM: return "out of device memory";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_record_bytes(const tq_cache_desc *desc, size_t *bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  size_t rec;
+  tq_status st = check_desc(desc, &rec);
+  if (st != TQ_OK) return st;
+  *bytes = rec;
+  return TQ_OK;
+}
+
+tq_status tq_pool_bytes(const tq_cache_desc *desc, size_t *bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  size_t rec;
+  tq_status st = check_desc(desc, &rec);
+  if (st != TQ_OK) return st;
+  *bytes = rec * (size_t)desc->num_blocks * (size_t)desc->num_kv_heads;
+  return TQ_OK;
+}
+
+tq_status tq_default_key_table(uint16_t out_f16[16]) {
+  if (!out_f16) return fail(TQ_ERR_INVALID_ARG, "output is NULL");
+  double c[16];
+  tq::lloyd_max_gaussian16(c);
+  for (int i = 0; i < 16; ++i) out_f16[i] = tq::f64_to_f16_rne(c[i]);
+  return TQ_OK;
+}
+
+tq_status tq_create_cache(const tq_cache_desc *desc, void *pool, size_t pool_bytes, tq_cache **out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  size_t rec;
+  tq_status st = check_desc(desc, &rec);
+  if (st != TQ_OK) return st;
+  const size_t need = rec * (size_t)desc->num_blocks * (size_t)desc->num_kv_heads;
+  if (pool && pool_bytes < need) return fail(TQ_ERR_INVALID_ARG, "pool smaller than tq_pool_bytes");
+
+  tq_cache c{};
+  c.desc = *desc;
+  c.desc.key_table = nullptr;
+  c.record_bytes = rec;
+  c.pool_bytes = need;
+  tq::DeviceTables host_tables{};
+  if (desc->format == TQ_FORMAT_TQ4) {
+    if (desc->key_table) {
+      for (int i = 0; i < 16; ++i) {
+        if (!std::isfinite(desc->key_table[i])) return fail(TQ_ERR_INVALID_ARG, "key table entries must be finite");
+        c.table_f16[i] = tq::f64_to_f16_rne((double)desc->key_table[i]);
+        if ((c.table_f16[i] & 0x7c00u) == 0x7c00u) return fail(TQ_ERR_INVALID_ARG, "key table entry overflows fp16");
+      }
+      for (int i = 0; i < 15; ++i)
+        if (!(tq::f16_to_f64(c.table_f16[i]) < tq::f16_to_f64(c.table_f16[i + 1])))
+          return fail(TQ_ERR_INVALID_ARG, "key table must be strictly ascending after rounding to fp16");
+    } else {
+      tq_default_key_table(c.table_f16);
+    }
+    if (!tq::build_key_tables(c.table_f16, &host_tables, &c.bins))
+      return fail(TQ_ERR_UNSUPPORTED, "key table midpoints are too close for the coder's bin table");
+  }
+
+  hipError_t e;
+  if (pool) {
+    c.pool = static_cast<uint8_t *>(pool);
+    c.owns_pool = false;
+  } else {
+    e = hipMalloc(&c.pool, need);
+    if (e != hipSuccess) return fail(TQ_ERR_OOM, std::string("pool allocation failed: ") + hipGetErrorString(e));
+    c.owns_pool = true;
+    e = hipMemset(c.pool, 0, need);
+    if (e != hipSuccess) {
+      (void)hipFree(c.pool);
+      return hip_fail(e, "hipMemset(pool)");
+    }
+  }
+  e = hipMalloc(&c.tables, sizeof(tq::DeviceTables));
+  if (e != hipSuccess) {
+    if (c.owns_pool) (void)hipFree(c.pool);
+    return fail(TQ_ERR_OOM, "table allocation failed");
+  }
+  e = hipMemcpy(c.tables, &host_tables, sizeof host_tables, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(c.tables);
+    if (c.owns_pool) (void)hipFree(c.pool);
+    return hip_fail(e, "hipMemcpy(tables)");
+  }
+  *out = new tq_cache(c);
+  return TQ_OK;
+}
+
+tq_status tq_cache_info(const tq_cache *cache, void **pool, size_t *pool_bytes, uint16_t *key_table_f16) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (pool) *pool = cache->pool;
+  if (pool_bytes) *pool_bytes = cache->pool_bytes;
+  if (key_table_f16) std::memcpy(key_table_f16, cache->table_f16, sizeof cache->table_f16);
+  return TQ_OK;
+}
+
+tq_status tq_quantize_append(tq_cache *cache, const void *k, const void *v, const int32_t *slot_mapping,
+                             int64_t num_tokens, void *stream) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (num_tokens < 0) return fail(TQ_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return TQ_OK;
+  if (!k || !v || !slot_mapping) return fail(TQ_ERR_INVALID_ARG, "k, v and slot_mapping must be non-NULL");
+  if (((uintptr_t)k | (uintptr_t)v) & 15) return fail(TQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (num_tokens > ((int64_t)1 << 36)) return fail(TQ_ERR_INVALID_ARG, "num_tokens too large");
+  tq::QuantizeArgs a{};
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.hkv = cache->desc.num_kv_heads;
+  a.pool = cache->pool;
+  a.num_blocks = cache->desc.num_blocks;
+  a.tables = cache->tables;
+  a.bins = cache->bins;
+  a.rsqrt_d = (float)(1.0 / std::sqrt((double)cache->desc.head_dim));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = cache->desc.format == TQ_FORMAT_TQ4 ? tq::launch_tq4_quantize(cache->desc.head_dim, a, s)
+                                                      : tq::launch_mxfp4_quantize(a, s);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return TQ_OK;
+}
+
+tq_status tq_decode_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_context_len, size_t *bytes) {
+  if (!cache || !bytes) return fail(TQ_ERR_INVALID_ARG, "cache and bytes must be non-NULL");
+  if (batch < 0 || num_q_heads < 1 || max_context_len < 0)
+    return fail(TQ_ERR_INVALID_ARG, "batch, num_q_heads or max_context_len out of range");
+  const tq::SplitPlan p = tq::plan_split(batch, cache->desc.num_kv_heads, max_context_len);
+  *bytes = p.nsplit > 1 ? (size_t)batch * num_q_heads * p.nsplit * (size_t)(cache->desc.head_dim + 2) * 4 : 0;
+  return TQ_OK;
+}
+
+tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                              const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                              int32_t batch, int32_t num_q_heads, int32_t max_context_len, float softmax_scale,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (batch < 0) return fail(TQ_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return TQ_OK;
+  if (!q || !out || !block_table || !context_lens)
+    return fail(TQ_ERR_INVALID_ARG, "q, out, block_table and context_lens must be non-NULL");
+  if (out_dtype != TQ_OUT_F32 && out_dtype != TQ_OUT_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
+  const int hkv = cache->desc.num_kv_heads;
+  if (num_q_heads < hkv || num_q_heads % hkv)
+    return fail(TQ_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  const int g = num_q_heads / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "query heads per kv-head must be 1, 2, 4 or 8");
+  if (max_context_len < 0) return fail(TQ_ERR_INVALID_ARG, "max_context_len must be >= 0");
+  if (max_blocks < (max_context_len + 15) / 16 || max_blocks < 1)
+    return fail(TQ_ERR_INVALID_ARG, "max_blocks must cover max_context_len");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(TQ_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  const tq::SplitPlan p = tq::plan_split(batch, hkv, max_context_len);
+  size_t need = 0;
+  tq_decode_workspace_bytes(cache, batch, num_q_heads, max_context_len, &need);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_decode_workspace_bytes (" + std::to_string(need) + ")");
+
+  tq::DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.out = out;
+  a.block_table = block_table;
+  a.ctx = context_lens;
+  a.pool = cache->pool;
+  a.tables = cache->tables;
+  const int d = cache->desc.head_dim;
+  if (p.nsplit > 1) {
+    a.part_ml = static_cast<float *>(workspace);
+    a.part_acc = a.part_ml + (size_t)batch * num_q_heads * p.nsplit * 2;
+  }
+  const double log2e = 1.4426950408889634074;
+  a.qscale = (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)));
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = hkv;
+  a.g = g;
+  a.split_blocks = p.split_blocks;
+  a.nsplit = p.nsplit;
+  a.out_bf16 = out_dtype == TQ_OUT_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = cache->desc.format == TQ_FORMAT_TQ4 ? tq::launch_tq4_decode(d, a, s) : tq::launch_mxfp4_decode(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (p.nsplit > 1) {
+    e = tq::launch_decode_merge(d, a, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return TQ_OK;
+}
+
+void tq_free(tq_cache *cache) {
+  if (!cache) return;
+  (void)hipDeviceSynchronize();
+  if (cache->tables) (void)hipFree(cache->tables);
+  if (cache->owns_pool && cache->pool) (void)hipFree(cache->pool);
+  delete cache;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kMaxBins = 1024;   // key-coder bin table capacity
+constexpr int kMaxGqa = 8;       // query heads per kv-head handled by one work-group
+
+// Device-side tables of one cache (one allocation, laid out in this order).
+struct DeviceTables {
+  uint32_t lut2[256];            // byte -> (fp16 c[lo nibble], fp16 c[hi nibble])
+  float2 bins[kMaxBins];         // key coder: (threshold inside the bin or +inf, code below as int bits)
+};
+
+// Key-coder bin parameters: bin(u) = clamp(floor(u * a + b), 0, nbins - 1).
+struct BinParams {
+  float a, b;
+  int nbins;
+};
+
+struct QuantizeArgs {
+  const uint16_t *k, *v;         // bf16 [n][hkv][d]
+  const int32_t *slots;          // [n]
+  int64_t num_tokens;
+  int32_t hkv;
+  uint8_t *pool;
+  int64_t num_blocks;
+  const DeviceTables *tables;
+  BinParams bins;
+  float rsqrt_d;                 // fp32(1/sqrt(d))
+};
+
+struct DecodeArgs {
+  const uint16_t *q;             // bf16 [batch][hq][d]
+  void *out;                     // fp32 / bf16 [batch][hq][d]
+  const int32_t *block_table;    // [batch][max_blocks]
+  const int32_t *ctx;            // [batch]
+  const uint8_t *pool;
+  const DeviceTables *tables;
+  float *part_ml;                // [batch][hq][nsplit][2] (max, sum) in log2 units
+  float *part_acc;               // [batch][hq][nsplit][d]
+  float qscale;                  // softmax_scale * log2(e) * fp32(1/sqrt(d))
+  int32_t max_blocks, batch, hq, hkv, g;
+  int32_t split_blocks;          // blocks per work-group
+  int32_t nsplit;                // splits per (sequence, kv-head)
+  int32_t out_bf16;
+};
+
+// Launchers (defined next to their kernels).
+hipError_t launch_tq4_quantize(int d, const QuantizeArgs &a, hipStream_t s);
+hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
+hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
+
+// Host table construction (pure C++, no HIP calls).
+void lloyd_max_gaussian16(double out[16]);
+uint16_t f64_to_f16_rne(double x);
+double f16_to_f64(uint16_t h);
+// Builds lut2 and the key-coder bins from an fp16 table; false if the table's
+// midpoints are too close for kMaxBins bins.
+bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *bp);
+
+// Record sizes.
+inline size_t tq4_record_bytes(int d) { return (size_t)16 * (d / 2 + 2 + d / 2 + (d / 32) * 4); }
+inline size_t mxfp4_record_bytes(int d) { return (size_t)16 * (d / 2 + d / 32 + d / 2 + d / 32); }
+
+// Split-K plan shared by the workspace query and the launch.
+struct SplitPlan {
+  int split_blocks, nsplit;
+};
+SplitPlan plan_split(int batch, int hkv, int max_context_len);
+
+}  // namespace tq

@@ -1,0 +1,176 @@
+/*
+ * tq.h - 4-bit paged KV cache (TQ4/4 and MX-FP4) and decode attention that
+ * reads the compressed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; every device pointer is a HIP device
+ * address, every `stream` argument is a hipStream_t (NULL = the legacy default
+ * stream).  Calls that take a stream are asynchronous on it; kernel faults
+ * surface at the caller's next synchronisation, as for any HIP launch.
+ * Functions return a tq_status; tq_last_error() gives a thread-local message
+ * for the last failure.  No function throws.
+ *
+ * Pages the operations come from (cited by title and section):
+ *   [TQ-AMD] "TurboQuant 在 AMD GPU 上把長上下文延遲壓下來" (ROCm TurboQuant in
+ *            vLLM): section 2 "TQ4/4 是最穩的預設值" - 4-bit K and 4-bit V,
+ *            K = rotation + LUT quantization, V = uniform quantization;
+ *            section 4 "Walsh-Hadamard 比隨機 rotation 更實用" - the rotation
+ *            is a Walsh-Hadamard transform; section 5 - no QJL at 4 bits.
+ *   [UQ]     "UltraQuant：4-bit KV 快取加速長代理": section "方法怎麼做，白話講"
+ *            - WHT rotation, K/V asymmetry, Lloyd-Max 16-entry table, and the
+ *            FP4 path (FP8 queries, FP4 KV, UE8M0 group scales, scaled MFMA).
+ *   [ST]     "StateTree-Representation：讓 LLM 壓縮後仍保留 BF16 精度": vLLM
+ *            paged KV blocks of 16 tokens.
+ *
+ * ---------------------------------------------------------------------------
+ * Formats.  D = head_dim, P = D/2, Q = D/8, G = D/32, token row t in [0,16)
+ * of a block, t = 4r + tt.  A pool is [num_blocks][num_kv_heads][record];
+ * a record holds one 16-token block of one kv-head.  A byte holds two 4-bit
+ * codes: the even channel in the low nibble.  fp16 values are little-endian.
+ *
+ * TQ4/4 (format 0, D = 64 or 128).  Per (token, kv-head):
+ *   key scale  s = fp16_RNE(sqrt(sum_i k_i^2 / D)) (exact; saturates at 65504)
+ *   key codes  x = unnormalized fp32 Walsh-Hadamard butterflies of k (stage
+ *              order h = 1, 2, ..., D/2; (a, b) -> (a + b, a - b)),
+ *              w = fp32(fp32(1/s) * fp32(1/sqrt(D))), u_i = fp32(x_i * w)
+ *              (u = 0 if s = 0), t_j = fp32((c_j + c_{j+1}) * 0.5) over the fp16
+ *              table c, code_i = #{ j : u_i > t_j } (nearest entry, ties low).
+ *              Dequantized keys stay rotated: k_hat_i = c[code_i] * s.
+ *   values     per 32-channel group: sc = fp16_sat(fp32(fp32(max - min) / 15)),
+ *              mn = fp16_sat(min), code = clamp(RNE(fp32(fp32(v - mn) *
+ *              fp32(1/sc))), 0, 15) (0 if sc = 0); v_hat = code * sc + mn.
+ *   record (2336 B at D = 128, 1184 B at D = 64):
+ *     Kc  16*P B   pair p of token t at ((p / Q) * 16 + t) * Q + p % Q
+ *     Ks  32 B     fp16 s of token t at 2t
+ *     Vc  16*P B   pair p = 16*gp + j of token t at ((r*16 + j)*G + gp)*4 + tt
+ *     Vm  64*G B   pos = {0,2,1,3}[tt]: sc(t,gp) at 2*((r*G + gp)*8 + pos),
+ *                  mn(t,gp) at 2*((r*G + gp)*8 + 4 + pos)
+ *
+ * MX-FP4 (format 1, D = 128).  Per (token, kv-head), groups of 32 channels:
+ *   keys are rotated first, y = fp32(x * fp32(1/sqrt(D))); values are not.
+ *   X = clamp(floor(log2(amax)) - 2, -127, 127) (amax = 0 -> -127), stored as
+ *   the byte X + 127; element code = e2m1_RNE(value / 2^X) saturating at +-6,
+ *   sign bit = the value's sign bit.  Queries: rotated the same way, cast to
+ *   FP8 e4m3 (OCP e4m3fn, RNE, saturating), unit scale.
+ *   record (2176 B):
+ *     Kc4 1024 B   e2m1 key codes, placed as Kc
+ *     Ks4 64 B     key exponent byte of (t, gp) at gp*16 + t
+ *     Vc4 1024 B   e2m1 value codes, placed as Vc
+ *     Vs4 64 B     value exponent byte of (t, gp) at (r*G + gp)*4 + tt
+ *
+ * Paging: token n of a quantize call goes to slot s = slot_mapping[n], block
+ * s / 16, row s % 16 of every kv-head; s < 0 skips the token.  Decode reads
+ * token t of sequence b from block block_table[b * max_blocks + t / 16].
+ * Several sequences may name the same block.  Query head h uses kv-head
+ * h / (num_q_heads / num_kv_heads).
+ * ---------------------------------------------------------------------------
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1,  /* a host-checked argument is out of range or NULL   */
+  TQ_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. head_dim 96)      */
+  TQ_ERR_OOM = 3,          /* device allocation failed                          */
+  TQ_ERR_WORKSPACE = 4,    /* workspace smaller than tq_decode_workspace_bytes  */
+  TQ_ERR_HIP = 5           /* a HIP runtime call failed (see tq_last_error)     */
+} tq_status;
+
+typedef enum tq_format { TQ_FORMAT_TQ4 = 0, TQ_FORMAT_MXFP4 = 1 } tq_format;
+typedef enum tq_out_dtype { TQ_OUT_F32 = 0, TQ_OUT_BF16 = 1 } tq_out_dtype;
+
+typedef struct tq_cache_desc {
+  int32_t format;          /* tq_format                                          */
+  int32_t head_dim;        /* TQ4: 64 or 128; MX-FP4: 128                         */
+  int32_t num_kv_heads;    /* >= 1                                                */
+  int32_t block_size;      /* must be 16                                          */
+  int64_t num_blocks;      /* >= 1                                                */
+  const float *key_table;  /* TQ4 only: host pointer to 16 strictly ascending
+                              finite values, or NULL for the 16-level Lloyd-Max
+                              quantizer of N(0,1) ([UQ] "方法怎麼做，白話講").
+                              Rounded to fp16 (RNE) when the cache is created.
+                              Must be NULL for MX-FP4.                            */
+} tq_cache_desc;
+
+typedef struct tq_cache tq_cache;  /* opaque handle */
+
+/* Bytes of one (block, kv-head) record (2336 / 1184 / 2176, see above). */
+tq_status tq_record_bytes(const tq_cache_desc *desc, size_t *bytes);
+
+/* Bytes of the whole pool: num_blocks * num_kv_heads * record bytes. */
+tq_status tq_pool_bytes(const tq_cache_desc *desc, size_t *bytes);
+
+/* Create a cache handle.  `pool` is a caller-owned device buffer of at least
+ * tq_pool_bytes bytes (its contents are kept), or NULL: then the library
+ * allocates the pool and fills it with zeros.  The library always owns the
+ * handle and a small device table buffer.  Synchronous.  Errors:
+ * INVALID_ARG (bad descriptor, pool too small, key table not ascending or not
+ * finite), UNSUPPORTED (head_dim / format combination, or a key table whose
+ * midpoints are too close for the coder's bin table: adjacent midpoints must
+ * differ by more than 1/64 of the table's midpoint range), OOM, HIP. */
+tq_status tq_create_cache(const tq_cache_desc *desc, void *pool, size_t pool_bytes, tq_cache **out);
+
+/* The pool's device address and size, and the fp16 key table in use (16 fp16
+ * bit patterns; NULL to skip; zeros for MX-FP4). */
+tq_status tq_cache_info(const tq_cache *cache, void **pool, size_t *pool_bytes, uint16_t *key_table_f16);
+
+/* The default key table, derived on the host: the 16-level Lloyd-Max
+ * quantizer of N(0,1) (fp64 fixed point of Lloyd's conditions), each level
+ * rounded to fp16; written as fp16 bit patterns.  No GPU needed. */
+tq_status tq_default_key_table(uint16_t out_f16[16]);
+
+/* Quantize and append tokens ([TQ-AMD] section 2; [UQ] "方法怎麼做，白話講").
+ * k, v: device bf16 [num_tokens][num_kv_heads][head_dim], contiguous.
+ * slot_mapping: device int32 [num_tokens]; slot = block * 16 + row, < 0 skips.
+ * Slots must be < num_blocks * 16 and distinct within one call (trusted, not
+ * checked on the device).  num_tokens = 0 is a no-op.  Asynchronous. */
+tq_status tq_quantize_append(tq_cache *cache, const void *k, const void *v, const int32_t *slot_mapping,
+                             int64_t num_tokens, void *stream);
+
+/* Workspace bytes that tq_decode_attention needs for these sizes (split-K
+ * partials; 0 when one split covers max_context_len). */
+tq_status tq_decode_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_context_len, size_t *bytes);
+
+/* Decode attention over the compressed cache, one query token per sequence:
+ *   out[b, h] = sum_{t < T_b} softmax_t(scale * <q~[b,h], k_hat_t>) v_hat_t
+ * with q~ the rotated query (TQ4: H_D q; MX-FP4: its e4m3 code values) and
+ * k_hat, v_hat the dequantized cache rows of kv-head h / g.  The keys are
+ * compared in the rotated domain, which leaves q . k unchanged ([TQ-AMD]
+ * section 4).  Split-K over the context with a log-sum-exp merge.
+ * q: device bf16 [batch][num_q_heads][head_dim]; out: device fp32 or bf16
+ * (out_dtype) of the same shape; block_table: device int32
+ * [batch][max_blocks]; context_lens: device int32 [batch], each in
+ * [0, max_context_len] with ceil(len/16) <= max_blocks (trusted); a zero
+ * length gives a zero row.  num_q_heads must be num_kv_heads * g with
+ * g in {1, 2, 4, 8}.  max_context_len is the host's bound, used to size the
+ * split.  softmax_scale > 0 (e.g. 1/sqrt(head_dim)).  workspace: device buffer
+ * of at least tq_decode_workspace_bytes (may be NULL when that is 0).
+ * Asynchronous. */
+tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                              const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                              int32_t batch, int32_t num_q_heads, int32_t max_context_len, float softmax_scale,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Free the handle (NULL-safe).  Synchronises the device first; frees the
+ * library-owned pool if the library allocated it. */
+void tq_free(tq_cache *cache);
+
+/* Static text of a status code. */
+const char *tq_status_string(tq_status status);
+
+/* Thread-local text of the last failure in this thread ("" if none). */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,107 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the C ABI, build the oracle's side from the same inputs."""
+import os
+import sys
+
+import numpy as np
+import torch
+
+import workloads
+from oracle import attention, paged
+
+TOL = 2e-3   # max over rows of ||o - o_ref||_inf / ||o_ref||_inf
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_dev_i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def row_rel_err(out, ref):
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.abs(out - ref).max(-1)
+    den = np.abs(ref).max(-1)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1), num)))
+
+
+class Case:
+    """One workload on the GPU and (for chosen sequences) in the oracle."""
+
+    def __init__(self, cfg, key_table=None):
+        from bit_quantized_kv_amd import Cache
+        self.w = workloads.make(cfg)
+        self.cfg = self.w.cfg
+        c = self.cfg
+        self.cache = Cache(c.fmt, c.head_dim, c.num_kv_heads, self.w.num_blocks, key_table=key_table)
+        self.key_table = key_table
+        self.table_dev = to_dev_i32(self.w.block_table)
+
+    def write_ranges(self, lens=None):
+        """Token ranges that write every cached token once (see workloads)."""
+        return self.w.write_plan(lens)
+
+    def quantize(self, ranges, chunk_tokens=1 << 22):
+        """One quantize call per chunk of concatenated token ranges."""
+        ks, vs, ss, n = [], [], [], 0
+        for b, t0, t1 in ranges:
+            k, v = self.w.sequence_kv(b)
+            ks.append(k[t0:t1])
+            vs.append(v[t0:t1])
+            ss.append(self.w.slots(b, t0, t1))
+            n += t1 - t0
+            if n >= chunk_tokens:
+                self._q(ks, vs, ss)
+                ks, vs, ss, n = [], [], [], 0
+        if ks:
+            self._q(ks, vs, ss)
+
+    def _q(self, ks, vs, ss):
+        k = to_dev_bf16(np.concatenate(ks))
+        v = to_dev_bf16(np.concatenate(vs))
+        s = to_dev_i32(np.concatenate(ss))
+        self.cache.quantize_append(k, v, s)
+
+    def pool_np(self):
+        torch.cuda.synchronize()
+        rec = self.cache.record_bytes
+        return self.cache.pool.cpu().numpy().reshape(self.w.num_blocks, self.cfg.num_kv_heads, rec)
+
+    def oracle_pool(self, ranges):
+        c = self.cfg
+        tab = None if self.key_table is None else np.asarray(self.key_table, np.float32).astype(np.float16)
+        op = paged.PagedPool(c.fmt, self.w.num_blocks, c.num_kv_heads, c.head_dim, tab)
+        for b, t0, t1 in ranges:
+            k, v = self.w.sequence_kv(b)
+            op.append(workloads.bf16_bits_to_f32(k[t0:t1]), workloads.bf16_bits_to_f32(v[t0:t1]),
+                      self.w.slots(b, t0, t1))
+        return op
+
+    def blocks_of(self, seqs, lens=None):
+        ids = []
+        for b in seqs:
+            n = -(-int((lens if lens is not None else self.w.total_lens)[b]) // 16)
+            ids.extend(self.w.block_table[b, :n].tolist())
+        return np.unique(np.array(ids, dtype=np.int64))
+
+    def decode(self, step=0, ctx=None, out_dtype=torch.float32):
+        c = self.cfg
+        q = to_dev_bf16(self.w.query_bits(step))
+        ctx = self.w.context_lens_at(step) if ctx is None else np.asarray(ctx, np.int32)
+        out = self.cache.decode(q, self.table_dev, to_dev_i32(ctx), int(max(1, ctx.max())), c.scale,
+                                out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy()
+
+    def oracle_decode(self, opool, rows, step=0, ctx=None):
+        q = workloads.bf16_bits_to_f32(self.w.query_bits(step))
+        ctx = self.w.context_lens_at(step) if ctx is None else np.asarray(ctx, np.int32)
+        return attention.decode(opool, q, self.w.block_table, ctx, self.cfg.scale, rows=rows)

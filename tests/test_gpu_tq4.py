@@ -1,0 +1,179 @@
+"""GPU parity of the TQ4/4 path against the CPU oracle, through the C ABI.
+
+Packed bytes must be identical (codes, scales, layout); decode attention must
+be within 2e-3 (max over rows of ||o - o_ref||_inf / ||o_ref||_inf) of the
+oracle's exact fp64 attention over the same dequantized cache."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import TOL, Case, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _split_env():
+    old = os.environ.pop("TQ_SPLIT_BLOCKS", None)
+    yield
+    os.environ.pop("TQ_SPLIT_BLOCKS", None)
+    if old is not None:
+        os.environ["TQ_SPLIT_BLOCKS"] = old
+
+
+def _check_case(case, seqs=None, rows=None, step=0):
+    c = case.cfg
+    seqs = list(range(c.batch)) if seqs is None else seqs
+    ranges = case.write_ranges()
+    case.quantize(ranges)
+    gpu = case.pool_np()
+    writer = case.w.prefix_writer()
+    op = case.oracle_pool([r for r in ranges if r[0] in seqs or r[0] == writer])
+    blocks = case.blocks_of(seqs)
+    mism = np.nonzero(np.any(gpu[blocks] != op.pool[blocks], axis=-1))
+    assert mism[0].size == 0, f"{mism[0].size} records differ, first block {blocks[mism[0][0]]} head {mism[1][0]}"
+    out = case.decode(step)
+    rows = rows if rows is not None else [(b, h) for b in seqs for h in range(c.num_q_heads)]
+    ref = case.oracle_decode(op, rows, step)
+    err = row_rel_err(np.array([out[b, h] for b, h in rows]), np.array([ref[b, h] for b, h in rows]))
+    say(f"  {c.name}: {len(blocks)} blocks byte-identical, {len(rows)} rows, max rel err {err:.2e}")
+    assert err <= TOL
+    return out, ref
+
+
+def test_tiny_config():
+    say("case: tiny (1 seq, 1 kv head, g=4, D=64, T=256)")
+    _check_case(Case(workloads.CONFIGS["tiny"]))
+
+
+@pytest.mark.parametrize("d,g,hkv,seed,split", [
+    (128, 4, 2, 101, None), (128, 8, 1, 102, None), (128, 1, 3, 103, 4), (128, 2, 2, 104, 8),
+    (64, 4, 2, 105, None), (64, 8, 1, 106, 4), (64, 1, 2, 107, None), (64, 2, 1, 108, 12),
+])
+def test_small_ragged(d, g, hkv, seed, split):
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=5, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                 ctx_range=(1, 700), seed=seed)
+    say(f"case: small ragged d={d} g={g} hkv={hkv} seed={seed} split={split}")
+    _check_case(Case(cfg))
+
+
+def test_edge_lengths_and_zero_context():
+    cfg = workloads.small_config(batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(1, 40), seed=109)
+    case = Case(cfg)
+    ranges = case.write_ranges()
+    case.quantize(ranges)
+    op = case.oracle_pool(ranges)
+    ctx = np.array([0, 1, 15, 16, 17, 32], np.int32)
+    ctx = np.minimum(ctx, case.w.prompt_lens.astype(np.int32))
+    say(f"case: edge lengths {ctx.tolist()}")
+    out = case.decode(ctx=ctx)
+    rows = [(b, h) for b in range(6) for h in range(8)]
+    ref = case.oracle_decode(op, rows, ctx=ctx)
+    assert np.all(out[ctx == 0] == 0)
+    assert row_rel_err(out, ref) <= TOL
+
+
+def test_bf16_output():
+    cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(100, 300), seed=110)
+    case = Case(cfg)
+    case.quantize(case.write_ranges())
+    say("case: bf16 output")
+    o32 = case.decode()
+    o16 = case.decode(out_dtype=torch.bfloat16)
+    assert np.max(np.abs(o16 - o32)) <= np.max(np.abs(o32)) * 2 ** -8
+
+
+def test_unaligned_skipped_and_single_token_slots():
+    """Slots that break the four-row fast path, skipped tokens, and appends
+    of one token at a time must give the same bytes as the oracle."""
+    cfg = workloads.small_config(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, ctx_range=(160, 160),
+                                 seed=111)
+    w = workloads.make(cfg)
+    from bit_quantized_kv_amd import Cache
+    from gpu_common import to_dev_bf16, to_dev_i32
+    from oracle import paged
+    k, v = w.sequence_kv(0)
+    rng = np.random.default_rng(5)
+    slots = rng.permutation(w.num_blocks * 16)[:160].astype(np.int32)
+    slots[rng.choice(160, 20, replace=False)] = -1
+    cache = Cache(0, 128, 2, w.num_blocks)
+    say("case: permuted slots with skips, then one-token appends")
+    cache.quantize_append(to_dev_bf16(k[:100]), to_dev_bf16(v[:100]), to_dev_i32(slots[:100]))
+    for i in range(100, 160):
+        cache.quantize_append(to_dev_bf16(k[i:i + 1]), to_dev_bf16(v[i:i + 1]), to_dev_i32(slots[i:i + 1]))
+    torch.cuda.synchronize()
+    gpu = cache.pool.cpu().numpy().reshape(w.num_blocks, 2, -1)
+    op = paged.PagedPool(0, w.num_blocks, 2, 128)
+    op.append(workloads.bf16_bits_to_f32(k), workloads.bf16_bits_to_f32(v), slots)
+    assert np.array_equal(gpu, op.pool)
+
+
+def test_custom_key_table():
+    table = list(np.linspace(-2.5, 2.5, 16))
+    cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(50, 400), seed=112)
+    say("case: uniform custom key table")
+    case = Case(cfg, key_table=table)
+    _check_case(case)
+
+
+def test_determinism_and_split_invariance():
+    cfg = workloads.small_config(batch=3, num_q_heads=16, num_kv_heads=2, head_dim=128, ctx_range=(900, 2000),
+                                 seed=113)
+    case = Case(cfg)
+    case.quantize(case.write_ranges())
+    a = case.pool_np().copy()
+    case.quantize(case.write_ranges())
+    assert np.array_equal(a, case.pool_np())
+    say("case: split invariance 4 / 16 / 64 blocks")
+    outs = []
+    for sb in ("4", "16", "64"):
+        os.environ["TQ_SPLIT_BLOCKS"] = sb
+        outs.append(case.decode())
+    assert row_rel_err(outs[0], outs[1]) <= 2e-4 and row_rel_err(outs[0], outs[2]) <= 2e-4
+
+
+def test_full_llama8b():
+    say("case: llama8b layer (B=1, 32/8, D=128, T=32768), full pool and all rows")
+    _check_case(Case(workloads.CONFIGS["llama8b"]))
+
+
+def test_full_agentic_sampled():
+    say("case: agentic (B=32, shared prefixes), sampled sequences")
+    _check_case(Case(workloads.CONFIGS["agentic"]), seqs=[0, 9, 15, 16, 31])
+
+
+def test_full_longprefix_sampled_steps():
+    cfg = workloads.CONFIGS["longprefix"]
+    case = Case(cfg)
+    w = case.w
+    say("case: longprefix quantize 8 x 25600 tokens, then 64 one-token appends + decodes")
+    case.quantize(case.write_ranges())
+    seqs = [0, 5]
+    from gpu_common import to_dev_bf16, to_dev_i32
+    kv = [w.sequence_kv(b) for b in range(cfg.batch)]
+    checks = (0, 31, 63)
+    gpu_outs = {}
+    for step in range(cfg.decode_steps):
+        t = int(w.prompt_lens[0]) + step
+        k = np.concatenate([kv[b][0][t:t + 1] for b in range(cfg.batch)])
+        v = np.concatenate([kv[b][1][t:t + 1] for b in range(cfg.batch)])
+        s = np.concatenate([w.slots(b, t, t + 1) for b in range(cfg.batch)])
+        case.cache.quantize_append(to_dev_bf16(k), to_dev_bf16(v), to_dev_i32(s))
+        if step in checks:
+            gpu_outs[step] = case.decode(step)
+    say("  steps done; building the oracle for sampled sequences")
+    op = case.oracle_pool([(b, 0, int(w.total_lens[b])) for b in seqs])
+    gpu = case.pool_np()
+    blocks = case.blocks_of(seqs)
+    assert np.array_equal(gpu[blocks], op.pool[blocks])
+    for step in checks:
+        rows = [(b, h) for b in seqs for h in range(0, cfg.num_q_heads, 7)]
+        ref = case.oracle_decode(op, rows, step)
+        err = row_rel_err(np.array([gpu_outs[step][b, h] for b, h in rows]), np.array([ref[b, h] for b, h in rows]))
+        say(f"  step {step}: max rel err {err:.2e}")
+        assert err <= TOL

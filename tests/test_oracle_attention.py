@@ -57,11 +57,9 @@ def _filled_pool(cfg):
     w = workloads.make(cfg)
     c = w.cfg
     pool = paged.PagedPool(c.fmt, w.num_blocks, c.num_kv_heads, c.head_dim)
-    for b in range(c.batch):
+    for b, t0, t1 in w.write_plan(w.total_lens):
         k, v = w.sequence_kv(b)
-        t0 = w.private_start(b) if b else 0
-        pool.append(workloads.bf16_bits_to_f32(k[t0:]), workloads.bf16_bits_to_f32(v[t0:]),
-                    w.slots(b, t0, int(w.total_lens[b])))
+        pool.append(workloads.bf16_bits_to_f32(k[t0:t1]), workloads.bf16_bits_to_f32(v[t0:t1]), w.slots(b, t0, t1))
     return w, pool
 
 

@@ -168,6 +168,27 @@ class Workload:
         """First token of sequence b that lives in a private block."""
         return int(self.uses_shared[b]) * BLOCK if b < self.cfg.shared_seqs else 0
 
+    def prefix_writer(self):
+        """The sharing sequence with the most shared blocks: it writes the
+        whole shared prefix (or -1 when nothing is shared)."""
+        if not self.cfg.shared_seqs:
+            return -1
+        return int(np.argmax(self.uses_shared[: self.cfg.shared_seqs]))
+
+    def write_plan(self, lens=None):
+        """(b, t0, t1) ranges that write every token any sequence reads exactly
+        once: the prefix writer writes from token 0, every other sequence only
+        its private tokens.  ``lens`` defaults to the prompt lengths."""
+        lens = self.prompt_lens if lens is None else np.asarray(lens)
+        wr = self.prefix_writer()
+        plan = []
+        for b in range(self.cfg.batch):
+            t0 = 0 if b == wr else self.private_start(b)
+            t1 = int(lens[b])
+            if t1 > t0:
+                plan.append((b, t0, t1))
+        return plan
+
     def slots(self, b, t0, t1):
         """Slot of each token t in [t0, t1) of sequence b."""
         t = np.arange(t0, t1)
