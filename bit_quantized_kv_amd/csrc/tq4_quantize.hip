@@ -168,11 +168,14 @@ __global__ __launch_bounds__(256) void tq4_quantize_kernel(QuantizeArgs a) {
   }
 
   // ---- does this quad of tokens fill four consecutive rows of one block? ------
+  // (every exchange runs on all lanes: a cross-lane read under a divergent
+  // exec mask would see inactive lanes)
   const int qid = (slot >= 0 && (slot & 3) == tq) ? (slot >> 2) : -1 - tq;
-  int qo = (int)xor4u((uint32_t)qid);
-  bool aligned = (qid == qo) && qid >= 0;
-  aligned = aligned && ((int)quad_xor2<D>((uint32_t)(aligned ? 1 : 0)) == 1);
-  aligned = aligned && ((int)quad_xor2<D>((uint32_t)qid) == qid);
+  const int qo = (int)xor4u((uint32_t)qid);
+  const uint32_t pair_ok = (qid == qo && qid >= 0) ? 1u : 0u;
+  const uint32_t other_ok = quad_xor2<D>(pair_ok);
+  const int qp = (int)quad_xor2<D>((uint32_t)qid);
+  const bool aligned = pair_ok && other_ok && qp == qid;
 
   // byte transposes among the quad (all lanes take part)
   uint32_t t1 = xor4u(vw);

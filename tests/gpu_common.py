@@ -105,3 +105,16 @@ class Case:
         q = workloads.bf16_bits_to_f32(self.w.query_bits(step))
         ctx = self.w.context_lens_at(step) if ctx is None else np.asarray(ctx, np.int32)
         return attention.decode(opool, q, self.w.block_table, ctx, self.cfg.scale, rows=rows)
+
+
+def describe_record_diff(gpu_rec, ora_rec, d, fmt=0):
+    """Text naming the sections, token rows and values of differing bytes."""
+    from oracle import layout
+    idx = np.nonzero(gpu_rec != ora_rec)[0]
+    sec = layout.tq4_sections(d) if fmt == 0 else layout.mxfp4_sections(d)
+    names = sorted(((v, k) for k, v in sec.items() if k != "end"))
+    out = []
+    for i in idx[:24]:
+        name = [k for v, k in names if v <= i][-1]
+        out.append(f"{name}+{i - sec[name]}: gpu {gpu_rec[i]:#04x} oracle {ora_rec[i]:#04x}")
+    return f"{len(idx)} bytes differ: " + "; ".join(out)
