@@ -1,0 +1,354 @@
+"""Benchmark of the 4-bit KV-cache hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+quantize-and-append the batch's tokens into the paged TQ4/4 cache, then decode
+attention over a cache.  The step decodes the batch quantized two steps
+earlier (R >= 3 rotating copies of inputs and pools, R * bytes >= 2x the 256 MB
+Infinity Cache), so the decode reads its 4-bit cache from HBM rather than from
+the cache the quantize kernel just wrote; every batch still goes through both
+kernels.  Inputs are resident in HBM before the timed region starts.
+
+Output: one JSON line.  ``value`` is the decode's effective KV bandwidth
+(logical 4-bit KV bytes read / decode time); ``quantize_tokens_per_s`` the
+quantize rate; ``roofline`` the dominant kernel (by time) against the 8 TB/s
+HBM peak, with its average launch time measured by HIP events on the launch
+stream; ``cpu_baseline`` the CPU oracle timed on this host on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama8b]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="llama8b", choices=["llama8b", "agentic", "longprefix", "fp4"])
+    p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of known size (for counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_kv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
+
+
+class Bench:
+    def __init__(self, cfg, copies):
+        import torch
+
+        import workloads
+        from bit_quantized_kv_amd import Cache
+        self.torch = torch
+        self.w = workloads.make(cfg)
+        self.cfg = self.w.cfg
+        c, w = self.cfg, self.w
+        dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        plan = w.write_plan()
+        ks, vs, ss = [], [], []
+        for b, t0, t1 in plan:
+            k, v = w.sequence_kv(b)
+            ks.append(k[t0:t1])
+            vs.append(v[t0:t1])
+            ss.append(w.slots(b, t0, t1))
+        self.n_tokens = int(sum(t1 - t0 for _, t0, t1 in plan))
+        k0, v0, s0 = dev(np.concatenate(ks)), dev(np.concatenate(vs)), i32(np.concatenate(ss))
+        # appended tokens (one per sequence per decode step), if any
+        self.appends = []
+        if c.appended:
+            kvs = [w.sequence_kv(b) for b in range(c.batch)]
+            for step in range(c.decode_steps):
+                t = w.prompt_lens + step
+                ka = np.stack([kvs[b][0][int(t[b])] for b in range(c.batch)])
+                va = np.stack([kvs[b][1][int(t[b])] for b in range(c.batch)])
+                sa = np.array([w.slots(b, int(t[b]), int(t[b]) + 1)[0] for b in range(c.batch)])
+                self.appends.append((dev(ka), dev(va), i32(sa)))
+        rec_bytes = Cache(c.fmt, c.head_dim, c.num_kv_heads, 1).record_bytes
+        self.row_bytes = rec_bytes // 16
+        pool_bytes = rec_bytes * c.num_kv_heads * w.num_blocks
+        in_bytes = k0.numel() * 4
+        if copies <= 0:
+            copies = max(3, -(-2 * 256 * 2 ** 20 // (pool_bytes + in_bytes)))
+        self.copies = copies
+        self.kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+        self.slots = s0
+        self.caches = [Cache(c.fmt, c.head_dim, c.num_kv_heads, w.num_blocks) for _ in range(copies)]
+        self.table = i32(w.block_table)
+        self.q = [dev(w.query_bits(s)) for s in range(c.decode_steps)]
+        self.ctx = [i32(w.context_lens_at(s)) for s in range(c.decode_steps)]
+        self.max_ctx = [int(w.context_lens_at(s).max()) for s in range(c.decode_steps)]
+        self.out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.float32, device="cuda")
+        for cache in self.caches:   # size the decode workspace outside the timed region
+            cache.workspace(c.batch, c.num_q_heads, max(self.max_ctx))
+        self.stream = torch.cuda.current_stream()
+
+    # algorithmic bytes ---------------------------------------------------------
+    def quantize_bytes(self):
+        c = self.cfg
+        per_tok = c.num_kv_heads * (2 * 2 * c.head_dim + self.row_bytes) + 4
+        n = self.n_tokens
+        return n * per_tok
+
+    def append_bytes(self):
+        c = self.cfg
+        return c.batch * (c.num_kv_heads * (2 * 2 * c.head_dim + self.row_bytes) + 4)
+
+    def decode_bytes(self, step, unique=False):
+        c, w = self.cfg, self.w
+        lens = w.context_lens_at(step).astype(np.int64)
+        kv = int(lens.sum()) * c.num_kv_heads * self.row_bytes
+        if unique and c.shared_seqs:
+            ids = set()
+            toks = 0
+            for b in range(c.batch):
+                nb = -(-int(lens[b]) // 16)
+                for j, bid in enumerate(w.block_table[b, :nb].tolist()):
+                    if bid not in ids:
+                        ids.add(bid)
+                        toks += min(16, int(lens[b]) - 16 * j)
+            kv = toks * c.num_kv_heads * self.row_bytes
+        other = c.batch * c.num_q_heads * c.head_dim * (2 + 4) + int((-(-lens // 16)).sum()) * 4 + c.batch * 4
+        return kv, kv + other
+
+    # one step --------------------------------------------------------------------
+    def step(self, i, ev=None):
+        c = self.cfg
+        qc = i % self.copies
+        dc = (i - 2) % self.copies
+        k, v = self.kv[qc]
+        if ev is not None:
+            ev["q0"].record(self.stream)
+        self.caches[qc].quantize_append(k, v, self.slots)
+        if ev is not None:
+            ev["q1"].record(self.stream)
+        cache = self.caches[dc]
+        for s in range(c.decode_steps):
+            if self.appends:
+                ka, va, sa = self.appends[s]
+                cache.quantize_append(ka, va, sa)
+            if ev is not None:
+                ev["d0"][s].record(self.stream)
+            cache.decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s], c.scale, out=self.out)
+            if ev is not None:
+                ev["d1"][s].record(self.stream)
+
+
+def cpu_baseline(cfg_name):
+    """The CPU oracle, as it stands, on a bounded sample of the workload:
+    quantize kv-head 0 of the first sequence and decode its query heads."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    import workloads
+    from oracle import attention, paged
+    w = workloads.make(cfg_name)
+    c = w.cfg
+    g = c.num_q_heads // c.num_kv_heads
+    b = 0
+    T = int(w.context_lens_at(0)[b])
+    k, v = w.sequence_kv(b)
+    ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx_mgr:
+        ctx_mgr.__enter__()
+    try:
+        pool = paged.PagedPool(c.fmt, w.num_blocks, 1, c.head_dim)
+        t0 = time.perf_counter()
+        pool.append(workloads.bf16_bits_to_f32(k[:T, :1]), workloads.bf16_bits_to_f32(v[:T, :1]), w.slots(b, 0, T))
+        t1 = time.perf_counter()
+        q = workloads.bf16_bits_to_f32(w.query_bits(0))[:, :g]
+        attention.decode(pool, q, w.block_table, w.context_lens_at(0), c.scale, rows=[(b, h) for h in range(g)])
+        t2 = time.perf_counter()
+    finally:
+        if ctx_mgr:
+            ctx_mgr.__exit__(None, None, None)
+    row = 146 if c.head_dim == 128 else 74
+    if c.fmt == 1:
+        row = 136
+    return {
+        "value": T * row / (t2 - t1) / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{cfg_name}: sequence 0, kv-head 0 ({T} tokens): quantize {t1 - t0:.2f} s, "
+                  f"decode of its {g} query heads {t2 - t1:.2f} s (numpy, BLAS limited to 1 thread)",
+        "quantize_tokens_per_s": T / (t1 - t0) / c.num_kv_heads,
+    }
+
+
+def traffic_from_profiles(kernel_key, launch_bytes_fn):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        if d.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        e = d["kernels"][kernel_key]
+        return (e["fetch_kib_per_dispatch"] * d["fetch_scale"] + e["write_kib_per_dispatch"] * d["write_scale"]) * 1024
+    except Exception:
+        return None
+
+
+_SPIN_CYCLES_PER_MS = None
+
+
+def gpu_spin(ms):
+    """Occupy the stream for about ``ms`` milliseconds (torch's spin kernel)."""
+    import torch
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(ms * _SPIN_CYCLES_PER_MS))
+
+
+def enqueue_time(bench, i, ev):
+    """Host seconds to enqueue one step (measured behind a GPU spin)."""
+    import torch
+    gpu_spin(50.0)
+    t0 = time.perf_counter()
+    bench.step(i, ev)
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    return t1 - t0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs no multi-GPU path "
+              "(the decode shards by sequence or kv-head with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    import workloads
+    torch.cuda.set_device(0)
+    bench = Bench(workloads.CONFIGS[args.config], args.copies)
+    c = bench.cfg
+    for i in range(args.warmup + bench.copies):
+        bench.step(i)
+    torch.cuda.synchronize()
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [{"q0": mk(), "q1": mk(), "d0": [mk() for _ in range(c.decode_steps)],
+            "d1": [mk() for _ in range(c.decode_steps)]} for _ in range(args.steps)]
+    start, stop = mk(), mk()
+    # The host enqueues slower than these kernels run, so a GPU spin placed
+    # before the timed region lets every step be queued first; the start
+    # event then fires when the spin ends, and each kernel's events bracket
+    # only its own execution.
+    host_per_step = enqueue_time(bench, args.warmup + bench.copies, evs[0])
+    spin_ms = 1.5 * host_per_step * args.steps * 1e3 + 2.0
+    torch.cuda.synchronize()
+    gpu_spin(spin_ms)
+    start.record(bench.stream)
+    base = args.warmup + bench.copies
+    for i in range(args.steps):
+        bench.step(base + i, evs[i])
+    stop.record(bench.stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    qt = sum(e["q0"].elapsed_time(e["q1"]) for e in evs)
+    dt = [sum(e["d0"][s].elapsed_time(e["d1"][s]) for e in evs) for s in range(c.decode_steps)]
+
+    q_ms = qt / args.steps
+    d_ms = sum(dt) / (args.steps * c.decode_steps)
+    kv_logical = sum(bench.decode_bytes(s)[0] for s in range(c.decode_steps)) / c.decode_steps
+    kv_unique = sum(bench.decode_bytes(s, unique=True)[0] for s in range(c.decode_steps)) / c.decode_steps
+    dec_alg = sum(bench.decode_bytes(s, unique=True)[1] for s in range(c.decode_steps)) / c.decode_steps
+    decode_gbps = kv_logical / (d_ms * 1e-3) / 1e9
+    q_alg = bench.quantize_bytes()
+    quant_gbps = q_alg / (q_ms * 1e-3) / 1e9
+    kernels = {
+        "quantize": {"avg_us": q_ms * 1e3, "bytes": q_alg, "GBps": quant_gbps},
+        "decode": {"avg_us": d_ms * 1e3, "bytes": dec_alg, "GBps": dec_alg / (d_ms * 1e-3) / 1e9},
+    }
+    dominant = "quantize" if q_ms >= d_ms * c.decode_steps else "decode"
+    kd = kernels[dominant]
+    traffic = traffic_from_profiles(dominant, None)
+    roof = {"bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
+            "bytes_per_launch": kd["bytes"], "avg_launch_us": round(kd["avg_us"], 2)}
+    other = "decode" if dominant == "quantize" else "quantize"
+    ko = kernels[other]
+    roof_other = {"bound": "hbm", "achieved": round(ko["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": round(ko["GBps"] / HBM_PEAK_GBPS, 4), "kernel": other,
+                  "bytes_per_launch": ko["bytes"], "avg_launch_us": round(ko["avg_us"], 2),
+                  "traffic": traffic_from_profiles(other, None)}
+    res = {
+        "metric": "4-bit KV decode attn: effective KV GB/s & % HBM peak; quantize tokens/s",
+        "value": round(decode_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes; f16 MFMA, f32 softmax",
+        "data": "synthetic (seeded; shapes of the pages' agentic workloads)",
+        "config": {"workload": f"{c.name}: batch {c.batch}, {c.num_q_heads}/{c.num_kv_heads} heads, "
+                               f"head_dim {c.head_dim}, context {int(bench.w.context_lens_at(0).max())}, "
+                               f"format {'TQ4/4' if c.fmt == 0 else 'MX-FP4'}",
+                   "tokens_quantized_per_step": bench.n_tokens, "decode_steps_per_step": c.decode_steps,
+                   "copies": bench.copies},
+        "decode_hbm_frac": round(kv_unique / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decode_us": round(d_ms * 1e3, 2),
+        "quantize_us": round(q_ms * 1e3, 2),
+        "quantize_tokens_per_s": round(bench.n_tokens / (q_ms * 1e-3), 1),
+        "roofline": roof,
+        "roofline_other": roof_other,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.config)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+// Pieces shared by the TQ4/4 and MX-FP4 decode kernels: the query rotation,
+// the online-softmax state and the end-of-work-group merge.
+#pragma once
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+// A running maximum is only raised when a block's maximum exceeds it by more
+// than this (log2 units), so most blocks skip the accumulator rescale; the
+// probabilities then stay below 2^kLazyRescale.
+constexpr float kLazyRescale = 8.0f;
+
+template <int GQ>
+__device__ __forceinline__ float xor_g(float x) {
+  if constexpr (GQ == 1) return xor1(x);
+  else if constexpr (GQ == 2) return xor2(x);
+  else if constexpr (GQ == 4) return xor4(x);
+  else return xor8(x);
+}
+
+// a + b on the lane holding a, a - b on the lane holding b, for lane xor 16 / 32
+__device__ __forceinline__ float bfly16(float x, float sgn) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u(x), as_u(x), false, false);
+  return __builtin_fmaf(sgn, as_f(p[1]), as_f(p[0]));
+}
+__device__ __forceinline__ float bfly32(float x, float sgn) {
+  auto p = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+  return __builtin_fmaf(sgn, as_f(p[1]), as_f(p[0]));
+}
+
+// One wave rotates one query row of D channels: unnormalized Walsh-Hadamard
+// butterflies in fp32 in the stage order h = 1, 2, ..., D/2 (the order the
+// record format fixes).  D = 128: lane l holds channels 2l, 2l+1 (stage h = 1
+// in-lane, h = 2..64 over lane xor 1..32); D = 64: lane l holds channel l.
+template <int D>
+__device__ __forceinline__ void rotate_row(const uint16_t *q, int lane, float &x0, float &x1) {
+  if constexpr (D == 128) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(q)[lane];
+    const float a = bf16_lo(w), b = bf16_hi(w);
+    x0 = a + b;
+    x1 = a - b;
+  } else {
+    x0 = as_f((uint32_t)q[lane] << 16);
+    x1 = 0.f;
+  }
+  const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s4 = (lane & 4) ? -1.f : 1.f;
+  const float s8 = (lane & 8) ? -1.f : 1.f, s16 = (lane & 16) ? -1.f : 1.f, s32 = (lane & 32) ? -1.f : 1.f;
+  x0 = __builtin_fmaf(s1, x0, xor1(x0));
+  x1 = __builtin_fmaf(s1, x1, xor1(x1));
+  x0 = __builtin_fmaf(s2, x0, xor2(x0));
+  x1 = __builtin_fmaf(s2, x1, xor2(x1));
+  x0 = __builtin_fmaf(s4, x0, xor4(x0));
+  x1 = __builtin_fmaf(s4, x1, xor4(x1));
+  x0 = __builtin_fmaf(s8, x0, xor8(x0));
+  x1 = __builtin_fmaf(s8, x1, xor8(x1));
+  x0 = bfly16(x0, s16);
+  x1 = bfly16(x1, s16);
+  x0 = bfly32(x0, s32);
+  x1 = bfly32(x1, s32);
+}
+
+// Channel of element e (0 or 1) of lane l after rotate_row.
+template <int D>
+__device__ __forceinline__ int rotated_channel(int lane, int e) {
+  return D == 128 ? 2 * lane + e : lane;
+}
+
+// Per-wave online-softmax state for the 16 operand columns.  Column n < g is
+// query head n (high fp16 part), g <= n < 2g the same head's low part.
+template <int G2>  // number of PV accumulator tiles (2 * D / 32)
+struct WaveState {
+  float m;          // running reference maximum (log2 units), per column
+  float l;          // running sum of probabilities over this lane's tokens
+  float4v acc[G2];  // out^T tiles: rows = channels, columns = operand columns
+};
+
+// Combine the NW waves of a work-group and write either the output (single
+// split) or a split partial.  s_m / s_l / s_acc are LDS scratch.
+template <int D, int GQ, int NW>
+__device__ __forceinline__ void finish_workgroup(const DecodeArgs &a, WaveState<2 * D / 32> &st, int b, int qh0,
+                                                 int sp, float (*s_m)[GQ], float (*s_l)[GQ],
+                                                 float (*s_acc)[GQ][D]) {
+  constexpr int G = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane >> 4, n = lane & 15;
+  float l = st.l;
+  l += xor16(l);
+  l += xor32(l);
+#pragma unroll
+  for (int t = 0; t < 2 * G; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[t][i] += xor_g<GQ>(st.acc[t][i]);
+  }
+  if (n < GQ) {
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_acc[wv][n][32 * gp + 2 * (4 * r + i) + par] = st.acc[2 * gp + par][i];
+      }
+    }
+    if (r == 0) {
+      s_m[wv][n] = st.m;
+      s_l[wv][n] = l;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * D; i += NW * 64) {
+    const int hh = i / D, c = i % D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = __builtin_fmaxf(mx, s_m[w][hh]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_m[w][hh];
+      const float f = (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
+      num += f * s_acc[w][hh][c];
+      den += f * s_l[w][hh];
+    }
+    const int64_t row = (int64_t)b * a.hq + qh0 + hh;
+    if (a.nsplit == 1) {
+      const float o = den > 0.f ? num / den : 0.f;
+      if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[row * D + c] = f32_to_bf16(o);
+      else reinterpret_cast<float *>(a.out)[row * D + c] = o;
+    } else {
+      const int64_t pi = row * a.nsplit + sp;
+      a.part_acc[pi * D + c] = num;
+      if (c == 0) {
+        a.part_ml[pi * 2] = mx;
+        a.part_ml[pi * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void write_zero_rows(const DecodeArgs &a, int b, int qh0, int gq) {
+  for (int i = threadIdx.x; i < gq * D; i += blockDim.x) {
+    const int64_t o = ((int64_t)b * a.hq + qh0) * D + i;
+    if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[o] = 0;
+    else reinterpret_cast<float *>(a.out)[o] = 0.f;
+  }
+}
+
+}  // namespace tq

@@ -5,36 +5,28 @@
 // q . k unchanged: "TurboQuant 在 AMD GPU 上把長上下文延遲壓下來", section 4),
 // values are dequantized in registers.
 //
-// Work-group = (sequence b, kv-head, split); its 4 waves take the split's
-// blocks in turn, each keeping an online-softmax state, merged in LDS at the
-// end.  Per 16-token block a wave does:
+// Work-group = (sequence b, kv-head, split) with NW waves.  Each wave takes
+// every NW-th block of the split, two blocks of loads in flight, and keeps an
+// online-softmax state; the waves are merged in LDS at the end.  Per 16-token
+// block a wave does:
 //   * one 128-bit load per lane of the key codes (the record places each lane's
 //     MFMA A-operand bytes contiguously), a byte-pair LUT lookup in LDS giving
 //     two exact fp16 table entries per byte;
 //   * logits = K_hat (16 tokens x D) times the rotated query group (D x 16
 //     columns: g columns of fp16 high parts, g of low parts) with
 //     v_mfma_f32_16x16x32_f16, then the per-token key scale;
-//   * online softmax in log2 units (the query carries log2(e));
+//   * online softmax in log2 units (the query carries log2(e)), rescaling the
+//     accumulators only when the running maximum moves by more than 2^8;
 //   * values dequantized to fp16 (code * scale + min, one rounding) and
 //     out^T (channels x columns) += V_hat^T P with v_mfma_f32_16x16x16_f16,
 //     P again split into fp16 high and low parts.
-// Partials (max, sum, acc) per (sequence, query head, split) go to the
-// workspace and a merge kernel combines them; a single split writes the output.
-#include "tq_device.h"
-#include "tq_internal.h"
+// Split partials (max, sum, acc) go to the workspace; decode_merge combines them.
+#include "decode_common.h"
 
 namespace tq {
 namespace {
 
-constexpr float kNegInf = -__builtin_huge_valf();
-
-template <int GQ>
-__device__ __forceinline__ float xor_g(float x) {
-  if constexpr (GQ == 1) return xor1(x);
-  else if constexpr (GQ == 2) return xor2(x);
-  else if constexpr (GQ == 4) return xor4(x);
-  else return xor8(x);
-}
+constexpr int kWaves = 8;
 
 template <int D>
 struct KTile;
@@ -52,284 +44,303 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
 }
 __device__ __forceinline__ uint32_t word(const uint2 &v, int i) { return i == 0 ? v.x : v.y; }
 
-// fp16 values of 4-bit codes: (w & 0x000F000F) | 0x6400_6400 = 1024 + code, exact
-__device__ __forceinline__ half2v nib2(uint32_t w) {
-  const half2v c = as_h2((w & 0x000F000Fu) | 0x64006400u);
-  return c - (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
+// fp16 values (1024 + code) of four 4-bit codes taken from nibble-isolated
+// bytes: v_perm places byte pairs under the 0x64 exponent byte.
+__device__ __forceinline__ half2v magic_pair(uint32_t nib_bytes, uint32_t sel) {
+  return as_h2(__builtin_amdgcn_perm(0x64646464u, nib_bytes, sel));
+}
+
+template <int D>
+struct Blk {
+  typename KTile<D>::T kq;  // key codes: this lane's A-operand bytes
+  uint2 ks;                 // key scales of tokens 4r .. 4r+3
+  typename KTile<D>::T vq;  // value codes: this lane's A-operand bytes
+  uint32_t vmw;             // one dword of the value (scale, min) tile; lane
+                            // (r, c) holds dword c of row r's 16*G bytes
+};
+
+// vm_keep: per-lane mask clearing the (scale, min) halves of rows past the
+// context, so those rows dequantize to exactly 0 whatever the pool holds.
+template <int D>
+__device__ __forceinline__ void load_blk(Blk<D> &o, const uint8_t *rec, int lane, uint32_t vm_keep) {
+  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
+  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
+  const int r = lane >> 4, c = lane & 15;
+  o.kq = *reinterpret_cast<const typename KTile<D>::T *>(rec + lane * Q);
+  o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
+  o.vq = *reinterpret_cast<const typename KTile<D>::T *>(rec + OFF_VC + lane * (4 * G));
+  o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))] & vm_keep;
+}
+
+// vm_slot: this wave's 16*D/8-byte LDS slot for the value (scale, min) tile.
+template <int D, int GQ>
+__device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D / 32], const uint32_t *s_lut,
+                                         uint32_t *vm_slot, WaveState<2 * D / 32> &st, float lo_mask, int lane,
+                                         int tok0, int T, bool tail) {
+  constexpr int G = D / 32, KS = D / 32;
+  // the value (scale, min) tile goes through LDS: lane (r, c) wrote dword c of
+  // row r; every lane reads its row's 16*G bytes back (broadcast reads)
+  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = bk.vmw;
+  // ---- logits ---------------------------------------------------------------
+  float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint32_t w = word(bk.kq, s);
+    uint4 e;
+    e.x = s_lut[w & 0xFF];
+    e.y = s_lut[(w >> 8) & 0xFF];
+    e.z = s_lut[(w >> 16) & 0xFF];
+    e.w = s_lut[w >> 24];
+    qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, e), bq[s], qk, 0, 0, 0);
+  }
+  const half2v s01 = as_h2(bk.ks.x), s23 = as_h2(bk.ks.y);
+  float x[4];
+  x[0] = (qk[0] + xor_g<GQ>(qk[0])) * (float)s01[0];
+  x[1] = (qk[1] + xor_g<GQ>(qk[1])) * (float)s01[1];
+  x[2] = (qk[2] + xor_g<GQ>(qk[2])) * (float)s23[0];
+  x[3] = (qk[3] + xor_g<GQ>(qk[3])) * (float)s23[1];
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (tok0 + i >= T) x[i] = kNegInf;
+  }
+
+  // ---- online softmax with lazy rescale ----------------------------------------
+  float bm = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
+  bm = __builtin_fmaxf(bm, xor16(bm));
+  bm = __builtin_fmaxf(bm, xor32(bm));
+  const bool raise = bm > st.m + kLazyRescale;
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float m_new = raise ? bm : st.m;
+    const float alpha = (st.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < 2 * G; ++t) st.acc[t] *= alpha;
+    st.m = m_new;
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  // B operand: k-slot order tokens 4r + (0, 2, 1, 3); high part on columns < g,
+  // low part (p - high) on columns g .. 2g-1; other columns are never read
+  half4v bp;
+  {
+    const half2v h02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[2]));
+    const half2v h13 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[1], p[3]));
+    const float r0 = __builtin_fmaf(-lo_mask, (float)h02[0], p[0]);
+    const float r2 = __builtin_fmaf(-lo_mask, (float)h02[1], p[2]);
+    const float r1 = __builtin_fmaf(-lo_mask, (float)h13[0], p[1]);
+    const float r3 = __builtin_fmaf(-lo_mask, (float)h13[1], p[3]);
+    const half2v a02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r2));
+    const half2v a13 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r1, r3));
+    bp = (half4v){a02[0], a02[1], a13[0], a13[1]};
+  }
+
+  // ---- values -----------------------------------------------------------------
+  const half2v k1024 = (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
+  const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
+#pragma unroll
+  for (int gp = 0; gp < G; ++gp) {
+    const uint32_t w = word(bk.vq, gp);
+    const uint4 vm = vm_row[gp];
+    // bytes = tokens 4r + 0..3 of one channel pair; low nibble = even channel
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const half2v sc02 = as_h2(vm.x), sc13 = as_h2(vm.y);
+    const half2v mn02 = as_h2(vm.z), mn13 = as_h2(vm.w);
+    const half2v e02 = __builtin_elementwise_fma(magic_pair(lo, 0x04020400u) - k1024, sc02, mn02);
+    const half2v e13 = __builtin_elementwise_fma(magic_pair(lo, 0x04030401u) - k1024, sc13, mn13);
+    const half2v o02 = __builtin_elementwise_fma(magic_pair(hi, 0x04020400u) - k1024, sc02, mn02);
+    const half2v o13 = __builtin_elementwise_fma(magic_pair(hi, 0x04030401u) - k1024, sc13, mn13);
+    const half4v ae = __builtin_bit_cast(half4v, make_uint2(as_u(e02), as_u(e13)));
+    const half4v ao = __builtin_bit_cast(half4v, make_uint2(as_u(o02), as_u(o13)));
+    st.acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x16f16(ae, bp, st.acc[2 * gp], 0, 0, 0);
+    st.acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ao, bp, st.acc[2 * gp + 1], 0, 0, 0);
+  }
 }
 
 template <int D, int GQ>
-__global__ __launch_bounds__(256) void tq4_decode_kernel(DecodeArgs a) {
-  constexpr int G = D / 32;
-  constexpr int KS = D / 32;          // 32-channel k-steps of the QK product
-  constexpr int Q = D / 8;            // key-code bytes per lane
-  constexpr int P16 = 16 * (D / 2);
-  constexpr int OFF_KS = P16;
-  constexpr int OFF_VC = OFF_KS + 32;
-  constexpr int OFF_VM = OFF_VC + P16;
-  constexpr int REC = OFF_VM + 64 * G;
-  typedef typename KTile<D>::T KT;
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void tq4_decode_kernel(
+    DecodeArgs a) {
+  constexpr int G = D / 32, KS = D / 32;
+  constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
+  constexpr int NW = kWaves;
 
   __shared__ uint32_t s_lut[256];
-  __shared__ float s_q[GQ][D];
-  __shared__ float s_m[4][GQ], s_l[4][GQ];
-  __shared__ float s_acc[4][GQ][D];
+  __shared__ __attribute__((aligned(16))) uint32_t s_vm[NW][64];
+  __shared__ __attribute__((aligned(16))) _Float16 s_bq[16][D];
+  __shared__ float s_m[NW][GQ], s_l[NW][GQ];
+  __shared__ float s_acc[NW][GQ][D];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: block ids load as scalars
   const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int b = (int)(wg % (uint32_t)a.batch);
   const uint32_t rest = wg / (uint32_t)a.batch;
   const int kvh = (int)(rest % (uint32_t)a.hkv);
   const int sp = (int)(rest / (uint32_t)a.hkv);
+  const int qh0 = kvh * GQ;
 
   const int T = a.ctx[b];
   const int nblk = (T + 15) >> 4;
   const int blk0 = sp * a.split_blocks;
-  const bool single = a.nsplit == 1;
-  const int qh0 = kvh * GQ;
   if (nblk == 0) {
-    if (single && sp == 0) {
-      for (int i = tid; i < GQ * D; i += 256) {
-        const int64_t o = ((int64_t)b * a.hq + qh0) * D + i;
-        if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[o] = 0;
-        else reinterpret_cast<float *>(a.out)[o] = 0.f;
-      }
-    }
+    if (a.nsplit == 1 && sp == 0) write_zero_rows<D>(a, b, qh0, GQ);
     return;
   }
   if (blk0 >= nblk) return;
   const int blk1 = min(nblk, blk0 + a.split_blocks);
 
-  // ---- stage the LUT and the rotated, scaled query group ----------------------
-  s_lut[tid] = a.tables->lut2[tid];
-  for (int i = tid; i < GQ * D; i += 256) {
-    const uint16_t qb = a.q[((int64_t)b * a.hq + qh0) * D + i];
-    s_q[i / D][i % D] = as_f((uint32_t)qb << 16);
-  }
-  __syncthreads();
-#pragma unroll 1
-  for (int hs = 1; hs < D; hs <<= 1) {
-    for (int i = tid; i < GQ * D / 2; i += 256) {
-      const int hh = i / (D / 2), pi = i % (D / 2);
-      const int lo = (pi / hs) * (2 * hs) + (pi % hs);
-      const float x0 = s_q[hh][lo], x1 = s_q[hh][lo + hs];
-      s_q[hh][lo] = x0 + x1;
-      s_q[hh][lo + hs] = x0 - x1;
-    }
-    __syncthreads();
-  }
-
-  const int lane = tid & 63, wv = tid >> 6;
-  const int r = lane >> 4, n = lane & 15;
-
-  // B operand of the QK product: column n < g is head n's high fp16 part,
-  // g <= n < 2g head n-g's low part; lane (r, n) holds channels r*D/4 + 8s + i.
-  half8v bq[KS];
-  {
-    const bool used = n < 2 * GQ;
-    const bool is_lo = n >= GQ;
-    const int hh = is_lo ? n - GQ : n;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xv = used ? s_q[used ? hh : 0][r * (D / 4) + 8 * s + i] * a.qscale : 0.f;
-        const _Float16 hi = (_Float16)xv;
-        const _Float16 lo = (_Float16)(xv - (float)hi);
-        bq[s][i] = used ? (is_lo ? lo : hi) : (_Float16)0.f;
-      }
-    }
-  }
-  const bool col_lo = n >= GQ && n < 2 * GQ;
-  const bool col_used = n < 2 * GQ;
-
-  float m_run = kNegInf, l_run = 0.f;
-  float4v acc[2 * G];
-#pragma unroll
-  for (int t = 0; t < 2 * G; ++t) acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
-
+  // ---- first loads go out before the set-up work -----------------------------
   const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
-#pragma unroll 1
-  for (int lb = blk0 + wv; lb < blk1; lb += 4) {
-    const int pid = btab[lb];
-    const uint8_t *rec = a.pool + ((int64_t)pid * a.hkv + kvh) * REC;
-    const KT kq = *reinterpret_cast<const KT *>(rec + lane * Q);
-    const uint2 ksv = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
-    const KT vq = *reinterpret_cast<const KT *>(rec + OFF_VC + lane * (4 * G));
-    uint4 vm[G];
-#pragma unroll
-    for (int gp = 0; gp < G; ++gp) vm[gp] = *reinterpret_cast<const uint4 *>(rec + OFF_VM + (r * G + gp) * 16);
-
-    // ---- logits ---------------------------------------------------------------
-    float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint32_t w = word(kq, s);
-      uint4 e;
-      e.x = s_lut[w & 0xFF];
-      e.y = s_lut[(w >> 8) & 0xFF];
-      e.z = s_lut[(w >> 16) & 0xFF];
-      e.w = s_lut[w >> 24];
-      qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, e), bq[s], qk, 0, 0, 0);
-    }
-    const half2v s01 = as_h2(ksv.x), s23 = as_h2(ksv.y);
-    const float ks[4] = {(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
-    float x[4];
-    const int tok0 = lb * 16 + 4 * r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (qk[i] + xor_g<GQ>(qk[i])) * ks[i];
-      if (tok0 + i >= T) x[i] = kNegInf;
-    }
-
-    // ---- online softmax ---------------------------------------------------------
-    float bm = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
-    bm = __builtin_fmaxf(bm, xor16(bm));
-    bm = __builtin_fmaxf(bm, xor32(bm));
-    const float m_new = __builtin_fmaxf(m_run, bm);
-    if (m_new > m_run) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < 2 * G; ++t) acc[t] *= alpha;
-      m_run = m_new;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    half4v bp;
-    {
-      // k-slot order of the value operand: tokens 4r + (0, 2, 1, 3)
-      const float pk[4] = {p[0], p[2], p[1], p[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 hi = (_Float16)pk[i];
-        const _Float16 lo = (_Float16)(pk[i] - (float)hi);
-        bp[i] = col_used ? (col_lo ? lo : hi) : (_Float16)0.f;
-      }
-    }
-
-    // ---- values -----------------------------------------------------------------
-    const bool tail = (lb + 1) * 16 > T;
-#pragma unroll
-    for (int gp = 0; gp < G; ++gp) {
-      const uint32_t w = word(vq, gp);
-      const half2v sc02 = as_h2(vm[gp].x), sc13 = as_h2(vm[gp].y);
-      const half2v mn02 = as_h2(vm[gp].z), mn13 = as_h2(vm[gp].w);
-      half2v e02 = __builtin_elementwise_fma(nib2(w), sc02, mn02);
-      half2v e13 = __builtin_elementwise_fma(nib2(w >> 8), sc13, mn13);
-      half2v o02 = __builtin_elementwise_fma(nib2(w >> 4), sc02, mn02);
-      half2v o13 = __builtin_elementwise_fma(nib2(w >> 12), sc13, mn13);
-      if (tail) {
-        // rows past the context may hold anything; zero them (p is 0 there)
-        const bool v0 = tok0 + 0 < T, v1 = tok0 + 1 < T, v2 = tok0 + 2 < T, v3 = tok0 + 3 < T;
-        const _Float16 z = (_Float16)0.f;
-        e02 = (half2v){v0 ? e02[0] : z, v2 ? e02[1] : z};
-        o02 = (half2v){v0 ? o02[0] : z, v2 ? o02[1] : z};
-        e13 = (half2v){v1 ? e13[0] : z, v3 ? e13[1] : z};
-        o13 = (half2v){v1 ? o13[0] : z, v3 ? o13[1] : z};
-      }
-      const half4v ae = (half4v){e02[0], e02[1], e13[0], e13[1]};
-      const half4v ao = (half4v){o02[0], o02[1], o13[0], o13[1]};
-      acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x16f16(ae, bp, acc[2 * gp], 0, 0, 0);
-      acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ao, bp, acc[2 * gp + 1], 0, 0, 0);
-    }
+  const uint8_t *base = a.pool + (int64_t)kvh * REC;
+  const int64_t stride = (int64_t)a.hkv * REC;
+  // this wave's blocks: blk0 + wv + k * NW, k < mine (mine <= 64); lane k
+  // holds block id k, read back with readlane.  Four blocks stay in flight:
+  // every step refills its buffer unconditionally (past the end with the
+  // wave's last block again, an L2 hit), so the number of loads in flight is
+  // the same on every path and the waits stay partial.
+  const int mine = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
+  const int my_id = btab[blk0 + wv + (lane < mine ? lane : 0) * NW];
+  auto rec_of = [&](int k) {
+    const int kk = k < mine ? k : mine - 1;
+    return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
+  };
+  // rows of the partial last block past the context get zero (scale, min)
+  const int tail_blk = (T & 15) ? nblk - 1 : nblk;
+  uint32_t tail_keep;
+  {
+    const int r0 = 4 * (lane >> 4), w = lane & 3;  // dword w of a group: SC02 SC13 MN02 MN13
+    const int ta = (T & 15) - (r0 + (w & 1)), tb = ta - 2;
+    tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
+  }
+  auto keep_of = [&](int k) { return blk0 + wv + (k < mine ? k : mine - 1) * NW == tail_blk ? tail_keep : ~0u; };
+  Blk<D> b0, b1, b2, b3;
+  if (mine > 0) {
+    load_blk<D>(b0, rec_of(0), lane, keep_of(0));
+    load_blk<D>(b1, rec_of(1), lane, keep_of(1));
+    load_blk<D>(b2, rec_of(2), lane, keep_of(2));
+    load_blk<D>(b3, rec_of(3), lane, keep_of(3));
   }
 
-  // ---- wave state -> LDS: combine high and low columns, sum over lane rows -------
-  l_run += xor16(l_run);
-  l_run += xor32(l_run);
+  // ---- LUT and the rotated, scaled query group (wave w < g rotates head w) ------
+  if (tid < 256) s_lut[tid] = a.tables->lut2[tid];
+  for (int i = tid; i < (16 - 2 * GQ) * D; i += NW * 64) s_bq[2 * GQ + i / D][i % D] = (_Float16)0.f;
+  if (wv < GQ) {
+    float x0, x1;
+    rotate_row<D>(a.q + ((int64_t)b * a.hq + qh0 + wv) * D, lane, x0, x1);
 #pragma unroll
-  for (int t = 0; t < 2 * G; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] += xor_g<GQ>(acc[t][i]);
-  }
-  if (n < GQ) {
-#pragma unroll
-    for (int gp = 0; gp < G; ++gp) {
-#pragma unroll
-      for (int par = 0; par < 2; ++par) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_acc[wv][n][32 * gp + 2 * (4 * r + i) + par] = acc[2 * gp + par][i];
-      }
-    }
-    if (r == 0) {
-      s_m[wv][n] = m_run;
-      s_l[wv][n] = l_run;
+    for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
+      const float xs = (e ? x1 : x0) * a.qscale;
+      const _Float16 hi = (_Float16)xs;
+      const _Float16 lo = (_Float16)(xs - (float)hi);
+      const int c = rotated_channel<D>(lane, e);
+      s_bq[wv][c] = hi;
+      s_bq[wv + GQ][c] = lo;
     }
   }
   __syncthreads();
 
-  // ---- merge the 4 waves ----------------------------------------------------------
-  for (int i = tid; i < GQ * D; i += 256) {
-    const int hh = i / D, c = i % D;
-    float mx = kNegInf;
+  const int r = lane >> 4, n = lane & 15;
+  half8v bq[KS];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = __builtin_fmaxf(mx, s_m[w][hh]);
-    float num = 0.f, den = 0.f;
+  for (int s = 0; s < KS; ++s) bq[s] = *reinterpret_cast<const half8v *>(&s_bq[n][r * (D / 4) + 8 * s]);
+  const float lo_mask = (n >= GQ && n < 2 * GQ) ? 1.f : 0.f;
+
+  WaveState<2 * G> st;
+  st.m = kNegInf;
+  st.l = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = (s_m[w][hh] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][hh] - mx);
-      num += f * s_acc[w][hh][c];
-      den += f * s_l[w][hh];
+  for (int t = 0; t < 2 * G; ++t) st.acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  // process buffer k (if it is one of this wave's blocks), then refill it
+  uint32_t *vm_slot = s_vm[wv];
+  auto run = [&](Blk<D> &buf, int k) {
+    if (k < mine) {
+      const int blk = blk0 + wv + k * NW;
+      do_block<D, GQ>(buf, bq, s_lut, vm_slot, st, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk);
     }
-    const int64_t row = (int64_t)b * a.hq + qh0 + hh;
-    if (single) {
-      const float o = den > 0.f ? num / den : 0.f;
-      if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[row * D + c] = f32_to_bf16(o);
-      else reinterpret_cast<float *>(a.out)[row * D + c] = o;
-    } else {
-      const int64_t pi = row * a.nsplit + sp;
-      a.part_acc[pi * D + c] = num;
-      if (c == 0) {
-        a.part_ml[pi * 2] = mx;
-        a.part_ml[pi * 2 + 1] = den;
-      }
-    }
+    load_blk<D>(buf, rec_of(k + 4), lane, keep_of(k + 4));
+  };
+#pragma unroll 1
+  for (int k = 0; k < mine; k += 4) {
+    run(b0, k);
+    run(b1, k + 1);
+    run(b2, k + 2);
+    run(b3, k + 3);
   }
+
+  finish_workgroup<D, GQ, NW>(a, st, b, qh0, sp, s_m, s_l, s_acc);
 }
 
-// One wave per (sequence, query head): combine the split partials.
+// One work-group per (sequence, query head): combine the split partials.
+// Pass 1 finds the largest partial maximum; in pass 2 thread t takes channels
+// 4*(t % (D/4)) .. +3 of splits s = t / (D/4) (mod 256 / (D/4)) with weights
+// exp2(m_s - M) (independent loads), and the slices are summed in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int CPL = D / 64;  // channels per lane
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.batch * a.hq) return;
-  const int lane = threadIdx.x & 63;
+  constexpr int CQ = D / 4;          // channel quads
+  constexpr int SL = 256 / CQ;       // split lanes
+  __shared__ float s_red[256];
+  __shared__ float s_l[SL];
+  __shared__ float4 s_acc[SL][CQ];
+  const int64_t row = blockIdx.x;
   const int b = (int)(row / a.hq);
   const int T = a.ctx[b];
   const int nblk = (T + 15) >> 4;
   const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
+  const int tid = threadIdx.x, cq = tid % CQ, sl = tid / CQ;
   const float *ml = a.part_ml + row * a.nsplit * 2;
   const float *pa = a.part_acc + row * a.nsplit * D;
   float mx = kNegInf;
-  for (int s = 0; s < ns; ++s) mx = __builtin_fmaxf(mx, ml[2 * s]);
-  float num[CPL] = {}, den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float m = ml[2 * s];
-    const float f = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
-    den += f * ml[2 * s + 1];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) num[c] += f * pa[(int64_t)s * D + lane * CPL + c];
+  for (int s = tid; s < ns; s += 256) mx = __builtin_fmaxf(mx, ml[2 * s]);
+  s_red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] = __builtin_fmaxf(s_red[tid], s_red[tid + w]);
+    __syncthreads();
   }
+  const float M = s_red[0];
+  float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int s = sl; s < ns; s += SL) {
+    const float m = ml[2 * s], l = ml[2 * s + 1];
+    const float4 v = *reinterpret_cast<const float4 *>(pa + (int64_t)s * D + 4 * cq);
+    const float f = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    den += f * l;
+    num.x += f * v.x; num.y += f * v.y; num.z += f * v.z; num.w += f * v.w;
+  }
+  if (cq == 0) s_l[sl] = den;
+  s_acc[sl][cq] = num;
+  __syncthreads();
+  if (sl == 0) {
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < SL; ++i) {
+      L += s_l[i];
+      o.x += s_acc[i][cq].x; o.y += s_acc[i][cq].y; o.z += s_acc[i][cq].z; o.w += s_acc[i][cq].w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const float o = den > 0.f ? num[c] / den : 0.f;
-    const int64_t oi = row * D + lane * CPL + c;
-    if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(o);
-    else reinterpret_cast<float *>(a.out)[oi] = o;
+    for (int c = 0; c < 4; ++c) {
+      const int64_t oi = row * D + 4 * cq + c;
+      if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(ov[c]);
+      else reinterpret_cast<float *>(a.out)[oi] = ov[c];
+    }
   }
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.nsplit;
+  const dim3 grid((unsigned)wgs), block(kWaves * 64);
   switch (a.g) {
-    case 1: hipLaunchKernelGGL((tq4_decode_kernel<D, 1>), dim3((unsigned)wgs), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((tq4_decode_kernel<D, 2>), dim3((unsigned)wgs), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((tq4_decode_kernel<D, 4>), dim3((unsigned)wgs), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((tq4_decode_kernel<D, 8>), dim3((unsigned)wgs), dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((tq4_decode_kernel<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((tq4_decode_kernel<D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((tq4_decode_kernel<D, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((tq4_decode_kernel<D, 8>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -342,10 +353,9 @@ hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.batch * a.hq;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (d == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)((int64_t)a.batch * a.hq)), block(256);
+  if (d == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

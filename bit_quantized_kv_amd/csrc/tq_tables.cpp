@@ -148,20 +148,21 @@ bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *
   return false;
 }
 
-// Split-K plan: blocks per work-group (a multiple of the 4 waves) chosen so
-// that the grid has several work-groups per compute unit, bounded below so
-// the partials stay small against the KV bytes, and above for load balance.
+// Split-K plan: blocks per work-group (a multiple of its 8 waves) chosen so
+// that a small batch still spreads over about two work-groups per compute
+// unit, bounded above so long contexts keep several splits for load balance.
+// The partials it implies are below 3% of the KV bytes for every shape.
 SplitPlan plan_split(int batch, int hkv, int max_context_len) {
   const int64_t max_nblk = ((int64_t)max_context_len + 15) / 16;
   const int64_t units = (int64_t)batch * hkv;
-  const int64_t target_wgs = 256 * 6;
+  const int64_t target_wgs = 256 * 2;
   int64_t s = (units * max_nblk + target_wgs - 1) / target_wgs;
-  s = ((s + 3) / 4) * 4;
-  if (s < 8) s = 8;
-  if (s > 64) s = 64;
+  s = ((s + 7) / 8) * 8;
+  if (s < 16) s = 16;
+  if (s > 128) s = 128;
   if (const char *env = std::getenv("TQ_SPLIT_BLOCKS")) {
     const long v = std::strtol(env, nullptr, 10);
-    if (v >= 4 && v <= 4096) s = v;
+    if (v >= 1 && v <= 65536) s = v;
   }
   SplitPlan p;
   p.split_blocks = (int)s;
