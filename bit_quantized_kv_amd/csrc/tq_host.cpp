@@ -242,7 +242,10 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
     a.part_acc = a.part_ml + (size_t)batch * num_q_heads * p.nsplit * 2;
   }
   const double log2e = 1.4426950408889634074;
-  a.qscale = (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)));
+  a.rsqrt_d = (float)(1.0 / std::sqrt((double)d));
+  a.qscale = cache->desc.format == TQ_FORMAT_TQ4
+                 ? (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)))
+                 : (float)((double)softmax_scale * log2e);
   a.max_blocks = max_blocks;
   a.batch = batch;
   a.hq = num_q_heads;

@@ -43,7 +43,8 @@ struct DecodeArgs {
   const DeviceTables *tables;
   float *part_ml;                // [batch][hq][nsplit][2] (max, sum) in log2 units
   float *part_acc;               // [batch][hq][nsplit][d]
-  float qscale;                  // softmax_scale * log2(e) * fp32(1/sqrt(d))
+  float qscale;                  // TQ4/4: softmax_scale * log2(e) * fp32(1/sqrt(d)); MX-FP4: softmax_scale * log2(e)
+  float rsqrt_d;                 // fp32(1/sqrt(d)), the rotation's normalization (MX-FP4 query)
   int32_t max_blocks, batch, hq, hkv, g;
   int32_t split_blocks;          // blocks per work-group
   int32_t nsplit;                // splits per (sequence, kv-head)

@@ -49,7 +49,7 @@ class Case:
         """Token ranges that write every cached token once (see workloads)."""
         return self.w.write_plan(lens)
 
-    def quantize(self, ranges, chunk_tokens=1 << 22):
+    def quantize(self, ranges, chunk_tokens=1 << 18):
         """One quantize call per chunk of concatenated token ranges."""
         ks, vs, ss, n = [], [], [], 0
         for b, t0, t1 in ranges:
