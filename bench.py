@@ -168,9 +168,10 @@ class Bench:
                 ev["d1"][s].record(self.stream)
 
 
-def cpu_baseline(cfg_name):
+def cpu_baseline(cfg_name, budget_s=10.0):
     """The CPU oracle, as it stands, on a bounded sample of the workload:
-    quantize kv-head 0 of the first sequence and decode its query heads."""
+    (sequence, kv-head) units in order, each quantized and then decoded for
+    its g query heads, until about ``budget_s`` seconds of CPU work."""
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:
@@ -180,20 +181,34 @@ def cpu_baseline(cfg_name):
     w = workloads.make(cfg_name)
     c = w.cfg
     g = c.num_q_heads // c.num_kv_heads
-    b = 0
-    T = int(w.context_lens_at(0)[b])
-    k, v = w.sequence_kv(b)
+    lens = w.context_lens_at(0)
+    q_all = workloads.bf16_bits_to_f32(w.query_bits(0))
+    tq = td = 0.0
+    toks = units = 0
     ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
     if ctx_mgr:
         ctx_mgr.__enter__()
     try:
-        pool = paged.PagedPool(c.fmt, w.num_blocks, 1, c.head_dim)
-        t0 = time.perf_counter()
-        pool.append(workloads.bf16_bits_to_f32(k[:T, :1]), workloads.bf16_bits_to_f32(v[:T, :1]), w.slots(b, 0, T))
-        t1 = time.perf_counter()
-        q = workloads.bf16_bits_to_f32(w.query_bits(0))[:, :g]
-        attention.decode(pool, q, w.block_table, w.context_lens_at(0), c.scale, rows=[(b, h) for h in range(g)])
-        t2 = time.perf_counter()
+        for b in range(c.batch):
+            T = int(lens[b])
+            k, v = w.sequence_kv(b)
+            for h in range(c.num_kv_heads):
+                pool = paged.PagedPool(c.fmt, w.num_blocks, 1, c.head_dim)
+                t0 = time.perf_counter()
+                pool.append(workloads.bf16_bits_to_f32(k[:T, h:h + 1]), workloads.bf16_bits_to_f32(v[:T, h:h + 1]),
+                            w.slots(b, 0, T))
+                t1 = time.perf_counter()
+                attention.decode(pool, q_all[:, h * g:(h + 1) * g], w.block_table, lens, c.scale,
+                                 rows=[(b, j) for j in range(g)])
+                t2 = time.perf_counter()
+                tq += t1 - t0
+                td += t2 - t1
+                toks += T
+                units += 1
+                if tq + td >= budget_s:
+                    break
+            if tq + td >= budget_s:
+                break
     finally:
         if ctx_mgr:
             ctx_mgr.__exit__(None, None, None)
@@ -201,19 +216,22 @@ def cpu_baseline(cfg_name):
     if c.fmt == 1:
         row = 136
     return {
-        "value": T * row / (t2 - t1) / 1e9,
+        "value": toks * row / td / 1e9,
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{cfg_name}: sequence 0, kv-head 0 ({T} tokens): quantize {t1 - t0:.2f} s, "
-                  f"decode of its {g} query heads {t2 - t1:.2f} s (numpy, BLAS limited to 1 thread)",
-        "quantize_tokens_per_s": T / (t1 - t0) / c.num_kv_heads,
+        "sample": f"{cfg_name}: {units} (sequence, kv-head) units, {toks} token-heads: quantize {tq:.2f} s, "
+                  f"decode of their {g} query heads each {td:.2f} s (numpy fp64, BLAS limited to 1 thread)",
+        "quantize_tokens_per_s": toks / tq / c.num_kv_heads,
     }
 
 
-def traffic_from_profiles(kernel_key, launch_bytes_fn):
-    """HBM bytes per launch from committed counter runs, if they were taken on
-    the current kernel sources (else None)."""
+def traffic_from_profiles(cfg_name, kernel):
+    """HBM bytes per launch of ``kernel`` ("quantize": the bulk quantize
+    dispatch; "decode": the decode kernel plus its merge) from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs, each scaled by what the counter
+    reads for a plain copy of known size.  None unless the counters were
+    taken on the current kernel sources."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -221,8 +239,14 @@ def traffic_from_profiles(kernel_key, launch_bytes_fn):
         d = json.load(open(path))
         if d.get("kernel_source_hash") != kernel_source_hash():
             return None
-        e = d["kernels"][kernel_key]
-        return (e["fetch_kib_per_dispatch"] * d["fetch_scale"] + e["write_kib_per_dispatch"] * d["write_scale"]) * 1024
+        ents = d["workloads"][cfg_name]
+        def hbm(e):
+            return (e["fetch_kib_per_dispatch"] * d["fetch_scale"] + e["write_kib_per_dispatch"] * d["write_scale"]) * 1024
+        if kernel == "quantize":
+            cands = [(int(k.split("|")[1]), e) for k, e in ents.items() if "quantize_kernel" in k]
+            return round(hbm(max(cands, key=lambda x: x[0])[1])) if cands else None
+        parts = [e for k, e in ents.items() if "decode" in k]
+        return round(sum(hbm(e) for e in parts)) if parts else None
     except Exception:
         return None
 
@@ -309,7 +333,7 @@ def main():
     }
     dominant = "quantize" if q_ms >= d_ms * c.decode_steps else "decode"
     kd = kernels[dominant]
-    traffic = traffic_from_profiles(dominant, None)
+    traffic = traffic_from_profiles(args.config, dominant)
     roof = {"bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
             "bytes_per_launch": kd["bytes"], "avg_launch_us": round(kd["avg_us"], 2)}
@@ -318,7 +342,7 @@ def main():
     roof_other = {"bound": "hbm", "achieved": round(ko["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": round(ko["GBps"] / HBM_PEAK_GBPS, 4), "kernel": other,
                   "bytes_per_launch": ko["bytes"], "avg_launch_us": round(ko["avg_us"], 2),
-                  "traffic": traffic_from_profiles(other, None)}
+                  "traffic": traffic_from_profiles(args.config, other)}
     res = {
         "metric": "4-bit KV decode attn: effective KV GB/s & % HBM peak; quantize tokens/s",
         "value": round(decode_gbps, 1),
