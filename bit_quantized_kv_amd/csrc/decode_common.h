@@ -13,6 +13,17 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // probabilities then stay below 2^kLazyRescale.
 constexpr float kLazyRescale = 8.0f;
 
+// A copy of a loaded value made by a VALU move the compiler cannot see
+// through.  Reading the copy later (v_readlane in the block loop) then carries
+// no dependency on an outstanding vector load, so the compiler's wait before
+// it does not drain the loads in flight (it emits vmcnt(0) for the loaded
+// register itself).
+__device__ __forceinline__ int settled(int x) {
+  int y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+
 template <int GQ>
 __device__ __forceinline__ float xor_g(float x) {
   if constexpr (GQ == 1) return xor1(x);
@@ -35,15 +46,20 @@ __device__ __forceinline__ float bfly32(float x, float sgn) {
 // butterflies in fp32 in the stage order h = 1, 2, ..., D/2 (the order the
 // record format fixes).  D = 128: lane l holds channels 2l, 2l+1 (stage h = 1
 // in-lane, h = 2..64 over lane xor 1..32); D = 64: lane l holds channel l.
+// `w` is this lane's query word (load_query_word).
 template <int D>
-__device__ __forceinline__ void rotate_row(const uint16_t *q, int lane, float &x0, float &x1) {
+__device__ __forceinline__ uint32_t load_query_word(const uint16_t *q, int lane) {
+  if constexpr (D == 128) return reinterpret_cast<const uint32_t *>(q)[lane];
+  else return (uint32_t)q[lane];
+}
+template <int D>
+__device__ __forceinline__ void rotate_row(uint32_t w, int lane, float &x0, float &x1) {
   if constexpr (D == 128) {
-    const uint32_t w = reinterpret_cast<const uint32_t *>(q)[lane];
     const float a = bf16_lo(w), b = bf16_hi(w);
     x0 = a + b;
     x1 = a - b;
   } else {
-    x0 = as_f((uint32_t)q[lane] << 16);
+    x0 = as_f(w << 16);
     x1 = 0.f;
   }
   const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s4 = (lane & 4) ? -1.f : 1.f;
@@ -66,6 +82,24 @@ __device__ __forceinline__ void rotate_row(const uint16_t *q, int lane, float &x
 template <int D>
 __device__ __forceinline__ int rotated_channel(int lane, int e) {
   return D == 128 ? 2 * lane + e : lane;
+}
+
+// Work-group -> (sequence, kv-head, split).  Logical ids (after the XCD remap,
+// which gives each XCD a contiguous range) run split-fastest, then sequence,
+// then kv-head: each XCD gets whole kv-heads (every split of every sequence),
+// so the XCDs carry equal work whatever the context lengths, and sequences
+// that share prefix blocks read them through the same L2.
+struct WgTask {
+  int b, kvh, sp;
+};
+__device__ __forceinline__ WgTask decode_task(const DecodeArgs &a) {
+  const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+  WgTask t;
+  t.sp = (int)(wg % (uint32_t)a.nsplit);
+  const uint32_t rest = wg / (uint32_t)a.nsplit;
+  t.b = (int)(rest % (uint32_t)a.batch);
+  t.kvh = (int)(rest / (uint32_t)a.batch);
+  return t;
 }
 
 // Per-wave online-softmax state for the 16 operand columns.  Column n < g is

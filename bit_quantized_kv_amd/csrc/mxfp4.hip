@@ -27,98 +27,103 @@ constexpr int kOffKs = 1024, kOffVc = 1088, kOffVs = 2112;
 
 // ---- quantize -----------------------------------------------------------------
 
-// Shared exponent and e2m1 codes of one lane's 8 values; the group's amax is
-// reduced over the 4 lanes of a 32-channel group (lane xor 1, 2).
-__device__ __forceinline__ uint32_t mx_encode8(const float (&y)[8], int &xexp) {
-  float am = 0.f;
+// Shared exponent and e2m1 codes of one lane's 16 values (two words, channel
+// e in nibble e % 8 of word e / 8); the group's amax is reduced over the two
+// lanes of a 32-channel group (lane ^ 1).  Keys (KEY): y = fp32(z * mul) with
+// mul = 1/sqrt(D) times the butterflies' sign, computed as fma(z, mul, +0) so
+// that an exact zero is +0 (the record format stores rotated zeros as +0);
+// values are encoded as they are, zero signs kept.
+template <bool KEY>
+__device__ __forceinline__ uint2 mx_encode16(const float (&y)[16], float mul, int &xexp) {
+  float t[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(y[e]));
+  for (int e = 0; e < 16; ++e) t[e] = KEY ? __builtin_fmaf(y[e], mul, 0.0f) : y[e];
+  float am = __builtin_fabsf(t[0]);
+#pragma unroll
+  for (int e = 1; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(t[e]));
   am = __builtin_fmaxf(am, xor1(am));
-  am = __builtin_fmaxf(am, xor2(am));
   int x = -127;
   if (am > 0.f) x = __builtin_amdgcn_frexp_expf(am) - 1 - 2;  // floor(log2 amax) - 2
   x = x < -127 ? -127 : (x > 127 ? 127 : x);
   xexp = x;
-  // 2^-127 is not a normal fp32 scale: pre-multiply by 2^127 instead (exact)
-  const float pre = x == -127 ? 0x1p127f : 1.0f;
-  const float scale = x == -127 ? 1.0f : as_f((uint32_t)(x + 127) << 23);
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * pre, y[1] * pre, scale, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * pre, y[3] * pre, scale, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * pre, y[5] * pre, scale, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * pre, y[7] * pre, scale, 3);
+  // 2^-127 is not a normal fp32 scale: pre-multiply by 2^127 instead (exact;
+  // only tiny groups take this path)
+  float scale = as_f((uint32_t)(x + 127) << 23);
+  if (x == -127) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] *= 0x1p127f;
+    scale = 1.0f;
+  }
+  uint2 w = make_uint2(0, 0);
+#define TQ_CVT(J)                                                                                    \
+  w.x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w.x, t[2 * J], t[2 * J + 1], scale, J);               \
+  w.y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w.y, t[8 + 2 * J], t[9 + 2 * J], scale, J);
+  TQ_CVT(0)
+  TQ_CVT(1)
+  TQ_CVT(2)
+  TQ_CVT(3)
+#undef TQ_CVT
   return w;
 }
 
-__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantizeArgs a) {
-  constexpr int TPW = QMap<kD>::TPW, Q = kD / 8;
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t group = wave / a.hkv;
-  const int h = (int)(wave - group * a.hkv);
-  const int li = QMap<kD>::li(lane);
-  const int tw = QMap<kD>::tw(lane);
-  const int tq = tw & 3;
-  const int64_t n = group * TPW + tw;
-  if (group * TPW >= a.num_tokens) return;
-  const bool in_range = n < a.num_tokens;
-  const int slot = in_range ? a.slots[n] : -1;
-
-  uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-  if (in_range) {
-    const int64_t base = (n * a.hkv + h) * kD + li * 8;
-    kr = *reinterpret_cast<const uint4 *>(a.k + base);
-    vr = *reinterpret_cast<const uint4 *>(a.v + base);
-  }
-  float x[8], v[8];
-  x[0] = bf16_lo(kr.x); x[1] = bf16_hi(kr.x); x[2] = bf16_lo(kr.y); x[3] = bf16_hi(kr.y);
-  x[4] = bf16_lo(kr.z); x[5] = bf16_hi(kr.z); x[6] = bf16_lo(kr.w); x[7] = bf16_hi(kr.w);
-  v[0] = bf16_lo(vr.x); v[1] = bf16_hi(vr.x); v[2] = bf16_lo(vr.y); v[3] = bf16_hi(vr.y);
-  v[4] = bf16_lo(vr.z); v[5] = bf16_hi(vr.z); v[6] = bf16_lo(vr.w); v[7] = bf16_hi(vr.w);
-
-  wht_rows<kD>(x, lane);
+// Quantize one token row (keys rotated, both MX-FP4) into its record.
+__device__ __forceinline__ void mx_quantize_row(const QuantizeArgs &a, const RowLoad<kD> &cur, int h, int lane,
+                                                int li, int tq, float ksign) {
+  constexpr int Q = kD / 8;
+  const int slot = cur.valid ? cur.slot : -1;
+  float z[16], v[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = x[e] * a.rsqrt_d;
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t kw = kword<kD>(cur, i), vw = vword<kD>(cur, i);
+    z[2 * i] = bf16_lo(kw);
+    z[2 * i + 1] = bf16_hi(kw);
+    v[2 * i] = bf16_lo(vw);
+    v[2 * i + 1] = bf16_hi(vw);
+  }
+  wht16<kD>(z, lane);
   int kx, vx;
-  const uint32_t kw = mx_encode8(x, kx);
-  const uint32_t vw = mx_encode8(v, vx);
+  const uint2 kc = mx_encode16<true>(z, ksign, kx);  // y = fp32(x * fp32(1/sqrt(D)))
+  const uint2 vc = mx_encode16<false>(v, 1.0f, vx);
 
-  // four consecutive rows of one block? (all exchanges run on every lane)
-  const int qid = (slot >= 0 && (slot & 3) == tq) ? (slot >> 2) : -1 - tq;
-  const int qo = (int)xor4u((uint32_t)qid);
-  const uint32_t pair_ok = (qid == qo && qid >= 0) ? 1u : 0u;
-  const uint32_t other_ok = xor32u(pair_ok);
-  const int qp = (int)xor32u((uint32_t)qid);
-  const bool aligned = pair_ok && other_ok && qp == qid;
-  // value-code bytes of the quad, transposed (as in the TQ4/4 kernel)
-  uint32_t t1 = xor4u(vw);
-  uint32_t vt = __builtin_amdgcn_perm(t1, vw, (tq & 1) ? 0x03070105u : 0x06020400u);
-  uint32_t t2 = xor32u(vt);
-  vt = __builtin_amdgcn_perm(t2, vt, (tq & 2) ? 0x03020706u : 0x05040100u);
+  const bool aligned = quad_aligned<kD>(slot, tq);
+  const uint32_t vt0 = quad_transpose<kD>(vc.x, tq), vt1 = quad_transpose<kD>(vc.y, tq);
   // the quad's four value exponents as one dword [t0, t1, t2, t3]
   const uint32_t xb = (uint32_t)(vx + 127) & 0xFFu;
-  const uint32_t xp1 = xor4u(xb);
+  const uint32_t xp1 = tok_xor1(xb);
   const uint32_t pr = (tq & 1) ? (xp1 | (xb << 8)) : (xb | (xp1 << 8));
-  const uint32_t xp2 = xor32u(pr);
+  const uint32_t xp2 = tok_xor2<kD>(pr);
   const uint32_t xq = (tq & 2) ? (xp2 | (pr << 16)) : (pr | (xp2 << 16));
-
   if (slot < 0) return;
   const int64_t blk = slot >> 4;
   const int t = slot & 15;
   uint8_t *rec = a.pool + ((int64_t)blk * a.hkv + h) * kRec;
-  const int p0 = 4 * li;
-  *reinterpret_cast<uint32_t *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = kw;
-  const int r = t >> 2, gp = li >> 2, j0 = 4 * (li & 3);
-  if ((li & 3) == 0) rec[kOffKs + gp * 16 + t] = (uint8_t)(kx + 127);
+  const int p0 = 8 * li;
+  *reinterpret_cast<uint2 *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = kc;
+  const int r = t >> 2, gp = li >> 1, j0 = 8 * (li & 1);
+  if ((li & 1) == 0) rec[kOffKs + gp * 16 + t] = (uint8_t)(kx + 127);
   if (aligned) {
-    *reinterpret_cast<uint32_t *>(rec + kOffVc + ((r * 16 + j0 + tq) * kG + gp) * 4) = vt;
-    if ((li & 3) == 0 && tq == 0) *reinterpret_cast<uint32_t *>(rec + kOffVs + (r * kG + gp) * 4) = xq;
+    *reinterpret_cast<uint32_t *>(rec + kOffVc + ((r * 16 + j0 + tq) * kG + gp) * 4) = vt0;
+    *reinterpret_cast<uint32_t *>(rec + kOffVc + ((r * 16 + j0 + 4 + tq) * kG + gp) * 4) = vt1;
+    if ((li & 1) == 0 && tq == 0) *reinterpret_cast<uint32_t *>(rec + kOffVs + (r * kG + gp) * 4) = xq;
   } else {
     const int tt = t & 3;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) rec[kOffVc + ((r * 16 + j0 + k) * kG + gp) * 4 + tt] = (uint8_t)(vw >> (8 * k));
-    if ((li & 3) == 0) rec[kOffVs + (r * kG + gp) * 4 + tt] = (uint8_t)xb;
+    for (int k = 0; k < 8; ++k)
+      rec[kOffVc + ((r * 16 + j0 + k) * kG + gp) * 4 + tt] = (uint8_t)((k < 4 ? vc.x : vc.y) >> (8 * (k & 3)));
+    if ((li & 1) == 0) rec[kOffVs + (r * kG + gp) * 4 + tt] = (uint8_t)xb;
   }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void mxfp4_quantize_kernel(QuantizeArgs a) {
+  using L = QLanes<kD>;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = L::li(lane), tw = L::tw(lane), tq = tw & 3;
+  // keys leave the butterflies with the sign (-1)^popcount(li); folding it into
+  // the 1/sqrt(D) factor is exact
+  const float ksign = a.rsqrt_d * wht16_sign(li);
+  quantize_loop<kD>(a, wv, tw, li, [] {},
+                    [&](const RowLoad<kD> &row, int h) { mx_quantize_row(a, row, h, lane, li, tq, ksign); });
 }
 
 // ---- decode -------------------------------------------------------------------
@@ -152,12 +157,12 @@ struct Blk4 {
   uint32_t vsw;   // one dword of the value exponent tile (lane (r, c): dword c & 3 of row r)
 };
 
-__device__ __forceinline__ void load_blk4(Blk4 &o, const uint8_t *rec, int lane, uint32_t vs_keep) {
+__device__ __forceinline__ void load_blk4(Blk4 &o, const uint8_t *rec, int lane) {
   const int r = lane >> 4, c = lane & 15;
   o.kq = *reinterpret_cast<const uint4 *>(rec + lane * 16);
   o.ksb = rec[kOffKs + lane];
   o.vq = *reinterpret_cast<const uint4 *>(rec + kOffVc + lane * 16);
-  o.vsw = reinterpret_cast<const uint32_t *>(rec + kOffVs)[4 * r + (c & 3)] & vs_keep;
+  o.vsw = reinterpret_cast<const uint32_t *>(rec + kOffVs)[4 * r + (c & 3)];
 }
 
 __device__ __forceinline__ uint32_t word4(const uint4 &v, int i) {
@@ -166,8 +171,11 @@ __device__ __forceinline__ uint32_t word4(const uint4 &v, int i) {
 
 template <int GQ>
 __device__ __forceinline__ void do_block4(const Blk4 &bk, const int8v &bq8, uint32_t *vs_slot, WaveState<8> &st,
-                                          float qscale, float lo_mask, int lane, int tok0, int T, bool tail) {
-  vs_slot[(lane >> 4) * 4 + (lane & 3)] = bk.vsw;
+                                          float qscale, float lo_mask, int lane, int tok0, int T, bool tail,
+                                          uint32_t vs_keep) {
+  // exponent bytes of rows past the context are cleared (those rows then
+  // dequantize to exactly 0), at the use so no early wait on the loads is forced
+  vs_slot[(lane >> 4) * 4 + (lane & 3)] = tail ? (bk.vsw & vs_keep) : bk.vsw;
   // ---- logits: one scaled MFMA per block ------------------------------------------
   const int8v ak = (int8v){(int)bk.kq.x, (int)bk.kq.y, (int)bk.kq.z, (int)bk.kq.w, 0, 0, 0, 0};
   float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
@@ -241,13 +249,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int b = (int)(wg % (uint32_t)a.batch);
-  const uint32_t rest = wg / (uint32_t)a.batch;
-  const int kvh = (int)(rest % (uint32_t)a.hkv);
-  const int sp = (int)(rest / (uint32_t)a.hkv);
+  const WgTask task = decode_task(a);
+  const int b = task.b, kvh = task.kvh, sp = task.sp;
   const int qh0 = kvh * GQ;
-  const int T = a.ctx[b];
+  const int T = a.ctx[b];  // a scalar load: nothing is written before it
+  // the query word next: it completes while the block ids are fetched
+  const uint32_t q_w = wv < GQ ? load_query_word<kD>(a.q + ((int64_t)b * a.hq + qh0 + wv) * kD, lane) : 0u;
+  __asm__ volatile("" ::: "memory");
   const int nblk = (T + 15) >> 4;
   const int blk0 = sp * a.split_blocks;
   if (nblk == 0) {
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   const uint8_t *base = a.pool + (int64_t)kvh * kRec;
   const int64_t stride = (int64_t)a.hkv * kRec;
   const int mine = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
-  const int my_id = btab[blk0 + wv + (lane < mine ? lane : 0) * NW];
+  const int my_id = settled(btab[blk0 + wv + (lane < mine ? lane : 0) * NW]);
   auto rec_of = [&](int k) {
     const int kk = k < mine ? k : mine - 1;
     return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
@@ -273,20 +281,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) tail_keep |= (rem > tt ? 0xFFu : 0u) << (8 * tt);
   }
-  auto keep_of = [&](int k) { return blk0 + wv + (k < mine ? k : mine - 1) * NW == tail_blk ? tail_keep : ~0u; };
   Blk4 b0, b1, b2, b3;
   if (mine > 0) {
-    load_blk4(b0, rec_of(0), lane, keep_of(0));
-    load_blk4(b1, rec_of(1), lane, keep_of(1));
-    load_blk4(b2, rec_of(2), lane, keep_of(2));
-    load_blk4(b3, rec_of(3), lane, keep_of(3));
+    // issued block by block, as the loop's refills are, so that the
+    // compiler's wait counts inside the loop stay partial on its first pass
+    load_blk4(b0, rec_of(0), lane);
+    __asm__ volatile("" ::: "memory");
+    load_blk4(b1, rec_of(1), lane);
+    __asm__ volatile("" ::: "memory");
+    load_blk4(b2, rec_of(2), lane);
+    __asm__ volatile("" ::: "memory");
+    load_blk4(b3, rec_of(3), lane);
   }
 
   // ---- the query group as e4m3 bytes: rows h and g + h both hold head h --------
   for (int i = tid; i < (16 - 2 * GQ) * kD; i += NW * 64) s_q8[2 * GQ + i / kD][i % kD] = 0;
   if (wv < GQ) {
     float x0, x1;
-    rotate_row<kD>(a.q + ((int64_t)b * a.hq + qh0 + wv) * kD, lane, x0, x1);
+    rotate_row<kD>(q_w, lane, x0, x1);
     const uint32_t c0 = e4m3_rne(x0 * a.rsqrt_d), c1 = e4m3_rne(x1 * a.rsqrt_d);
     s_q8[wv][2 * lane] = (uint8_t)c0;
     s_q8[wv][2 * lane + 1] = (uint8_t)c1;
@@ -312,9 +324,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   auto run = [&](Blk4 &buf, int k) {
     if (k < mine) {
       const int blk = blk0 + wv + k * NW;
-      do_block4<GQ>(buf, bq8, vs_slot, st, a.qscale, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk);
+      do_block4<GQ>(buf, bq8, vs_slot, st, a.qscale, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk, tail_keep);
     }
-    load_blk4(buf, rec_of(k + 4), lane, keep_of(k + 4));
+    load_blk4(buf, rec_of(k + 4), lane);
   };
 #pragma unroll 1
   for (int k = 0; k < mine; k += 4) {
@@ -331,8 +343,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s) {
   if (a.num_tokens <= 0) return hipSuccess;
-  const int64_t waves = ((a.num_tokens + 3) / 4) * a.hkv;
-  hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  const int64_t tasks = quantize_tasks(kD, a.num_tokens, a.hkv);
+  const int grid = quantize_grid((const void *)mxfp4_quantize_kernel, kQuantThreads, tasks);
+  hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3(grid), dim3(kQuantThreads), 0, s, a);
   return hipGetLastError();
 }
 

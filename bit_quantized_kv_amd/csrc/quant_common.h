@@ -1,5 +1,6 @@
-// Pieces shared by the quantize kernels: the lane mapping of a wave over
-// token rows and the in-register Walsh-Hadamard butterflies.
+// Pieces shared by the quantize kernels: the lane mapping of a wave over token
+// rows, the in-register Walsh-Hadamard butterflies, the quad byte transposes
+// and the persistent launch geometry.
 #pragma once
 
 #include "tq_device.h"
@@ -7,68 +8,252 @@
 
 namespace tq {
 
-// One wave handles TPW token rows of one kv-head, D/8 lanes per row, 8
-// channels per lane.  Lane bits {0,1,3,4} select the 8-channel chunk li
-// (channel = 8*li + e), the remaining lane bits select the token tw, so the
-// cross-lane butterfly stages (channel bits 3..6) run over lane xor 1, 2 (DPP
-// quad_perm), xor 8 (DPP row_ror:8) and xor 16 (gfx950 permlane16 swap).
+// A wave handles TPW token rows of one kv-head; a row is spread over LPT lanes
+// with 16 channels per lane (channel = 16*li + e).  The lane bits that carry
+// the chunk index li are those whose exchanges are single DPP operations:
+// lane bits 0, 1 (quad_perm) and 3 (row_ror:8).  The token index tw takes the
+// remaining lane bits; its bit 0 is lane bit 2 and its bit 1 is lane bit TB1.
 template <int D>
-struct QMap;
+struct QLanes;
 template <>
-struct QMap<128> {
-  static constexpr int TPW = 4;  // token rows per wave
-  __device__ static int li(int l) { return (l & 3) | ((l >> 1) & 0xC); }
-  __device__ static int tw(int l) { return ((l >> 2) & 1) | ((l >> 4) & 2); }
+struct QLanes<128> {
+  static constexpr int LPT = 8, TPW = 8, TB1 = 4;
+  __device__ static int li(int l) { return (l & 3) | ((l >> 1) & 4); }
+  __device__ static int tw(int l) { return ((l >> 2) & 1) | ((l >> 3) & 6); }
 };
 template <>
-struct QMap<64> {
-  static constexpr int TPW = 8;
-  __device__ static int li(int l) { return (l & 3) | ((l >> 1) & 0x4); }
-  __device__ static int tw(int l) { return ((l >> 2) & 1) | ((l >> 3) & 2) | ((l >> 3) & 4); }
+struct QLanes<64> {
+  static constexpr int LPT = 4, TPW = 16, TB1 = 3;
+  __device__ static int li(int l) { return l & 3; }
+  __device__ static int tw(int l) { return l >> 2; }
 };
 
-// exchange with the lane holding the token whose in-quad index differs in bit 1
-// (lane bit 5 for D = 128, lane bit 4 for D = 64); bit 0 is lane bit 2 for both
+// Exchange with the lane of the token whose in-quad index differs in bit 0 /
+// bit 1 (ds_swizzle: these run in the LDS pipe, not on the VALU).
+__device__ __forceinline__ uint32_t tok_xor1(uint32_t x) { return swz_xor_u<4>(x); }
 template <int D>
-__device__ __forceinline__ uint32_t quad_xor2(uint32_t x) {
-  if constexpr (D == 128) return xor32u(x);
-  else return xor16u(x);
+__device__ __forceinline__ uint32_t tok_xor2(uint32_t x) {
+  return swz_xor_u<(1 << QLanes<D>::TB1)>(x);
 }
 
-// Unnormalized Walsh-Hadamard butterflies over the D channels of one token
-// row, in the fixed stage order h = 1, 2, ..., D/2, fp32.
+// fp32 x + partner(x) on all lanes, partner = lane ^ 1, ^ 2, ^ 8 (DPP, one op)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(x), CTRL, 0xF, 0xF, true));
+}
+
+// Unnormalized Walsh-Hadamard butterflies over one token row, fp32, in the
+// stage order h = 1, 2, ..., D/2 ((a, b) -> (a + b, a - b)).  Stages h = 1..8
+// are in-lane.  The cross-lane stages (h = 16, 32, 64: chunk bits 0, 1, 2 =
+// lane bits 0, 1, 3) are one v_fmac_f32_dpp each: z += s * z[partner] with
+// s = -1 on the lane whose chunk bit is set.  That lane then holds -(a - b)
+// instead of a - b; the values leave this function as sigma * y with
+// sigma = (-1)^popcount(li), which the caller folds into its scale (the
+// rounding of each stage is symmetric in sign, so sigma * y is exactly the
+// negation of the correctly rounded stage result).
 template <int D>
-__device__ __forceinline__ void wht_rows(float (&x)[8], int lane) {
+__device__ __forceinline__ void wht16(float (&z)[16], int lane) {
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+  for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       if (!(i & h)) {
-        float a = x[i], b = x[i + h];
-        x[i] = a + b;
-        x[i + h] = a - b;
+        const float a = z[i], b = z[i + h];
+        z[i] = a + b;
+        z[i + h] = a - b;
       }
     }
   }
-  // lane holding a (bit clear) gets a + b, lane holding b gets a - b
-  const float s1 = (lane & 1) ? -1.f : 1.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(s1, x[i], xor1(x[i]));
-  const float s2 = (lane & 2) ? -1.f : 1.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(s2, x[i], xor2(x[i]));
-  const float s8 = (lane & 8) ? -1.f : 1.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(s8, x[i], xor8(x[i]));
+  const float s0 = (lane & 1) ? -1.f : 1.f;
+  const float s1 = (lane & 2) ? -1.f : 1.f;
+  // s_nop 1: a DPP source must not be written by the two preceding VALU ops
+#define TQ_F16(ctl, s)                                                                              \
+  "v_fmac_f32_dpp %0, %0, " s " " ctl "\n\tv_fmac_f32_dpp %1, %1, " s " " ctl "\n\t"                \
+  "v_fmac_f32_dpp %2, %2, " s " " ctl "\n\tv_fmac_f32_dpp %3, %3, " s " " ctl "\n\t"                \
+  "v_fmac_f32_dpp %4, %4, " s " " ctl "\n\tv_fmac_f32_dpp %5, %5, " s " " ctl "\n\t"                \
+  "v_fmac_f32_dpp %6, %6, " s " " ctl "\n\tv_fmac_f32_dpp %7, %7, " s " " ctl "\n\t"                \
+  "v_fmac_f32_dpp %8, %8, " s " " ctl "\n\tv_fmac_f32_dpp %9, %9, " s " " ctl "\n\t"                \
+  "v_fmac_f32_dpp %10, %10, " s " " ctl "\n\tv_fmac_f32_dpp %11, %11, " s " " ctl "\n\t"            \
+  "v_fmac_f32_dpp %12, %12, " s " " ctl "\n\tv_fmac_f32_dpp %13, %13, " s " " ctl "\n\t"            \
+  "v_fmac_f32_dpp %14, %14, " s " " ctl "\n\tv_fmac_f32_dpp %15, %15, " s " " ctl "\n\t"
+#define TQ_ZOPS                                                                                     \
+  "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]), "+v"(z[6]), "+v"(z[7]),  \
+      "+v"(z[8]), "+v"(z[9]), "+v"(z[10]), "+v"(z[11]), "+v"(z[12]), "+v"(z[13]), "+v"(z[14]),     \
+      "+v"(z[15])
   if constexpr (D == 128) {
-    const float s16 = (lane & 16) ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // even rows get (own, partner), odd rows (partner, own): a +- b = p0 +- p1
-      auto p = __builtin_amdgcn_permlane16_swap(as_u(x[i]), as_u(x[i]), false, false);
-      x[i] = __builtin_fmaf(s16, as_f(p[1]), as_f(p[0]));
+    const float s3 = (lane & 8) ? -1.f : 1.f;
+    asm volatile("s_nop 1\n\t" TQ_F16("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf", "%16")
+                     TQ_F16("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf", "%17")
+                         TQ_F16("row_ror:8 row_mask:0xf bank_mask:0xf", "%18")
+                 : TQ_ZOPS
+                 : "v"(s0), "v"(s1), "v"(s3));
+  } else {
+    asm volatile("s_nop 1\n\t" TQ_F16("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf", "%16")
+                     TQ_F16("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf", "%17")
+                 : TQ_ZOPS
+                 : "v"(s0), "v"(s1));
+  }
+#undef TQ_F16
+#undef TQ_ZOPS
+}
+
+// sigma of wht16: (-1)^popcount(li)
+__device__ __forceinline__ float wht16_sign(int li) { return (__builtin_popcount(li) & 1) ? -1.f : 1.f; }
+
+// 4 x 4 byte transpose among the quad of tokens (tq = in-quad token index):
+// lane tq receives byte tq of each of the four tokens' words, token order.
+template <int D>
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t w, int tq) {
+  const uint32_t t1 = tok_xor1(w);
+  uint32_t t = __builtin_amdgcn_perm(t1, w, (tq & 1) ? 0x03070105u : 0x06020400u);
+  const uint32_t t2 = tok_xor2<D>(t);
+  return __builtin_amdgcn_perm(t2, t, (tq & 2) ? 0x03020706u : 0x05040100u);
+}
+
+// Is this lane's token one of four consecutive rows r*4 .. r*4+3 of one block,
+// with the quad's tokens in order?  Every exchange runs on all lanes (a
+// cross-lane read under a divergent mask would see inactive lanes).
+template <int D>
+__device__ __forceinline__ bool quad_aligned(int slot, int tq) {
+  const int qid = (slot >= 0 && (slot & 3) == tq) ? (slot >> 2) : -1 - tq;
+  const int qo = (int)tok_xor1((uint32_t)qid);
+  const uint32_t pair_ok = (qid == qo && qid >= 0) ? 1u : 0u;
+  const uint32_t other_ok = tok_xor2<D>(pair_ok);
+  const int qp = (int)tok_xor2<D>((uint32_t)qid);
+  return pair_ok && other_ok && qp == qid;
+}
+
+// Correctly rounded fp32 1/h for an fp16 h >= 0 given by its bits, from the
+// table of significand reciprocals (recip[f] = fp32(1 / (1 + f/1024))); 1/h of
+// a normal h is that entry times 2^(15 - E), an exact scaling.  Zero gives 0;
+// subnormal h takes the division.
+__device__ __forceinline__ float recip_f16(uint32_t hb, const float *s_recip) {
+  if (hb == 0) return 0.f;
+  if (hb < 0x400u) return __fdiv_rn(1.0f, (float)h_from((uint16_t)hb));
+  return __builtin_amdgcn_ldexpf(s_recip[hb & 0x3FFu], 15 - (int)(hb >> 10));
+}
+
+// fp32 r -> fp16 RNE is decided safely from an approximation of r within a
+// few ulps unless r lies near an fp16 rounding boundary (the low 13 bits of a
+// normal fp16-range fp32 value near 0x1000) or outside the normal fp16 range.
+__device__ __forceinline__ bool f16_round_safe(float r, uint32_t ulps) {
+  const uint32_t b = as_u(r);
+  const uint32_t m13 = b & 0x1FFFu;
+  return r >= 0x1p-14f && r < 65504.0f && (m13 + ulps - 0x1000u) > 2u * ulps;
+}
+
+// v_min3 / v_max3 of finite values (written out so that bit-cast inputs need
+// no canonicalizing instruction first)
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <int D>
+struct RowLoad {
+  uint4 k0, k1, v0, v1;  // 16 bf16 channels of K and of V
+  int slot;
+  bool valid;            // the lane's token exists
+};
+
+// Loads of the rows of one wave: tokens n0 + tw (n0 wave-uniform).  Tokens past
+// the end are clamped to the last token, so every load is valid and
+// unconditional; `valid` says whether the lane's token exists.  Addresses are a
+// wave-uniform base plus a 32-bit lane offset.
+template <int D>
+__device__ __forceinline__ void load_row(RowLoad<D> &o, const QuantizeArgs &a, int64_t n0, int h, int tw, int li) {
+  const int64_t last = a.num_tokens - 1;
+  const int64_t b0 = n0 < last ? n0 : last;
+  const int64_t span = last - b0;
+  const int lim = span < 64 ? (int)span : 64;
+  const int t = tw < lim ? tw : lim;
+  const int64_t ubase = (b0 * a.hkv + h) * D;
+  const uint32_t loff = ((uint32_t)t * (uint32_t)a.hkv * D + (uint32_t)li * 16u) * 2u;
+  const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.k + ubase);
+  const uint8_t *vb = reinterpret_cast<const uint8_t *>(a.v + ubase);
+  o.k0 = *reinterpret_cast<const uint4 *>(kb + loff);
+  o.k1 = *reinterpret_cast<const uint4 *>(kb + loff + 16);
+  o.v0 = *reinterpret_cast<const uint4 *>(vb + loff);
+  o.v1 = *reinterpret_cast<const uint4 *>(vb + loff + 16);
+  o.slot = (a.slots + b0)[t];
+  o.valid = n0 <= last && tw <= span;
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t kword(const RowLoad<D> &r, int i) {
+  const uint4 &q = i < 4 ? r.k0 : r.k1;
+  const int j = i & 3;
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+}
+template <int D>
+__device__ __forceinline__ uint32_t vword(const RowLoad<D> &r, int i) {
+  const uint4 &q = i < 4 ? r.v0 : r.v1;
+  const int j = i & 3;
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+}
+
+// The persistent loop of the quantize kernels.  A work-group task is (chunk of
+// 4 * TPW tokens, kv-head): wave wv codes tokens chunk * 4 * TPW + wv * TPW +
+// tw, so one work-group writes whole 16-token records.  The grid strides
+// through the tasks, tracked as (chunk, head) pairs so the loop needs no 64-bit
+// division.  Two row buffers: every step loads the next task into one (clamped
+// to a valid task, so the loads are unconditional) while coding the other.
+// `stage` runs once, after the first loads are issued (table staging);
+// `code(row, h)` codes one row.
+constexpr int kQuantThreads = 256;  // four waves per work-group
+
+template <int D, class Stage, class Code>
+__device__ __forceinline__ void quantize_loop(const QuantizeArgs &a, int wv, int tw, int li, Stage stage, Code code) {
+  constexpr int TPW = QLanes<D>::TPW, WG_TOK = 4 * TPW;
+  const int64_t chunks = (a.num_tokens + WG_TOK - 1) / WG_TOK;
+  const int hkv = a.hkv;
+  const int64_t gq = gridDim.x / hkv;
+  const int gr = (int)(gridDim.x % hkv);
+  auto advance = [&](int64_t &c, int &h) {
+    c += gq;
+    h += gr;
+    if (h >= hkv) {
+      h -= hkv;
+      ++c;
     }
+  };
+  int64_t c = blockIdx.x / hkv;
+  int h = (int)(blockIdx.x % hkv);
+  RowLoad<D> ra, rb;
+  load_row<D>(ra, a, c * WG_TOK + wv * TPW, h, tw, li);
+  stage();
+  while (c < chunks) {
+    int64_t c2 = c;
+    int h2 = h;
+    advance(c2, h2);
+    load_row<D>(rb, a, (c2 < chunks ? c2 : c) * WG_TOK + wv * TPW, c2 < chunks ? h2 : h, tw, li);
+    code(ra, h);
+    if (c2 >= chunks) break;
+    c = c2;
+    h = h2;
+    advance(c2, h2);
+    load_row<D>(ra, a, (c2 < chunks ? c2 : c) * WG_TOK + wv * TPW, c2 < chunks ? h2 : h, tw, li);
+    code(rb, h);
+    c = c2;
+    h = h2;
   }
 }
+
+// Work-group tasks of a quantize launch.
+inline int64_t quantize_tasks(int d, int64_t num_tokens, int hkv) {
+  const int wg_tok = d == 128 ? 4 * 8 : 4 * 16;
+  return ((num_tokens + wg_tok - 1) / wg_tok) * hkv;
+}
+
+// Launch geometry of the persistent quantize kernels: enough work-groups to
+// fill every compute unit at the kernel's occupancy, each taking work-group
+// tasks with a stride of the grid size.
+int quantize_grid(const void *kernel, int threads, int64_t tasks);
 
 }  // namespace tq

@@ -59,28 +59,30 @@ struct Blk {
                             // (r, c) holds dword c of row r's 16*G bytes
 };
 
-// vm_keep: per-lane mask clearing the (scale, min) halves of rows past the
-// context, so those rows dequantize to exactly 0 whatever the pool holds.
 template <int D>
-__device__ __forceinline__ void load_blk(Blk<D> &o, const uint8_t *rec, int lane, uint32_t vm_keep) {
+__device__ __forceinline__ void load_blk(Blk<D> &o, const uint8_t *rec, int lane) {
   constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
   constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
   const int r = lane >> 4, c = lane & 15;
   o.kq = *reinterpret_cast<const typename KTile<D>::T *>(rec + lane * Q);
   o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
   o.vq = *reinterpret_cast<const typename KTile<D>::T *>(rec + OFF_VC + lane * (4 * G));
-  o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))] & vm_keep;
+  o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
 }
 
 // vm_slot: this wave's 16*D/8-byte LDS slot for the value (scale, min) tile.
+// vm_keep: per-lane mask clearing the (scale, min) halves of rows past the
+// context, so those rows dequantize to exactly 0 whatever the pool holds
+// (applied here, at the use, so that no wait on the block's loads is forced
+// earlier).
 template <int D, int GQ>
 __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D / 32], const uint32_t *s_lut,
                                          uint32_t *vm_slot, WaveState<2 * D / 32> &st, float lo_mask, int lane,
-                                         int tok0, int T, bool tail) {
+                                         int tok0, int T, bool tail, uint32_t vm_keep) {
   constexpr int G = D / 32, KS = D / 32;
   // the value (scale, min) tile goes through LDS: lane (r, c) wrote dword c of
   // row r; every lane reads its row's 16*G bytes back (broadcast reads)
-  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = bk.vmw;
+  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = tail ? (bk.vmw & vm_keep) : bk.vmw;
   // ---- logits ---------------------------------------------------------------
   float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -174,14 +176,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: block ids load as scalars
-  const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int b = (int)(wg % (uint32_t)a.batch);
-  const uint32_t rest = wg / (uint32_t)a.batch;
-  const int kvh = (int)(rest % (uint32_t)a.hkv);
-  const int sp = (int)(rest / (uint32_t)a.hkv);
+  const WgTask task = decode_task(a);
+  const int b = task.b, kvh = task.kvh, sp = task.sp;
   const int qh0 = kvh * GQ;
 
-  const int T = a.ctx[b];
+  const int T = a.ctx[b];  // a scalar load: nothing is written before it
+  // set-up loads next (table word, query word): they complete while the block
+  // ids are fetched, so the set-up below waits on nothing
+  const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
+  const uint32_t q_w = wv < GQ ? load_query_word<D>(a.q + ((int64_t)b * a.hq + qh0 + wv) * D, lane) : 0u;
+  __asm__ volatile("" ::: "memory");
   const int nblk = (T + 15) >> 4;
   const int blk0 = sp * a.split_blocks;
   if (nblk == 0) {
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   // wave's last block again, an L2 hit), so the number of loads in flight is
   // the same on every path and the waits stay partial.
   const int mine = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
-  const int my_id = btab[blk0 + wv + (lane < mine ? lane : 0) * NW];
+  const int my_id = settled(btab[blk0 + wv + (lane < mine ? lane : 0) * NW]);
   auto rec_of = [&](int k) {
     const int kk = k < mine ? k : mine - 1;
     return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
@@ -214,21 +218,25 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     const int ta = (T & 15) - (r0 + (w & 1)), tb = ta - 2;
     tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
   }
-  auto keep_of = [&](int k) { return blk0 + wv + (k < mine ? k : mine - 1) * NW == tail_blk ? tail_keep : ~0u; };
   Blk<D> b0, b1, b2, b3;
   if (mine > 0) {
-    load_blk<D>(b0, rec_of(0), lane, keep_of(0));
-    load_blk<D>(b1, rec_of(1), lane, keep_of(1));
-    load_blk<D>(b2, rec_of(2), lane, keep_of(2));
-    load_blk<D>(b3, rec_of(3), lane, keep_of(3));
+    // issued block by block, as the loop's refills are, so that the
+    // compiler's wait counts inside the loop stay partial on its first pass
+    load_blk<D>(b0, rec_of(0), lane);
+    __asm__ volatile("" ::: "memory");
+    load_blk<D>(b1, rec_of(1), lane);
+    __asm__ volatile("" ::: "memory");
+    load_blk<D>(b2, rec_of(2), lane);
+    __asm__ volatile("" ::: "memory");
+    load_blk<D>(b3, rec_of(3), lane);
   }
 
   // ---- LUT and the rotated, scaled query group (wave w < g rotates head w) ------
-  if (tid < 256) s_lut[tid] = a.tables->lut2[tid];
+  if (tid < 256) s_lut[tid] = lut_w;
   for (int i = tid; i < (16 - 2 * GQ) * D; i += NW * 64) s_bq[2 * GQ + i / D][i % D] = (_Float16)0.f;
   if (wv < GQ) {
     float x0, x1;
-    rotate_row<D>(a.q + ((int64_t)b * a.hq + qh0 + wv) * D, lane, x0, x1);
+    rotate_row<D>(q_w, lane, x0, x1);
 #pragma unroll
     for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
       const float xs = (e ? x1 : x0) * a.qscale;
@@ -258,9 +266,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   auto run = [&](Blk<D> &buf, int k) {
     if (k < mine) {
       const int blk = blk0 + wv + k * NW;
-      do_block<D, GQ>(buf, bq, s_lut, vm_slot, st, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk);
+      do_block<D, GQ>(buf, bq, s_lut, vm_slot, st, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk, tail_keep);
     }
-    load_blk<D>(buf, rec_of(k + 4), lane, keep_of(k + 4));
+    load_blk<D>(buf, rec_of(k + 4), lane);
   };
 #pragma unroll 1
   for (int k = 0; k < mine; k += 4) {

@@ -6,166 +6,223 @@
 // LUT, V = uniform; section 4: Walsh-Hadamard rotation).  The exact decision
 // rules (fp32 operation order) and the record layout are stated in tq.h.
 //
-// One wave handles TPW token rows of one kv-head, D/8 lanes per row, 8
-// channels per lane (one 128-bit load of K and of V).  Lane bits {0,1,3,4}
-// select the 8-channel chunk, so the cross-lane butterfly stages (channel bits
-// 3..6) run over lane xor 1, 2 (DPP quad_perm), xor 8 (DPP row_ror:8) and xor 16
-// (gfx950 permlane16 swap); the remaining lane bits select the token.
+// The kernel is VALU-bound unless every step is lean, so:
+//   * a lane holds 16 channels of one token row (two 128-bit loads of K and of
+//     V); the three cross-lane butterfly stages are one DPP fmac each;
+//   * the key scale comes from an fp32 sum of squares (bf16 dot2) and is
+//     rounded to fp16 directly unless the RMS lies within a few ulps of an fp16
+//     rounding boundary, where the exact fp64 rule decides (rare);
+//   * 1/s and 1/sc are correctly rounded from a table of significand
+//     reciprocals; sc = fp16(fp32(range/15)) likewise falls back to the exact
+//     division only near a rounding boundary;
+//   * key codes: one bin lookup (v_cvt_pk_u8 gives the clamped bin) plus one
+//     comparison; value codes: v_cvt_pk_u8 rounds to nearest even and packs;
+//   * persistent work-groups: each takes (32- or 64-token chunk, kv-head)
+//     tasks, so one work-group writes whole 16-token records, and every wave
+//     loads its next task before coding the current one.
 #include "quant_common.h"
 
 namespace tq {
 namespace {
 
+// Exact key scale of a token row (the rare path): fp64 sum of the bf16 squares
+// over the row's LPT lanes (this lane's 16 channels in k0, k1), exact fp16 RMS.
 template <int D>
-__global__ __launch_bounds__(256) void tq4_quantize_kernel(QuantizeArgs a) {
-  constexpr int TPW = QMap<D>::TPW;
-  constexpr int G = D / 32;
-  constexpr int Q = D / 8;
-  constexpr int P16 = 16 * (D / 2);
-  constexpr int OFF_KS = P16;
-  constexpr int OFF_VC = OFF_KS + 32;
-  constexpr int OFF_VM = OFF_VC + P16;
-  constexpr int REC = OFF_VM + 64 * G;
-
-  __shared__ float2 s_bins[kMaxBins];
-  for (int i = threadIdx.x; i < a.bins.nbins; i += blockDim.x) s_bins[i] = a.tables->bins[i];
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t group = wave / a.hkv;
-  const int h = (int)(wave - group * a.hkv);
-  const int li = QMap<D>::li(lane);
-  const int tw = QMap<D>::tw(lane);
-  const int tq = tw & 3;  // token index within its quad
-  const int64_t n = group * TPW + tw;
-  if (group * TPW >= a.num_tokens) return;  // whole wave past the end
-
-  const bool in_range = n < a.num_tokens;
-  const int slot = in_range ? a.slots[n] : -1;
-
-  uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-  if (in_range) {
-    const int64_t base = (n * a.hkv + h) * D + li * 8;
-    kr = *reinterpret_cast<const uint4 *>(a.k + base);
-    vr = *reinterpret_cast<const uint4 *>(a.v + base);
-  }
-  float x[8], v[8];
-  x[0] = bf16_lo(kr.x); x[1] = bf16_hi(kr.x); x[2] = bf16_lo(kr.y); x[3] = bf16_hi(kr.y);
-  x[4] = bf16_lo(kr.z); x[5] = bf16_hi(kr.z); x[6] = bf16_lo(kr.w); x[7] = bf16_hi(kr.w);
-  v[0] = bf16_lo(vr.x); v[1] = bf16_hi(vr.x); v[2] = bf16_lo(vr.y); v[3] = bf16_hi(vr.y);
-  v[4] = bf16_lo(vr.z); v[5] = bf16_hi(vr.z); v[6] = bf16_lo(vr.w); v[7] = bf16_hi(vr.w);
-
-  // ---- key scale: exact sum of bf16 squares in fp64, exact fp16 RMS ----------
+__device__ __forceinline__ uint32_t key_scale_exact(const uint4 &k0, const uint4 &k1) {
   double ss = 0.0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[e], (double)x[e], ss);
+  for (int i = 0; i < 8; ++i) {
+    const uint4 &q = i < 4 ? k0 : k1;
+    const uint32_t w = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+    const double lo = (double)bf16_lo(w), hi = (double)bf16_hi(w);
+    ss = __builtin_fma(lo, lo, ss);
+    ss = __builtin_fma(hi, hi, ss);
+  }
   ss += dpp64_xor1(ss);
   ss += dpp64_xor2(ss);
-  ss += dpp64_xor8(ss);
-  if constexpr (D == 128) ss += dpp64_xor16(ss);
-  const _Float16 s16 = f16_rne_sqrt(ss * (1.0 / D));
-  const float sf = (float)s16;
+  if constexpr (D == 128) ss += dpp64_xor8(ss);
+  return h_bits(f16_rne_sqrt(ss * (1.0 / D)));
+}
 
-  // ---- key codes ---------------------------------------------------------------
-  wht_rows<D>(x, lane);
-  const float inv_s = sf > 0.f ? __fdiv_rn(1.0f, sf) : 0.0f;
-  const float w = inv_s * a.rsqrt_d;
-  const float nbm1 = (float)(a.bins.nbins - 1);
-  uint32_t kw = 0;
+// Quantize one token row held by the LPT lanes of this lane's token and write
+// its codes and scales into the record of (slot / 16, h).
+template <int D>
+__device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoad<D> &cur, int h, int lane,
+                                             int li, int tq, const float2 *s_bins,
+                                             const float *s_recip, float bin_a, float bin_b, float sigma) {
+  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
+  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
+  constexpr int REC = OFF_VM + 64 * G;
+  const int slot = cur.valid ? cur.slot : -1;
+  // ---- key scale: fp32 sum of squares, exact fp16 RMS -------------------------
+  float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float u = x[e] * w;
-    float fb = __builtin_fmaf(u, a.bins.a, a.bins.b);
-    fb = __builtin_amdgcn_fmed3f(fb, 0.f, nbm1);
-    const float2 bt = s_bins[(int)fb];
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = kword<D>(cur, i);
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w), __builtin_bit_cast(bf2, w), ss, false);
+  }
+  ss = dpp_add<0xB1>(ss);
+  ss = dpp_add<0x4E>(ss);
+  if constexpr (D == 128) ss = dpp_add<0x128>(ss);
+  // ss carries <= 12 roundings of <= 1 ulp; sqrt adds 1 ulp: 32 ulps is safe
+  const float rms = __builtin_amdgcn_sqrtf(ss * (1.0f / D));
+  uint32_t sb = h_bits((_Float16)rms);
+  if (!(rms == 0.f || f16_round_safe(rms, 32))) sb = key_scale_exact<D>(cur.k0, cur.k1);
+
+  // ---- rotation -------------------------------------------------------------------
+  float z[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = kword<D>(cur, i);
+    z[2 * i] = bf16_lo(w);
+    z[2 * i + 1] = bf16_hi(w);
+  }
+  wht16<D>(z, lane);
+
+  // ---- key codes: u = fp32(y * w), w = fp32(fp32(1/s) / sqrt(D)) ------------------
+  const float w = recip_f16(sb, s_recip) * a.rsqrt_d * sigma;  // sigma: sign of z
+  const float wa = w * bin_a;
+  uint32_t kc0 = 0, kc1 = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float u = z[e] * w;
+    const uint32_t bin = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(z[e], wa, bin_b), 0, 0);
+    const float2 bt = s_bins[bin];
     const uint32_t code = (uint32_t)__float_as_int(bt.y) + (u > bt.x ? 1u : 0u);
-    kw |= code << (4 * e);
+    if (e < 8) kc0 |= code << (4 * e);
+    else kc1 |= code << (4 * (e - 8));
   }
 
-  // ---- value codes: 32-channel groups = 4 consecutive chunks (lane xor 1, 2) ----
-  float mn = v[0], mx = v[0];
+  // ---- value codes: the 32-channel group is this lane and lane ^ 1 -------------------
+  float v[16];
 #pragma unroll
-  for (int e = 1; e < 8; ++e) {
-    mn = __builtin_fminf(mn, v[e]);
-    mx = __builtin_fmaxf(mx, v[e]);
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w2 = vword<D>(cur, i);
+    v[2 * i] = bf16_lo(w2);
+    v[2 * i + 1] = bf16_hi(w2);
   }
+  float mn = min3f(v[0], v[1], v[2]), mx = max3f(v[0], v[1], v[2]);
+#pragma unroll
+  for (int e = 3; e < 15; e += 2) {
+    mn = min3f(mn, v[e], v[e + 1]);
+    mx = max3f(mx, v[e], v[e + 1]);
+  }
+  mn = __builtin_fminf(mn, v[15]);
+  mx = __builtin_fmaxf(mx, v[15]);
   mn = __builtin_fminf(mn, xor1(mn));
   mx = __builtin_fmaxf(mx, xor1(mx));
-  mn = __builtin_fminf(mn, xor2(mn));
-  mx = __builtin_fmaxf(mx, xor2(mx));
   const float range = mx - mn;
-  const _Float16 sc16 = f16_sat(__fdiv_rn(range, 15.0f));
-  const _Float16 mn16 = f16_sat(mn);
-  const float scv = (float)sc16, mnv = (float)mn16;
-  const float inv_sc = scv > 0.f ? __fdiv_rn(1.0f, scv) : 0.0f;
-  uint32_t vw = 0;
+  const float qs = range * (1.0f / 15.0f);  // within 2 ulps of fp32(range / 15)
+  uint32_t scb = h_bits((_Float16)qs);
+  if (!(qs == 0.f || f16_round_safe(qs, 4))) scb = h_bits(f16_sat(__fdiv_rn(range, 15.0f)));
+  const _Float16 mn16 = (_Float16)__builtin_amdgcn_fmed3f(mn, -65504.0f, 65504.0f);  // saturating RNE
+  const float mnv = (float)mn16;
+  const float inv_sc = recip_f16(scb, s_recip);
+  uint32_t ve0 = 0, ve1 = 0, vo0 = 0, vo1 = 0;  // bytes: even / odd channels
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float d = v[e] - mnv;
-    const float q = __builtin_rintf(d * inv_sc);
-    vw |= (uint32_t)__builtin_amdgcn_fmed3f(q, 0.f, 15.f) << (4 * e);
-  }
-
-  // ---- does this quad of tokens fill four consecutive rows of one block? ------
-  // (every exchange runs on all lanes: a cross-lane read under a divergent
-  // exec mask would see inactive lanes)
-  const int qid = (slot >= 0 && (slot & 3) == tq) ? (slot >> 2) : -1 - tq;
-  const int qo = (int)xor4u((uint32_t)qid);
-  const uint32_t pair_ok = (qid == qo && qid >= 0) ? 1u : 0u;
-  const uint32_t other_ok = quad_xor2<D>(pair_ok);
-  const int qp = (int)quad_xor2<D>((uint32_t)qid);
-  const bool aligned = pair_ok && other_ok && qp == qid;
-
-  // byte transposes among the quad (all lanes take part)
-  uint32_t t1 = xor4u(vw);
-  uint32_t vt = __builtin_amdgcn_perm(t1, vw, (tq & 1) ? 0x03070105u : 0x06020400u);
-  uint32_t t2 = quad_xor2<D>(vt);
-  vt = __builtin_amdgcn_perm(t2, vt, (tq & 2) ? 0x03020706u : 0x05040100u);
-  const uint32_t scmn = (uint32_t)h_bits(sc16) | ((uint32_t)h_bits(mn16) << 16);
-  const uint32_t scmn_p = quad_xor2<D>(scmn);
-
-  if (slot < 0) return;
-  const int64_t blk = slot >> 4;
-  const int t = slot & 15;
-  uint8_t *rec = a.pool + ((int64_t)blk * a.hkv + h) * REC;
-  const int p0 = 4 * li;  // first channel pair of this lane
-  *reinterpret_cast<uint32_t *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = kw;
-  if (li == 0) *reinterpret_cast<uint16_t *>(rec + OFF_KS + 2 * t) = h_bits(s16);
-  const int r = t >> 2, gp = li >> 2, j0 = 4 * (li & 3);
-  if (aligned) {
-    // lane tq writes the 4 tokens' byte of channel pair j0 + tq
-    *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + tq) * G + gp) * 4) = vt;
-    if ((li & 3) == 0 && tq < 2) {
-      uint8_t *vm = rec + OFF_VM + (r * G + gp) * 16;
-      *reinterpret_cast<uint32_t *>(vm + 4 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x05040100u);
-      *reinterpret_cast<uint32_t *>(vm + 8 + 4 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x07060302u);
+  for (int e = 0; e < 16; ++e) {
+    const float qv = __builtin_amdgcn_fmed3f((v[e] - mnv) * inv_sc, 0.f, 15.f);
+    const int bsel = (e & 7) >> 1;
+    if (e < 8) {
+      if (e & 1) vo0 = __builtin_amdgcn_cvt_pk_u8_f32(qv, bsel, vo0);
+      else ve0 = __builtin_amdgcn_cvt_pk_u8_f32(qv, bsel, ve0);
+    } else {
+      if (e & 1) vo1 = __builtin_amdgcn_cvt_pk_u8_f32(qv, bsel, vo1);
+      else ve1 = __builtin_amdgcn_cvt_pk_u8_f32(qv, bsel, ve1);
     }
-  } else {
-    const int tt = t & 3;
+  }
+  const uint32_t vc0 = ve0 | (vo0 << 4), vc1 = ve1 | (vo1 << 4);  // pairs 0..3, 4..7 of this lane
+
+  // ---- placement ----------------------------------------------------------------------
+  const bool aligned = quad_aligned<D>(slot, tq);
+  const uint32_t vt0 = quad_transpose<D>(vc0, tq), vt1 = quad_transpose<D>(vc1, tq);
+  const uint32_t scmn = scb | ((uint32_t)h_bits(mn16) << 16);
+  const uint32_t scmn_p = tok_xor2<D>(scmn);
+  if (slot >= 0) {
+    const int64_t blk = slot >> 4;
+    const int t = slot & 15;
+    uint8_t *rec = a.pool + ((int64_t)blk * a.hkv + h) * REC;
+    // key codes: pairs 8*li .. 8*li+7 are contiguous in the key section
+    const int p0 = 8 * li;
+    *reinterpret_cast<uint2 *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = make_uint2(kc0, kc1);
+    if (li == 0) *reinterpret_cast<uint16_t *>(rec + OFF_KS + 2 * t) = (uint16_t)sb;
+    const int r = t >> 2, gp = li >> 1, j0 = 8 * (li & 1);
+    if (aligned) {
+      // lane tq writes the quad's bytes of channel pairs j0 + tq and j0 + 4 + tq
+      *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + tq) * G + gp) * 4) = vt0;
+      *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + 4 + tq) * G + gp) * 4) = vt1;
+      if ((li & 1) == 0 && tq < 2) {
+        uint8_t *vm = rec + OFF_VM + (r * G + gp) * 16;
+        *reinterpret_cast<uint32_t *>(vm + 4 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vm + 8 + 4 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x07060302u);
+      }
+    } else {
+      const int tt = t & 3;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      rec[OFF_VC + ((r * 16 + j0 + k) * G + gp) * 4 + tt] = (uint8_t)(vw >> (8 * k));
-    if ((li & 3) == 0) {
-      const int pos = (tt == 1) ? 2 : (tt == 2) ? 1 : tt;
-      uint16_t *vm = reinterpret_cast<uint16_t *>(rec + OFF_VM) + (r * G + gp) * 8;
-      vm[pos] = h_bits(sc16);
-      vm[4 + pos] = h_bits(mn16);
+      for (int k = 0; k < 8; ++k)
+        rec[OFF_VC + ((r * 16 + j0 + k) * G + gp) * 4 + tt] = (uint8_t)((k < 4 ? vc0 : vc1) >> (8 * (k & 3)));
+      if ((li & 1) == 0) {
+        const int pos = (tt == 1) ? 2 : (tt == 2) ? 1 : tt;
+        uint16_t *vm = reinterpret_cast<uint16_t *>(rec + OFF_VM) + (r * G + gp) * 8;
+        vm[pos] = (uint16_t)scb;
+        vm[4 + pos] = h_bits(mn16);
+      }
     }
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void tq4_quantize_kernel(QuantizeArgs a) {
+  using L = QLanes<D>;
+  __shared__ float2 s_bins[kMaxBins];
+  __shared__ float s_recip[1024];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = L::li(lane), tw = L::tw(lane), tq = tw & 3;
+  const float bin_a = a.bins.a, bin_b = a.bins.b - 0.5f;  // v_cvt_pk_u8 rounds: floor via -0.5
+  const float sigma = wht16_sign(li);
+  quantize_loop<D>(a, wv, tw, li,
+                   [&] {
+                     for (int i = threadIdx.x; i < kMaxBins; i += kQuantThreads) s_bins[i] = a.tables->bins[i];
+                     for (int i = threadIdx.x; i < 1024; i += kQuantThreads) s_recip[i] = a.tables->recip[i];
+                     __syncthreads();
+                   },
+                   [&](const RowLoad<D> &row, int h) {
+                     quantize_row<D>(a, row, h, lane, li, tq, s_bins, s_recip, bin_a, bin_b, sigma);
+                   });
+}
+
 }  // namespace
+
+int quantize_grid(const void *kernel, int threads, int64_t tasks) {
+  static int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached_cus = cus;
+    cached_dev = dev;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 2;
+  const int64_t cap = (int64_t)cached_cus * per_cu;
+  return (int)(tasks < cap ? tasks : cap);
+}
 
 hipError_t launch_tq4_quantize(int d, const QuantizeArgs &a, hipStream_t s) {
   if (a.num_tokens <= 0) return hipSuccess;
-  const int tpw = (d == 128) ? 4 : 8;
-  const int64_t waves = ((a.num_tokens + tpw - 1) / tpw) * a.hkv;
-  const int64_t blocks = (waves + 3) / 4;
-  if (d == 128)
-    hipLaunchKernelGGL(tq4_quantize_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(tq4_quantize_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  const int64_t tasks = quantize_tasks(d, a.num_tokens, a.hkv);
+  if (d == 128) {
+    const int grid = quantize_grid((const void *)tq4_quantize_kernel<128>, kQuantThreads, tasks);
+    hipLaunchKernelGGL(tq4_quantize_kernel<128>, dim3(grid), dim3(kQuantThreads), 0, s, a);
+  } else {
+    const int grid = quantize_grid((const void *)tq4_quantize_kernel<64>, kQuantThreads, tasks);
+    hipLaunchKernelGGL(tq4_quantize_kernel<64>, dim3(grid), dim3(kQuantThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -35,7 +35,8 @@ tq_status hip_fail(hipError_t e, const char *what) {
 tq_status check_desc(const tq_cache_desc *d, size_t *record) {
   if (!d) return fail(TQ_ERR_INVALID_ARG, "descriptor is NULL");
   if (d->block_size != 16) return fail(TQ_ERR_INVALID_ARG, "block_size must be 16");
-  if (d->num_kv_heads < 1) return fail(TQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (d->num_kv_heads < 1 || d->num_kv_heads > 65536)
+    return fail(TQ_ERR_INVALID_ARG, "num_kv_heads must be in [1, 65536]");
   if (d->num_blocks < 1) return fail(TQ_ERR_INVALID_ARG, "num_blocks must be >= 1");
   if (d->format == TQ_FORMAT_TQ4) {
     if (d->head_dim != 64 && d->head_dim != 128)

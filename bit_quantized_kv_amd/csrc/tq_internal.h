@@ -7,13 +7,14 @@
 
 namespace tq {
 
-constexpr int kMaxBins = 1024;   // key-coder bin table capacity
+constexpr int kMaxBins = 256;    // key-coder bins (indexed by a saturating byte conversion)
 constexpr int kMaxGqa = 8;       // query heads per kv-head handled by one work-group
 
 // Device-side tables of one cache (one allocation, laid out in this order).
 struct DeviceTables {
   uint32_t lut2[256];            // byte -> (fp16 c[lo nibble], fp16 c[hi nibble])
   float2 bins[kMaxBins];         // key coder: (threshold inside the bin or +inf, code below as int bits)
+  float recip[1024];             // fp32(1 / (1 + f/1024)), correctly rounded: 1/x of fp16 significands
 };
 
 // Key-coder bin parameters: bin(u) = clamp(floor(u * a + b), 0, nbins - 1).
@@ -62,8 +63,8 @@ hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
 void lloyd_max_gaussian16(double out[16]);
 uint16_t f64_to_f16_rne(double x);
 double f16_to_f64(uint16_t h);
-// Builds lut2 and the key-coder bins from an fp16 table; false if the table's
-// midpoints are too close for kMaxBins bins.
+// Builds lut2, the key-coder bins and the reciprocal table from an fp16 table;
+// false if the table's midpoints are too close for kMaxBins bins.
 bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *bp);
 
 // Record sizes.

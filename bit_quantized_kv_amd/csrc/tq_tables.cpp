@@ -97,6 +97,19 @@ double f16_to_f64(uint16_t h) {
 //   at most one threshold; `below` counts the thresholds under the widened bin.
 // ---------------------------------------------------------------------------
 bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *bp) {
+  // recip[f] = fp32 RNE of 1024 / (1024 + f), by exact integer long division
+  for (int f = 0; f < 1024; ++f) {
+    const uint64_t den = 1024 + (uint64_t)f;
+    if (f == 0) {
+      t->recip[0] = 1.0f;
+      continue;
+    }
+    // 1024/den lies in (0.5, 1): its 24-bit significand is floor(2^24 * 1024 / den)
+    const uint64_t num = (uint64_t)1024 << 24;
+    uint64_t q = num / den, r = num % den;
+    if (2 * r > den || (2 * r == den && (q & 1))) ++q;  // round to nearest even
+    t->recip[f] = (float)std::ldexp((double)q, -24);
+  }
   for (int e = 0; e < 256; ++e) t->lut2[e] = (uint32_t)table_f16[e & 15] | ((uint32_t)table_f16[e >> 4] << 16);
 
   float th[15];
@@ -108,7 +121,7 @@ bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *
   }
   const double span = (double)th[14] - (double)th[0];
   const float inf = std::numeric_limits<float>::infinity();
-  for (int nb = 256; nb <= kMaxBins; nb *= 2) {
+  for (int nb = kMaxBins; nb <= kMaxBins; nb *= 2) {
     const double width = span > 0 ? span / (nb - 8) : 1.0;
     for (int shift = 0; shift < 8; ++shift) {
       const double origin = (double)th[0] - 4.0 * width - shift * width / 8.0;
@@ -148,18 +161,30 @@ bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *
   return false;
 }
 
-// Split-K plan: blocks per work-group (a multiple of its 8 waves) chosen so
-// that a small batch still spreads over about two work-groups per compute
-// unit, bounded above so long contexts keep several splits for load balance.
-// The partials it implies are below 3% of the KV bytes for every shape.
+// Split-K plan: blocks per work-group S (a multiple of its 8 waves, 16..256).
+// All work-groups of a launch are resident at once in rounds of about two per
+// compute unit (512 on the full chip); with every sequence at the host's
+// maximum length a launch takes ceil(units * nsplit / 512) rounds, each about
+// S + kWgOverhead block-times long (the overhead: block-id fetch, query
+// rotation, the final merge of the waves).  The plan minimizes that; the cap
+// of 256 blocks keeps ragged batches balanced, since short sequences leave
+// their later splits empty.
 SplitPlan plan_split(int batch, int hkv, int max_context_len) {
   const int64_t max_nblk = ((int64_t)max_context_len + 15) / 16;
   const int64_t units = (int64_t)batch * hkv;
-  const int64_t target_wgs = 256 * 2;
-  int64_t s = (units * max_nblk + target_wgs - 1) / target_wgs;
-  s = ((s + 7) / 8) * 8;
-  if (s < 16) s = 16;
-  if (s > 128) s = 128;
+  const int64_t slots = 512;
+  const int64_t kWgOverhead = 16;
+  int64_t best_s = 16, best_cost = -1;
+  for (int64_t s = 16; s <= 256; s += 8) {
+    const int64_t nsplit = std::max<int64_t>(1, (max_nblk + s - 1) / s);
+    const int64_t rounds = (units * nsplit + slots - 1) / slots;
+    const int64_t cost = rounds * (std::min<int64_t>(s, std::max<int64_t>(max_nblk, 1)) + kWgOverhead);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_s = s;
+    }
+  }
+  int64_t s = best_s;
   if (const char *env = std::getenv("TQ_SPLIT_BLOCKS")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 1 && v <= 65536) s = v;

@@ -46,7 +46,8 @@
  *                  mn(t,gp) at 2*((r*G + gp)*8 + 4 + pos)
  *
  * MX-FP4 (format 1, D = 128).  Per (token, kv-head), groups of 32 channels:
- *   keys are rotated first, y = fp32(x * fp32(1/sqrt(D))); values are not.
+ *   keys are rotated first, y = fp32(x * fp32(1/sqrt(D))), an exactly zero y
+ *   stored as +0; values are not rotated (their zeros keep their sign).
  *   X = clamp(floor(log2(amax)) - 2, -127, 127) (amax = 0 -> -127), stored as
  *   the byte X + 127; element code = e2m1_RNE(value / 2^X) saturating at +-6,
  *   sign bit = the value's sign bit.  Queries: rotated the same way, cast to
@@ -89,7 +90,7 @@ typedef enum tq_out_dtype { TQ_OUT_F32 = 0, TQ_OUT_BF16 = 1 } tq_out_dtype;
 typedef struct tq_cache_desc {
   int32_t format;          /* tq_format                                          */
   int32_t head_dim;        /* TQ4: 64 or 128; MX-FP4: 128                         */
-  int32_t num_kv_heads;    /* >= 1                                                */
+  int32_t num_kv_heads;    /* 1 .. 65536                                          */
   int32_t block_size;      /* must be 16                                          */
   int64_t num_blocks;      /* >= 1                                                */
   const float *key_table;  /* TQ4 only: host pointer to 16 strictly ascending
@@ -113,8 +114,9 @@ tq_status tq_pool_bytes(const tq_cache_desc *desc, size_t *bytes);
  * handle and a small device table buffer.  Synchronous.  Errors:
  * INVALID_ARG (bad descriptor, pool too small, key table not ascending or not
  * finite), UNSUPPORTED (head_dim / format combination, or a key table whose
- * midpoints are too close for the coder's bin table: adjacent midpoints must
- * differ by more than 1/64 of the table's midpoint range), OOM, HIP. */
+ * midpoints are too close for the coder's bin table: adjacent midpoints more
+ * than 1/200 of the table's midpoint range apart are always accepted), OOM,
+ * HIP. */
 tq_status tq_create_cache(const tq_cache_desc *desc, void *pool, size_t pool_bytes, tq_cache **out);
 
 /* The pool's device address and size, and the fp16 key table in use (16 fp16

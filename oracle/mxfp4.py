@@ -15,7 +15,10 @@ conversions):
 * X = floor(log2(amax)) - 2 clamped to [-127, 127] (amax = 0 -> -127), stored
   as the byte X + 127; element code = e2m1_RNE(x / 2^X), saturating at +-6;
 * the rotated key is y = fp32(x * fp32(1/sqrt(D))) with x the fp32 butterflies
-  of ``wht.fwht_f32_unnormalized``;
+  of ``wht.fwht_f32_unnormalized``; a rotated key element that is exactly
+  zero is stored as +0 (in exact arithmetic the rotation yields an unsigned
+  zero; the sign fp32 gives it depends only on the order of the butterflies'
+  operations, not on the data).  Values keep the sign of their zeros;
 * the query is rotated the same way and cast to e4m3 (RNE, saturating, unit
   scale); the softmax scale is applied to the fp32 logits.
 
@@ -57,8 +60,9 @@ def mx_decode(codes, xexp):
 
 
 def encode_rows(k, v):
-    """FP4-encode key rows (rotated first) and value rows (not rotated)."""
-    kc, kx = mx_encode(rotate_f32(k))
+    """FP4-encode key rows (rotated first; zeros as +0) and value rows (not
+    rotated)."""
+    kc, kx = mx_encode(rotate_f32(k) + np.float32(0.0))
     vc, vx = mx_encode(np.asarray(v, dtype=np.float32))
     return {"kcode": kc, "kexp": kx, "vcode": vc, "vexp": vx}
 

@@ -38,7 +38,8 @@ def test_key_path_rotates_first():
     k = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(rng.standard_normal((50, 128)).astype(np.float32)))
     enc = mxfp4.encode_rows(k, k)
     c2, x2 = mxfp4.mx_encode(mxfp4.rotate_f32(k))
-    assert np.array_equal(enc["kcode"], c2) and np.array_equal(enc["kexp"], x2)
+    nz = mxfp4.rotate_f32(k) != 0
+    assert np.array_equal(enc["kcode"][nz], c2[nz]) and np.array_equal(enc["kexp"], x2)
     y = mxfp4.mx_decode(enc["kcode"], enc["kexp"])
     assert np.max(np.abs(y - wht.wht_f64(k))) < 0.5 * np.max(np.abs(wht.wht_f64(k)))
 
@@ -49,3 +50,20 @@ def test_query_cast_matches_torch_fp8():
     ours = mxfp4.query_fp8(q)
     ref = torch.from_numpy(mxfp4.rotate_f32(q)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(ours, ref)
+
+
+def test_zero_signs():
+    """A rotated key element that is exactly zero is stored as +0 (code 0);
+    values keep the sign of their zeros (OCP: -0 -> code 8)."""
+    k = np.full((1, 128), -0.0, np.float32)     # butterflies give -0 and +0 here
+    y = mxfp4.rotate_f32(k)
+    assert np.any(np.signbit(y)) and np.all(y == 0)
+    enc = mxfp4.encode_rows(k, k)
+    assert np.all(enc["kcode"] == 0) and np.all(enc["kexp"] == -127)
+    assert np.all(enc["vcode"] == 8) and np.all(enc["vexp"] == -127)
+    # exact cancellation: k = e0 + e1 rotates to 2/sqrt(D) on even channels, 0 on odd
+    k = np.zeros((1, 128), np.float32)
+    k[0, :2] = 1.0
+    enc = mxfp4.encode_rows(k, np.zeros_like(k))
+    y = mxfp4.mx_decode(enc["kcode"], enc["kexp"])[0]
+    assert np.all(enc["kcode"][0, 1::2] == 0) and np.all(y[1::2] == 0) and np.all(y[0::2] > 0)
