@@ -1,18 +1,24 @@
 """Benchmark of the 4-bit KV-cache hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-quantize-and-append the batch's tokens into the paged TQ4/4 cache, then decode
-attention over a cache.  The step decodes the batch quantized two steps
-earlier (R >= 3 rotating copies of inputs and pools, R * bytes >= 2x the 256 MB
-Infinity Cache), so the decode reads its 4-bit cache from HBM rather than from
-the cache the quantize kernel just wrote; every batch still goes through both
-kernels.  Inputs are resident in HBM before the timed region starts.
+quantize-and-append the batch's tokens into the paged cache, then decode
+attention over a cache (the longprefix workload appends one token per sequence
+before each of its 64 decodes).  The step decodes the pool quantized two steps
+earlier.  Inputs and pools rotate over enough copies that each kernel's
+distinct data spans at least twice the 256 MB Infinity Cache, so every launch
+reads from HBM.  Inputs are resident in HBM before any timed region starts.
+
+Timing (HIP events on the launch stream, the host queue filled first):
+  * ms_per_step: K whole steps between two events;
+  * per-kernel launch time: K back-to-back launches of the kernel alone over
+    the rotating copies between two events (the decode launch includes its
+    split merge), so that event markers add nothing to each kernel.
 
 Output: one JSON line.  ``value`` is the decode's effective KV bandwidth
 (logical 4-bit KV bytes read / decode time); ``quantize_tokens_per_s`` the
-quantize rate; ``roofline`` the dominant kernel (by time) against the 8 TB/s
-HBM peak, with its average launch time measured by HIP events on the launch
-stream; ``cpu_baseline`` the CPU oracle timed on this host on a bounded sample.
+quantize rate; ``roofline`` the kernel that takes most of the step time
+against the 8 TB/s HBM peak; ``cpu_baseline`` the CPU oracle timed on this
+host on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama8b]
 """
@@ -102,12 +108,14 @@ class Bench:
         self.row_bytes = rec_bytes // 16
         pool_bytes = rec_bytes * c.num_kv_heads * w.num_blocks
         in_bytes = k0.numel() * 4
-        if copies <= 0:
-            copies = max(3, -(-2 * 256 * 2 ** 20 // (pool_bytes + in_bytes)))
-        self.copies = copies
-        self.kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+        # rotating copies so that no launch finds its data in the 256 MB
+        # Infinity Cache: every kernel's distinct data spans >= 2x its size
+        mall2 = 2 * 256 * 2 ** 20
+        self.in_copies = copies if copies > 0 else max(3, -(-mall2 // in_bytes))
+        self.pool_copies = copies if copies > 0 else max(3, -(-mall2 // pool_bytes))
+        self.kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(self.in_copies - 1)]
         self.slots = s0
-        self.caches = [Cache(c.fmt, c.head_dim, c.num_kv_heads, w.num_blocks) for _ in range(copies)]
+        self.caches = [Cache(c.fmt, c.head_dim, c.num_kv_heads, w.num_blocks) for _ in range(self.pool_copies)]
         self.table = i32(w.block_table)
         self.q = [dev(w.query_bits(s)) for s in range(c.decode_steps)]
         self.ctx = [i32(w.context_lens_at(s)) for s in range(c.decode_steps)]
@@ -145,27 +153,27 @@ class Bench:
         other = c.batch * c.num_q_heads * c.head_dim * (2 + 4) + int((-(-lens // 16)).sum()) * 4 + c.batch * 4
         return kv, kv + other
 
-    # one step --------------------------------------------------------------------
-    def step(self, i, ev=None):
+    # launches --------------------------------------------------------------------
+    def quantize(self, i):
+        k, v = self.kv[i % self.in_copies]
+        self.caches[i % self.pool_copies].quantize_append(k, v, self.slots)
+
+    def decode(self, i, s):
         c = self.cfg
-        qc = i % self.copies
-        dc = (i - 2) % self.copies
-        k, v = self.kv[qc]
-        if ev is not None:
-            ev["q0"].record(self.stream)
-        self.caches[qc].quantize_append(k, v, self.slots)
-        if ev is not None:
-            ev["q1"].record(self.stream)
-        cache = self.caches[dc]
+        self.caches[i % self.pool_copies].decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s], c.scale,
+                                                 out=self.out)
+
+    def step(self, i):
+        """One pass of the whole path: quantize-append batch i into pool copy
+        i, then (append one token per sequence and) decode over pool copy i-2."""
+        c = self.cfg
+        self.quantize(i)
+        dc = (i - 2) % self.pool_copies
         for s in range(c.decode_steps):
             if self.appends:
                 ka, va, sa = self.appends[s]
-                cache.quantize_append(ka, va, sa)
-            if ev is not None:
-                ev["d0"][s].record(self.stream)
-            cache.decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s], c.scale, out=self.out)
-            if ev is not None:
-                ev["d1"][s].record(self.stream)
+                self.caches[dc].quantize_append(ka, va, sa)
+            self.decode(dc, s)
 
 
 def cpu_baseline(cfg_name, budget_s=10.0):
@@ -268,15 +276,23 @@ def gpu_spin(ms):
     torch.cuda._sleep(int(ms * _SPIN_CYCLES_PER_MS))
 
 
-def enqueue_time(bench, i, ev):
-    """Host seconds to enqueue one step (measured behind a GPU spin)."""
-    import torch
-    gpu_spin(50.0)
+def timed(torch, stream, launches, enqueue):
+    """Average GPU time of `launches` calls of enqueue(j), measured with two HIP
+    events on the launch stream around them.  A GPU spin placed first lets the
+    host queue every launch before the first one runs, so host enqueue time
+    does not show up as gaps between kernels."""
     t0 = time.perf_counter()
-    bench.step(i, ev)
-    t1 = time.perf_counter()
+    enqueue(0)
     torch.cuda.synchronize()
-    return t1 - t0
+    per = time.perf_counter() - t0
+    gpu_spin(1.5 * per * launches * 1e3 + 2.0)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for j in range(launches):
+        enqueue(j)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / launches
 
 
 def main():
@@ -293,34 +309,20 @@ def main():
     torch.cuda.set_device(0)
     bench = Bench(workloads.CONFIGS[args.config], args.copies)
     c = bench.cfg
-    for i in range(args.warmup + bench.copies):
+    stream = bench.stream
+    for i in range(args.warmup + bench.pool_copies):
         bench.step(i)
     torch.cuda.synchronize()
 
-    mk = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [{"q0": mk(), "q1": mk(), "d0": [mk() for _ in range(c.decode_steps)],
-            "d1": [mk() for _ in range(c.decode_steps)]} for _ in range(args.steps)]
-    start, stop = mk(), mk()
-    # The host enqueues slower than these kernels run, so a GPU spin placed
-    # before the timed region lets every step be queued first; the start
-    # event then fires when the spin ends, and each kernel's events bracket
-    # only its own execution.
-    host_per_step = enqueue_time(bench, args.warmup + bench.copies, evs[0])
-    spin_ms = 1.5 * host_per_step * args.steps * 1e3 + 2.0
-    torch.cuda.synchronize()
-    gpu_spin(spin_ms)
-    start.record(bench.stream)
-    base = args.warmup + bench.copies
-    for i in range(args.steps):
-        bench.step(base + i, evs[i])
-    stop.record(bench.stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    qt = sum(e["q0"].elapsed_time(e["q1"]) for e in evs)
-    dt = [sum(e["d0"][s].elapsed_time(e["d1"][s]) for e in evs) for s in range(c.decode_steps)]
+    # 1. the whole path: K steps between two events
+    base = args.warmup + bench.pool_copies
+    step_ms = timed(torch, stream, args.steps, lambda j: bench.step(base + j))
+    # 2. each kernel alone, back to back over the rotating copies (the decode
+    #    launch includes its split merge)
+    q_ms = timed(torch, stream, args.steps, lambda j: bench.quantize(base + j))
+    nd = args.steps * c.decode_steps
+    d_ms = timed(torch, stream, nd, lambda j: bench.decode(j, j % c.decode_steps))
 
-    q_ms = qt / args.steps
-    d_ms = sum(dt) / (args.steps * c.decode_steps)
     kv_logical = sum(bench.decode_bytes(s)[0] for s in range(c.decode_steps)) / c.decode_steps
     kv_unique = sum(bench.decode_bytes(s, unique=True)[0] for s in range(c.decode_steps)) / c.decode_steps
     dec_alg = sum(bench.decode_bytes(s, unique=True)[1] for s in range(c.decode_steps)) / c.decode_steps
@@ -332,17 +334,13 @@ def main():
         "decode": {"avg_us": d_ms * 1e3, "bytes": dec_alg, "GBps": dec_alg / (d_ms * 1e-3) / 1e9},
     }
     dominant = "quantize" if q_ms >= d_ms * c.decode_steps else "decode"
-    kd = kernels[dominant]
-    traffic = traffic_from_profiles(args.config, dominant)
-    roof = {"bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
-            "bytes_per_launch": kd["bytes"], "avg_launch_us": round(kd["avg_us"], 2)}
-    other = "decode" if dominant == "quantize" else "quantize"
-    ko = kernels[other]
-    roof_other = {"bound": "hbm", "achieved": round(ko["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                  "frac": round(ko["GBps"] / HBM_PEAK_GBPS, 4), "kernel": other,
-                  "bytes_per_launch": ko["bytes"], "avg_launch_us": round(ko["avg_us"], 2),
-                  "traffic": traffic_from_profiles(args.config, other)}
+
+    def roof(name):
+        k = kernels[name]
+        return {"bound": "hbm", "achieved": round(k["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(k["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(args.config, name),
+                "kernel": name, "bytes_per_launch": k["bytes"], "avg_launch_us": round(k["avg_us"], 2)}
+
     res = {
         "metric": "4-bit KV decode attn: effective KV GB/s & % HBM peak; quantize tokens/s",
         "value": round(decode_gbps, 1),
@@ -350,7 +348,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total_ms / args.steps, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -360,13 +358,13 @@ def main():
                                f"head_dim {c.head_dim}, context {int(bench.w.context_lens_at(0).max())}, "
                                f"format {'TQ4/4' if c.fmt == 0 else 'MX-FP4'}",
                    "tokens_quantized_per_step": bench.n_tokens, "decode_steps_per_step": c.decode_steps,
-                   "copies": bench.copies},
+                   "input_copies": bench.in_copies, "pool_copies": bench.pool_copies},
         "decode_hbm_frac": round(kv_unique / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "decode_us": round(d_ms * 1e3, 2),
         "quantize_us": round(q_ms * 1e3, 2),
         "quantize_tokens_per_s": round(bench.n_tokens / (q_ms * 1e-3), 1),
-        "roofline": roof,
-        "roofline_other": roof_other,
+        "roofline": roof(dominant),
+        "roofline_other": roof("decode" if dominant == "quantize" else "quantize"),
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -111,6 +111,36 @@ struct WaveState {
   float4v acc[G2];  // out^T tiles: rows = channels, columns = operand columns
 };
 
+// Online softmax over one 16-token block with lazy rescale.  x: this lane's
+// four logits (log2 units; -inf for rows past the context), column n = lane %
+// 16; the four lanes n, n+16, n+32, n+48 of a column share its running max.
+// The common case needs no cross-lane work: a lane only checks whether one of
+// its own logits exceeds the running max by more than kLazyRescale; when some
+// lane does, the columns' block maxima are reduced and the raised columns
+// rescale their accumulators.  Leaves p = 2^(x - m) and adds them to st.l.
+template <int G2>
+__device__ __forceinline__ void softmax_block(const float (&x)[4], WaveState<G2> &st, float (&p)[4]) {
+  // v_max3 + v_max written out: the logits need no canonicalizing first
+  float lm;
+  __asm__("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4"
+          : "=&v"(lm)
+          : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+  if (__builtin_amdgcn_ballot_w64(lm > st.m + kLazyRescale) != 0) {
+    float bm = __builtin_fmaxf(lm, xor16(lm));
+    bm = __builtin_fmaxf(bm, xor32(bm));
+    const bool raise = bm > st.m + kLazyRescale;
+    const float m_new = raise ? bm : st.m;
+    const float alpha = (st.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < G2; ++t) st.acc[t] *= alpha;
+    st.m = m_new;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+}
+
 // Combine the NW waves of a work-group and write either the output (single
 // split) or a split partial.  s_m / s_l / s_acc are LDS scratch.
 template <int D, int GQ, int NW>

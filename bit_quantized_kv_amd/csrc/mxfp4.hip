@@ -169,13 +169,20 @@ __device__ __forceinline__ uint32_t word4(const uint4 &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// tail: the partial last block of its sequence (rows past the context masked).
 template <int GQ>
 __device__ __forceinline__ void do_block4(const Blk4 &bk, const int8v &bq8, uint32_t *vs_slot, WaveState<8> &st,
                                           float qscale, float lo_mask, int lane, int tok0, int T, bool tail,
                                           uint32_t vs_keep) {
   // exponent bytes of rows past the context are cleared (those rows then
-  // dequantize to exactly 0), at the use so no early wait on the loads is forced
-  vs_slot[(lane >> 4) * 4 + (lane & 3)] = tail ? (bk.vsw & vs_keep) : bk.vsw;
+  // dequantize to exactly 0), at the use so no early wait on the loads is
+  // forced; the tail fix-ups sit behind real branches
+  uint32_t vsw = bk.vsw;
+  if (tail) {
+    __asm__ volatile("");
+    vsw &= vs_keep;
+  }
+  vs_slot[(lane >> 4) * 4 + (lane & 3)] = vsw;
   // ---- logits: one scaled MFMA per block ------------------------------------------
   const int8v ak = (int8v){(int)bk.kq.x, (int)bk.kq.y, (int)bk.kq.z, (int)bk.kq.w, 0, 0, 0, 0};
   float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
@@ -184,27 +191,13 @@ __device__ __forceinline__ void do_block4(const Blk4 &bk, const int8v &bq8, uint
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = qk[i] * qscale;
   if (tail) {
+    __asm__ volatile("");
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (tok0 + i >= T) x[i] = kNegInf;
   }
-  // ---- online softmax with lazy rescale ---------------------------------------
-  float bm = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
-  bm = __builtin_fmaxf(bm, xor16(bm));
-  bm = __builtin_fmaxf(bm, xor32(bm));
-  const bool raise = bm > st.m + kLazyRescale;
-  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-    const float m_new = raise ? bm : st.m;
-    const float alpha = (st.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) st.acc[t] *= alpha;
-    st.m = m_new;
-  }
   float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  softmax_block<8>(x, st, p);
   half4v bp;
   {
     const half2v h02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[2]));
@@ -253,11 +246,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   const int b = task.b, kvh = task.kvh, sp = task.sp;
   const int qh0 = kvh * GQ;
   const int T = a.ctx[b];  // a scalar load: nothing is written before it
+  // this wave's block ids, fetched before the context length is known (index
+  // clamped into the table row; entries past the context are never used)
+  const int blk0 = sp * a.split_blocks;
+  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
+  const int my_id_raw = btab[min(blk0 + wv + lane * NW, a.max_blocks - 1)];
   // the query word next: it completes while the block ids are fetched
   const uint32_t q_w = wv < GQ ? load_query_word<kD>(a.q + ((int64_t)b * a.hq + qh0 + wv) * kD, lane) : 0u;
   __asm__ volatile("" ::: "memory");
   const int nblk = (T + 15) >> 4;
-  const int blk0 = sp * a.split_blocks;
   if (nblk == 0) {
     if (a.nsplit == 1 && sp == 0) write_zero_rows<kD>(a, b, qh0, GQ);
     return;
@@ -265,11 +262,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   if (blk0 >= nblk) return;
   const int blk1 = min(nblk, blk0 + a.split_blocks);
 
-  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
   const uint8_t *base = a.pool + (int64_t)kvh * kRec;
   const int64_t stride = (int64_t)a.hkv * kRec;
   const int mine = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
-  const int my_id = settled(btab[blk0 + wv + (lane < mine ? lane : 0) * NW]);
+  const int my_id = settled(my_id_raw);
   auto rec_of = [&](int k) {
     const int kk = k < mine ? k : mine - 1;
     return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;

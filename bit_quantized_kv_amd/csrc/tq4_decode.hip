@@ -75,6 +75,8 @@ __device__ __forceinline__ void load_blk(Blk<D> &o, const uint8_t *rec, int lane
 // context, so those rows dequantize to exactly 0 whatever the pool holds
 // (applied here, at the use, so that no wait on the block's loads is forced
 // earlier).
+// tail: the block is the partial last one of its sequence (rows past the
+// context are masked: -inf logits, zero value scale and minimum).
 template <int D, int GQ>
 __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D / 32], const uint32_t *s_lut,
                                          uint32_t *vm_slot, WaveState<2 * D / 32> &st, float lo_mask, int lane,
@@ -82,7 +84,14 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
   constexpr int G = D / 32, KS = D / 32;
   // the value (scale, min) tile goes through LDS: lane (r, c) wrote dword c of
   // row r; every lane reads its row's 16*G bytes back (broadcast reads)
-  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = tail ? (bk.vmw & vm_keep) : bk.vmw;
+  // (the tail fix-ups sit behind real branches: an if-converted select would
+  // cost every block several instructions)
+  uint32_t vmw = bk.vmw;
+  if (tail) {
+    __asm__ volatile("");
+    vmw &= vm_keep;
+  }
+  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = vmw;
   // ---- logits ---------------------------------------------------------------
   float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -96,34 +105,21 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
     qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, e), bq[s], qk, 0, 0, 0);
   }
   const half2v s01 = as_h2(bk.ks.x), s23 = as_h2(bk.ks.y);
+  // logit = (high + low column) * key scale, one v_fma_mix each (the fp16
+  // scale taken directly; the +0 addend only turns a -0 product into +0)
   float x[4];
-  x[0] = (qk[0] + xor_g<GQ>(qk[0])) * (float)s01[0];
-  x[1] = (qk[1] + xor_g<GQ>(qk[1])) * (float)s01[1];
-  x[2] = (qk[2] + xor_g<GQ>(qk[2])) * (float)s23[0];
-  x[3] = (qk[3] + xor_g<GQ>(qk[3])) * (float)s23[1];
+  x[0] = __builtin_fmaf(qk[0] + xor_g<GQ>(qk[0]), (float)s01[0], 0.0f);
+  x[1] = __builtin_fmaf(qk[1] + xor_g<GQ>(qk[1]), (float)s01[1], 0.0f);
+  x[2] = __builtin_fmaf(qk[2] + xor_g<GQ>(qk[2]), (float)s23[0], 0.0f);
+  x[3] = __builtin_fmaf(qk[3] + xor_g<GQ>(qk[3]), (float)s23[1], 0.0f);
   if (tail) {
+    __asm__ volatile("");
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (tok0 + i >= T) x[i] = kNegInf;
   }
-
-  // ---- online softmax with lazy rescale ----------------------------------------
-  float bm = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3]));
-  bm = __builtin_fmaxf(bm, xor16(bm));
-  bm = __builtin_fmaxf(bm, xor32(bm));
-  const bool raise = bm > st.m + kLazyRescale;
-  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-    const float m_new = raise ? bm : st.m;
-    const float alpha = (st.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int t = 0; t < 2 * G; ++t) st.acc[t] *= alpha;
-    st.m = m_new;
-  }
   float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  softmax_block<2 * G>(x, st, p);
   // B operand: k-slot order tokens 4r + (0, 2, 1, 3); high part on columns < g,
   // low part (p - high) on columns g .. 2g-1; other columns are never read
   half4v bp;
@@ -181,13 +177,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   const int qh0 = kvh * GQ;
 
   const int T = a.ctx[b];  // a scalar load: nothing is written before it
+  // this wave's block ids, fetched before the context length is known (the
+  // index is clamped into the table row; entries past the context are never
+  // used): blocks blk0 + wv + k * NW, lane k holds the id of the k-th
+  const int blk0 = sp * a.split_blocks;
+  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
+  const int my_id_raw = btab[min(blk0 + wv + lane * NW, a.max_blocks - 1)];
   // set-up loads next (table word, query word): they complete while the block
   // ids are fetched, so the set-up below waits on nothing
   const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
   const uint32_t q_w = wv < GQ ? load_query_word<D>(a.q + ((int64_t)b * a.hq + qh0 + wv) * D, lane) : 0u;
   __asm__ volatile("" ::: "memory");
   const int nblk = (T + 15) >> 4;
-  const int blk0 = sp * a.split_blocks;
   if (nblk == 0) {
     if (a.nsplit == 1 && sp == 0) write_zero_rows<D>(a, b, qh0, GQ);
     return;
@@ -196,7 +197,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   const int blk1 = min(nblk, blk0 + a.split_blocks);
 
   // ---- first loads go out before the set-up work -----------------------------
-  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
   const uint8_t *base = a.pool + (int64_t)kvh * REC;
   const int64_t stride = (int64_t)a.hkv * REC;
   // this wave's blocks: blk0 + wv + k * NW, k < mine (mine <= 64); lane k
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   // wave's last block again, an L2 hit), so the number of loads in flight is
   // the same on every path and the waits stay partial.
   const int mine = blk1 - blk0 > wv ? (blk1 - blk0 - wv + NW - 1) / NW : 0;
-  const int my_id = settled(btab[blk0 + wv + (lane < mine ? lane : 0) * NW]);
+  const int my_id = settled(my_id_raw);
   auto rec_of = [&](int k) {
     const int kk = k < mine ? k : mine - 1;
     return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
@@ -282,52 +282,58 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 }
 
 // One work-group per (sequence, query head): combine the split partials.
-// Pass 1 finds the largest partial maximum; in pass 2 thread t takes channels
-// 4*(t % (D/4)) .. +3 of splits s = t / (D/4) (mod 256 / (D/4)) with weights
-// exp2(m_s - M) (independent loads), and the slices are summed in LDS.
+// Every wave finds the largest partial maximum M on its own (lane-strided
+// loads, a wave reduction: no barrier); then thread (cq, sl) sums channels
+// 4*cq .. 4*cq+3 of splits sl, sl + SL, ... with weights 2^(m_s - M), loads
+// independent of each other, and the SL slices are added in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int CQ = D / 4;          // channel quads
   constexpr int SL = 256 / CQ;       // split lanes
-  __shared__ float s_red[256];
-  __shared__ float s_l[SL];
+  __shared__ float s_l[SL][CQ];
   __shared__ float4 s_acc[SL][CQ];
   const int64_t row = blockIdx.x;
   const int b = (int)(row / a.hq);
   const int T = a.ctx[b];
   const int nblk = (T + 15) >> 4;
   const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
-  const int tid = threadIdx.x, cq = tid % CQ, sl = tid / CQ;
+  const int tid = threadIdx.x, lane = tid & 63, cq = tid % CQ, sl = tid / CQ;
   const float *ml = a.part_ml + row * a.nsplit * 2;
   const float *pa = a.part_acc + row * a.nsplit * D;
-  float mx = kNegInf;
-  for (int s = tid; s < ns; s += 256) mx = __builtin_fmaxf(mx, ml[2 * s]);
-  s_red[tid] = mx;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] = __builtin_fmaxf(s_red[tid], s_red[tid + w]);
-    __syncthreads();
-  }
-  const float M = s_red[0];
+  float M = kNegInf;
+  for (int sp = lane; sp < ns; sp += 64) M = __builtin_fmaxf(M, ml[2 * sp]);
+  M = __builtin_fmaxf(M, xor1(M));
+  M = __builtin_fmaxf(M, xor2(M));
+  M = __builtin_fmaxf(M, xor4(M));
+  M = __builtin_fmaxf(M, xor8(M));
+  M = __builtin_fmaxf(M, xor16(M));
+  M = __builtin_fmaxf(M, xor32(M));
   float den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-  for (int s = sl; s < ns; s += SL) {
-    const float m = ml[2 * s], l = ml[2 * s + 1];
-    const float4 v = *reinterpret_cast<const float4 *>(pa + (int64_t)s * D + 4 * cq);
-    const float f = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    den += f * l;
-    num.x += f * v.x; num.y += f * v.y; num.z += f * v.z; num.w += f * v.w;
+  for (int sp = sl; sp < ns; sp += SL) {
+    const float2 m_l = reinterpret_cast<const float2 *>(ml)[sp];
+    const float4 v = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
+    const float f = (m_l.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_l.x - M);
+    den += f * m_l.y;
+    num.x += f * v.x;
+    num.y += f * v.y;
+    num.z += f * v.z;
+    num.w += f * v.w;
   }
-  if (cq == 0) s_l[sl] = den;
+  s_l[sl][cq] = den;
   s_acc[sl][cq] = num;
   __syncthreads();
   if (sl == 0) {
     float L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
     for (int i = 0; i < SL; ++i) {
-      L += s_l[i];
-      o.x += s_acc[i][cq].x; o.y += s_acc[i][cq].y; o.z += s_acc[i][cq].z; o.w += s_acc[i][cq].w;
+      L += s_l[i][cq];
+      o.x += s_acc[i][cq].x;
+      o.y += s_acc[i][cq].y;
+      o.z += s_acc[i][cq].z;
+      o.w += s_acc[i][cq].w;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};

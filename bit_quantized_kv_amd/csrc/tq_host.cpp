@@ -199,7 +199,9 @@ tq_status tq_decode_workspace_bytes(const tq_cache *cache, int32_t batch, int32_
   if (batch < 0 || num_q_heads < 1 || max_context_len < 0)
     return fail(TQ_ERR_INVALID_ARG, "batch, num_q_heads or max_context_len out of range");
   const tq::SplitPlan p = tq::plan_split(batch, cache->desc.num_kv_heads, max_context_len);
-  *bytes = p.nsplit > 1 ? (size_t)batch * num_q_heads * p.nsplit * (size_t)(cache->desc.head_dim + 2) * 4 : 0;
+  // (max, sum) pairs, then the accumulators from a 256-byte boundary
+  const size_t rows = (size_t)batch * num_q_heads * p.nsplit;
+  *bytes = p.nsplit > 1 ? ((rows * 2 * 4 + 255) / 256) * 256 + rows * (size_t)cache->desc.head_dim * 4 : 0;
   return TQ_OK;
 }
 
@@ -240,7 +242,7 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
   const int d = cache->desc.head_dim;
   if (p.nsplit > 1) {
     a.part_ml = static_cast<float *>(workspace);
-    a.part_acc = a.part_ml + (size_t)batch * num_q_heads * p.nsplit * 2;
+    a.part_acc = a.part_ml + (((size_t)batch * num_q_heads * p.nsplit * 2 + 63) / 64) * 64;
   }
   const double log2e = 1.4426950408889634074;
   a.rsqrt_d = (float)(1.0 / std::sqrt((double)d));

@@ -185,9 +185,11 @@ SplitPlan plan_split(int batch, int hkv, int max_context_len) {
     }
   }
   int64_t s = best_s;
+  // override for tests; a wave keeps at most 64 block ids (one per lane), so a
+  // work-group of 8 waves takes at most 512 blocks
   if (const char *env = std::getenv("TQ_SPLIT_BLOCKS")) {
     const long v = std::strtol(env, nullptr, 10);
-    if (v >= 1 && v <= 65536) s = v;
+    if (v >= 1 && v <= 512) s = v;
   }
   SplitPlan p;
   p.split_blocks = (int)s;

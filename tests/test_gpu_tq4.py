@@ -17,11 +17,12 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(autouse=True)
 def _split_env():
-    old = os.environ.pop("TQ_SPLIT_BLOCKS", None)
+    saved = {k: os.environ.pop(k, None) for k in ("TQ_SPLIT_BLOCKS",)}
     yield
-    os.environ.pop("TQ_SPLIT_BLOCKS", None)
-    if old is not None:
-        os.environ["TQ_SPLIT_BLOCKS"] = old
+    for k, v in saved.items():
+        os.environ.pop(k, None)
+        if v is not None:
+            os.environ[k] = v
 
 
 def _check_case(case, seqs=None, rows=None, step=0):
@@ -82,6 +83,30 @@ def test_edge_lengths_and_zero_context():
     ref = case.oracle_decode(op, rows, ctx=ctx)
     assert np.all(out[ctx == 0] == 0)
     assert row_rel_err(out, ref) <= TOL
+
+
+def test_split_merge_with_zero_and_short_contexts():
+    """Many splits per sequence merged by the merge kernel, mixed with a
+    sequence without tokens and one that fits in a single split; repeated
+    calls give the same result."""
+    cfg = workloads.small_config(batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(300, 900), seed=114)
+    case = Case(cfg)
+    ranges = case.write_ranges()
+    case.quantize(ranges)
+    op = case.oracle_pool(ranges)
+    ctx = case.w.prompt_lens.astype(np.int32).copy()
+    ctx[1], ctx[4] = 0, 100
+    os.environ["TQ_SPLIT_BLOCKS"] = "8"
+    say(f"case: split merge, contexts {ctx.tolist()}")
+    rows = [(b, h) for b in range(6) for h in range(8)]
+    ref = case.oracle_decode(op, rows, ctx=ctx)
+    first = None
+    for _ in range(3):
+        out = case.decode(ctx=ctx)
+        assert np.all(out[1] == 0)
+        assert row_rel_err(out, ref) <= TOL
+        first = out if first is None else first
+        assert np.array_equal(out, first)
 
 
 def test_bf16_output():
