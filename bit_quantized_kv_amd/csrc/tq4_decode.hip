@@ -44,10 +44,11 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
 }
 __device__ __forceinline__ uint32_t word(const uint2 &v, int i) { return i == 0 ? v.x : v.y; }
 
-// fp16 values (1024 + code) of four 4-bit codes taken from nibble-isolated
-// bytes: v_perm places byte pairs under the 0x64 exponent byte.
-__device__ __forceinline__ half2v magic_pair(uint32_t nib_bytes, uint32_t sel) {
-  return as_h2(__builtin_amdgcn_perm(0x64646464u, nib_bytes, sel));
+// Two 4-bit codes, each alone in a byte of `bytes` (word `hi_word`), as exact
+// fp16 values: 0000cccc is the OCP e4m3 encoding of c * 2^-9.
+template <bool HI_WORD>
+__device__ __forceinline__ half2v codes_f16(uint32_t bytes) {
+  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
 }
 
 template <int D>
@@ -120,23 +121,26 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
   }
   float p[4];
   softmax_block<2 * G>(x, st, p);
-  // B operand: k-slot order tokens 4r + (0, 2, 1, 3); high part on columns < g,
-  // low part (p - high) on columns g .. 2g-1; other columns are never read
+  // B operand: tokens 4r + 0..3 in k order; high part on columns < g, low
+  // part (p - high) on columns g .. 2g-1; other columns are never read
   half4v bp;
   {
-    const half2v h02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[2]));
-    const half2v h13 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[1], p[3]));
-    const float r0 = __builtin_fmaf(-lo_mask, (float)h02[0], p[0]);
-    const float r2 = __builtin_fmaf(-lo_mask, (float)h02[1], p[2]);
-    const float r1 = __builtin_fmaf(-lo_mask, (float)h13[0], p[1]);
-    const float r3 = __builtin_fmaf(-lo_mask, (float)h13[1], p[3]);
-    const half2v a02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r2));
-    const half2v a13 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r1, r3));
-    bp = (half4v){a02[0], a02[1], a13[0], a13[1]};
+    const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
+    const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
+    const float r0 = __builtin_fmaf(-lo_mask, (float)h01[0], p[0]);
+    const float r1 = __builtin_fmaf(-lo_mask, (float)h01[1], p[1]);
+    const float r2 = __builtin_fmaf(-lo_mask, (float)h23[0], p[2]);
+    const float r3 = __builtin_fmaf(-lo_mask, (float)h23[1], p[3]);
+    const half2v a01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    const half2v a23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r2, r3));
+    bp = (half4v){a01[0], a01[1], a23[0], a23[1]};
   }
 
   // ---- values -----------------------------------------------------------------
-  const half2v k1024 = (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
+  // A nibble isolated in a byte, 0000cccc, is the OCP e4m3 encoding of
+  // c * 2^-9 (codes 0..7 subnormal, 8..15 with exponent field 1), so the fp8
+  // conversion with scale 2^9 turns two such bytes into two exact fp16 codes;
+  // one fma with the fp16 (scale, min) pair then dequantizes with one rounding.
   const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
 #pragma unroll
   for (int gp = 0; gp < G; ++gp) {
@@ -144,14 +148,14 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
     const uint4 vm = vm_row[gp];
     // bytes = tokens 4r + 0..3 of one channel pair; low nibble = even channel
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    const half2v sc02 = as_h2(vm.x), sc13 = as_h2(vm.y);
-    const half2v mn02 = as_h2(vm.z), mn13 = as_h2(vm.w);
-    const half2v e02 = __builtin_elementwise_fma(magic_pair(lo, 0x04020400u) - k1024, sc02, mn02);
-    const half2v e13 = __builtin_elementwise_fma(magic_pair(lo, 0x04030401u) - k1024, sc13, mn13);
-    const half2v o02 = __builtin_elementwise_fma(magic_pair(hi, 0x04020400u) - k1024, sc02, mn02);
-    const half2v o13 = __builtin_elementwise_fma(magic_pair(hi, 0x04030401u) - k1024, sc13, mn13);
-    const half4v ae = __builtin_bit_cast(half4v, make_uint2(as_u(e02), as_u(e13)));
-    const half4v ao = __builtin_bit_cast(half4v, make_uint2(as_u(o02), as_u(o13)));
+    const half2v sc01 = as_h2(vm.x), sc23 = as_h2(vm.y);
+    const half2v mn01 = as_h2(vm.z), mn23 = as_h2(vm.w);
+    const half2v e01 = __builtin_elementwise_fma(codes_f16<false>(lo), sc01, mn01);
+    const half2v e23 = __builtin_elementwise_fma(codes_f16<true>(lo), sc23, mn23);
+    const half2v o01 = __builtin_elementwise_fma(codes_f16<false>(hi), sc01, mn01);
+    const half2v o23 = __builtin_elementwise_fma(codes_f16<true>(hi), sc23, mn23);
+    const half4v ae = __builtin_bit_cast(half4v, make_uint2(as_u(e01), as_u(e23)));
+    const half4v ao = __builtin_bit_cast(half4v, make_uint2(as_u(o01), as_u(o23)));
     st.acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x16f16(ae, bp, st.acc[2 * gp], 0, 0, 0);
     st.acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ao, bp, st.acc[2 * gp + 1], 0, 0, 0);
   }
@@ -214,8 +218,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   const int tail_blk = (T & 15) ? nblk - 1 : nblk;
   uint32_t tail_keep;
   {
-    const int r0 = 4 * (lane >> 4), w = lane & 3;  // dword w of a group: SC02 SC13 MN02 MN13
-    const int ta = (T & 15) - (r0 + (w & 1)), tb = ta - 2;
+    // dword w of a group's 16 bytes: (sc t0, t1) (sc t2, t3) (mn t0, t1) (mn t2, t3)
+    const int r0 = 4 * (lane >> 4), w = lane & 3;
+    const int ta = (T & 15) - (r0 + 2 * (w & 1)), tb = ta - 1;
     tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
   }
   Blk<D> b0, b1, b2, b3;

@@ -138,7 +138,7 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
   const bool aligned = quad_aligned<D>(slot, tq);
   const uint32_t vt0 = quad_transpose<D>(vc0, tq), vt1 = quad_transpose<D>(vc1, tq);
   const uint32_t scmn = scb | ((uint32_t)h_bits(mn16) << 16);
-  const uint32_t scmn_p = tok_xor2<D>(scmn);
+  const uint32_t scmn_p = tok_xor1(scmn);
   if (slot >= 0) {
     const int64_t blk = slot >> 4;
     const int t = slot & 15;
@@ -152,10 +152,11 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
       // lane tq writes the quad's bytes of channel pairs j0 + tq and j0 + 4 + tq
       *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + tq) * G + gp) * 4) = vt0;
       *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + 4 + tq) * G + gp) * 4) = vt1;
-      if ((li & 1) == 0 && tq < 2) {
+      if ((li & 1) == 0 && (tq & 1) == 0) {
+        // tokens tq, tq + 1: their scales form one dword, their minima another
         uint8_t *vm = rec + OFF_VM + (r * G + gp) * 16;
-        *reinterpret_cast<uint32_t *>(vm + 4 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(vm + 8 + 4 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x07060302u);
+        *reinterpret_cast<uint32_t *>(vm + 2 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vm + 8 + 2 * tq) = __builtin_amdgcn_perm(scmn_p, scmn, 0x07060302u);
       }
     } else {
       const int tt = t & 3;
@@ -163,10 +164,9 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
       for (int k = 0; k < 8; ++k)
         rec[OFF_VC + ((r * 16 + j0 + k) * G + gp) * 4 + tt] = (uint8_t)((k < 4 ? vc0 : vc1) >> (8 * (k & 3)));
       if ((li & 1) == 0) {
-        const int pos = (tt == 1) ? 2 : (tt == 2) ? 1 : tt;
         uint16_t *vm = reinterpret_cast<uint16_t *>(rec + OFF_VM) + (r * G + gp) * 8;
-        vm[pos] = (uint16_t)scb;
-        vm[4 + pos] = h_bits(mn16);
+        vm[tt] = (uint16_t)scb;
+        vm[4 + tt] = h_bits(mn16);
       }
     }
   }

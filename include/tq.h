@@ -42,8 +42,8 @@
  *     Kc  16*P B   pair p of token t at ((p / Q) * 16 + t) * Q + p % Q
  *     Ks  32 B     fp16 s of token t at 2t
  *     Vc  16*P B   pair p = 16*gp + j of token t at ((r*16 + j)*G + gp)*4 + tt
- *     Vm  64*G B   pos = {0,2,1,3}[tt]: sc(t,gp) at 2*((r*G + gp)*8 + pos),
- *                  mn(t,gp) at 2*((r*G + gp)*8 + 4 + pos)
+ *     Vm  64*G B   sc(t,gp) at 2*((r*G + gp)*8 + tt),
+ *                  mn(t,gp) at 2*((r*G + gp)*8 + 4 + tt)
  *
  * MX-FP4 (format 1, D = 128).  Per (token, kv-head), groups of 32 channels:
  *   keys are rotated first, y = fp32(x * fp32(1/sqrt(D))), an exactly zero y

@@ -17,8 +17,8 @@ TQ4/4 record (D = 64 or 128), sections in this order:
   Kc  16*P bytes  key codes:     pair p of token t at  ((p // Q) * 16 + t) * Q + p % Q
   Ks  16*2 bytes  key scales:    fp16 s_t at byte 2t
   Vc  16*P bytes  value codes:   pair p = 16*gp + j of token t at ((r*16 + j)*G + gp)*4 + tt
-  Vm  16*G*4 B    value scale/min: with pos = [0, 2, 1, 3][tt],
-                   sc(t, gp) at 2*((r*G + gp)*8 + pos),  mn(t, gp) at 2*((r*G + gp)*8 + 4 + pos)
+  Vm  16*G*4 B    value scale/min:
+                   sc(t, gp) at 2*((r*G + gp)*8 + tt),  mn(t, gp) at 2*((r*G + gp)*8 + 4 + tt)
   Record bytes: 2336 (D=128), 1184 (D=64)  = 16 * (D/2 + 2 + D/2 + G*4).
 
 MX-FP4 record (D = 128 only), sections in this order:
@@ -35,7 +35,6 @@ section offset map is a bijection onto its section, nibble pack/unpack over all
 import numpy as np
 
 BLOCK = 16
-_POS = np.array([0, 2, 1, 3])
 
 
 def tq4_record_bytes(d):
@@ -79,7 +78,7 @@ def vm_offsets(t, gp, d):
     gp = np.asarray(gp)
     r, tt = t // 4, t % 4
     base = (r * g + gp) * 8
-    return 2 * (base + _POS[tt]), 2 * (base + 4 + _POS[tt])
+    return 2 * (base + tt), 2 * (base + 4 + tt)
 
 
 def ks4_offset(t, gp):
