@@ -162,28 +162,19 @@ bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *
 }
 
 // Split-K plan: blocks per work-group S (a multiple of its 8 waves, 16..256).
-// All work-groups of a launch are resident at once in rounds of about two per
-// compute unit (512 on the full chip); with every sequence at the host's
-// maximum length a launch takes ceil(units * nsplit / 512) rounds, each about
-// S + kWgOverhead block-times long (the overhead: block-id fetch, query
-// rotation, the final merge of the waves).  The plan minimizes that; the cap
-// of 256 blocks keeps ragged batches balanced, since short sequences leave
-// their later splits empty.
+// Measured on MI355X across the workloads: about one work-group per compute
+// unit (256) is best (fewer, longer work-groups pay the block-id fetch, query
+// rotation and wave merge fewer times, and leave fewer partials to merge),
+// while more than 256 blocks per work-group unbalances ragged batches (short
+// sequences leave their later splits empty).  So: nsplit = the larger of
+// ceil(256 / units) and ceil(blocks / 256), S = ceil(blocks / nsplit) rounded up
+// to a multiple of 8.
 SplitPlan plan_split(int batch, int hkv, int max_context_len) {
-  const int64_t max_nblk = ((int64_t)max_context_len + 15) / 16;
-  const int64_t units = (int64_t)batch * hkv;
-  const int64_t slots = 512;
-  const int64_t kWgOverhead = 16;
-  int64_t best_s = 16, best_cost = -1;
-  for (int64_t s = 16; s <= 256; s += 8) {
-    const int64_t nsplit = std::max<int64_t>(1, (max_nblk + s - 1) / s);
-    const int64_t rounds = (units * nsplit + slots - 1) / slots;
-    const int64_t cost = rounds * (std::min<int64_t>(s, std::max<int64_t>(max_nblk, 1)) + kWgOverhead);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best_s = s;
-    }
-  }
+  const int64_t max_nblk = std::max<int64_t>(1, ((int64_t)max_context_len + 15) / 16);
+  const int64_t units = std::max<int64_t>(1, (int64_t)batch * hkv);
+  const int64_t want = std::max((256 + units - 1) / units, (max_nblk + 255) / 256);
+  int64_t best_s = (max_nblk + want - 1) / want;
+  best_s = std::min<int64_t>(256, std::max<int64_t>(16, ((best_s + 7) / 8) * 8));
   int64_t s = best_s;
   // override for tests; a wave keeps at most 64 block ids (one per lane), so a
   // work-group of 8 waves takes at most 512 blocks
