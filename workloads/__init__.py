@@ -210,6 +210,29 @@ def make(name_or_cfg):
     return Workload(cfg)
 
 
+def calibration_keys(layers=32, tokens=20, num_kv_heads=8, head_dim=128, seed=1006):
+    """Calibration keys of a stack of layers: bf16 bits [layers, tokens *
+    num_kv_heads, head_dim] (rows token-major, then kv-head).
+
+    About 20 captured vectors per layer stand in for one forward pass's keys
+    ([UQ] "方法怎麼做，白話講").  Layers differ in shape so that their key
+    MSEs differ: per layer, Student-t entries with df ~ U[3, 30], a per-(head,
+    channel) bias N(0, 0.5^2), and 1-4 outlier channels per kv-head scaled by
+    ~U[1, 60] (a strong outlier makes the rotated row nearly two-valued)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((layers, tokens * num_kv_heads, head_dim), dtype=np.uint16)
+    for layer in range(layers):
+        df = g.uniform(3.0, 30.0)
+        mult = np.float32(g.uniform(1.0, 60.0))
+        nout = int(g.integers(1, 5))
+        k = g.standard_t(df, size=(tokens, num_kv_heads, head_dim)).astype(np.float32)
+        k += g.normal(0.0, 0.5, size=(num_kv_heads, head_dim)).astype(np.float32)[None]
+        for h in range(num_kv_heads):
+            k[:, h, g.choice(head_dim, size=nout, replace=False)] *= mult
+        out[layer] = f32_to_bf16_bits(k.reshape(tokens * num_kv_heads, head_dim))
+    return out
+
+
 def small_config(name="small", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(1, 200),
                  fmt=0, seed=7, shared_seqs=0, shared_tokens=0, outliers=2, bias_std=0.5, identity_table=False):
     """A small ragged configuration for parity tests (several tiles, a ragged tail)."""
