@@ -20,7 +20,8 @@ TQ_OUT_BF16 = 1
 EXPORTS = (
     "tq_record_bytes", "tq_pool_bytes", "tq_create_cache", "tq_cache_info", "tq_default_key_table",
     "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_free",
-    "tq_status_string", "tq_last_error",
+    "tq_status_string", "tq_last_error", "tq_calibrate_workspace_bytes", "tq_calibrate_key_tables",
+    "tq_select_layers",
 )
 
 
@@ -57,6 +58,12 @@ def _load():
         "tq_decode_workspace_bytes": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, sz], ctypes.c_int),
         "tq_decode_attention": ([P, P, P, ctypes.c_int32, P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
+        "tq_calibrate_workspace_bytes": ([ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, sz], ctypes.c_int),
+        "tq_calibrate_key_tables": ([P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_float), ctypes.c_int32, P, P, P, P, P,
+                                     ctypes.c_size_t, P], ctypes.c_int),
+        "tq_select_layers": ([ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
+                              ctypes.POINTER(ctypes.c_uint8)], ctypes.c_int),
         "tq_free": ([P], None),
         "tq_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
@@ -157,6 +164,39 @@ def tq_decode_attention(cache, q, out, block_table, context_lens, max_context_le
     _check(LIB.tq_decode_attention(cache, _ptr(q), _ptr(out), out_dtype, _ptr(block_table),
                                    int(block_table.shape[1]), _ptr(context_lens), b, hq, int(max_context_len),
                                    float(softmax_scale), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def tq_calibrate_workspace_bytes(num_layers, rows, head_dim):
+    out = ctypes.c_size_t()
+    _check(LIB.tq_calibrate_workspace_bytes(num_layers, rows, head_dim, ctypes.byref(out)))
+    return out.value
+
+
+def tq_calibrate_key_tables(k, init_table, max_iters, tables_f16, levels=None, mse=None, updates=None,
+                            workspace=None, stream=None):
+    """k: device bf16 [layers, rows, head_dim]; outputs are device tensors
+    (int16 [layers, 16], float64 [layers, 16], float64 [layers, 2], int32
+    [layers]); ``init_table``: 16 floats or None (the default table)."""
+    layers, rows, d = k.shape
+    keep = None
+    tab = None
+    if init_table is not None:
+        keep = (ctypes.c_float * 16)(*[float(x) for x in init_table])
+        tab = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(LIB.tq_calibrate_key_tables(_ptr(k), layers, rows, d, tab, int(max_iters), _ptr(tables_f16),
+                                       _ptr(levels), _ptr(mse), _ptr(updates), _ptr(workspace), wbytes,
+                                       _stream(stream)))
+    del keep
+
+
+def tq_select_layers(mse, percent=10):
+    """Host-side choice of the layers that get a fitted table: list of bools."""
+    n = len(mse)
+    arr = (ctypes.c_double * max(n, 1))(*[float(x) for x in mse])
+    out = (ctypes.c_uint8 * max(n, 1))()
+    _check(LIB.tq_select_layers(arr, n, int(percent), out))
+    return [bool(out[i]) for i in range(n)]
 
 
 def tq_free(cache):

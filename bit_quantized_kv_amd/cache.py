@@ -54,3 +54,19 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+def calibrate_key_tables(k, init_table=None, max_iters=100, stream=None):
+    """Fit one key table per layer on calibration keys ``k`` (device bf16
+    [layers, rows, head_dim]).  Returns device tensors (tables int16 fp16
+    bits [layers, 16], levels float64 [layers, 16], mse float64 [layers, 2],
+    updates int32 [layers]).  Marshalling only: the fit runs in the library."""
+    layers, rows, d = k.shape
+    dev = k.device
+    tables = torch.empty((layers, 16), dtype=torch.int16, device=dev)
+    levels = torch.empty((layers, 16), dtype=torch.float64, device=dev)
+    mse = torch.empty((layers, 2), dtype=torch.float64, device=dev)
+    updates = torch.empty((layers,), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, B.tq_calibrate_workspace_bytes(layers, rows, d)), dtype=torch.uint8, device=dev)
+    B.tq_calibrate_key_tables(k, init_table, max_iters, tables, levels, mse, updates, ws, stream)
+    return tables, levels, mse, updates

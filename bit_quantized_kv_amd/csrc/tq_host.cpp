@@ -267,6 +267,67 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
   return TQ_OK;
 }
 
+tq_status tq_calibrate_workspace_bytes(int32_t num_layers, int64_t rows, int32_t head_dim, size_t *bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_layers < 0 || num_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "num_layers must be in [0, 65535]");
+  if (rows < 0 || rows > (int64_t(1) << 30) / head_dim)
+    return fail(TQ_ERR_INVALID_ARG, "rows must be in [0, 2^30 / head_dim]");
+  *bytes = tq::calibrate_workspace_bytes(num_layers, rows, head_dim);
+  return TQ_OK;
+}
+
+tq_status tq_calibrate_key_tables(const void *k, int32_t num_layers, int64_t rows, int32_t head_dim,
+                                  const float *init_table, int32_t max_iters, uint16_t *tables_f16,
+                                  double *levels, double *mse, int32_t *updates, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  tq_status st = tq_calibrate_workspace_bytes(num_layers, rows, head_dim, &need);
+  if (st != TQ_OK) return st;
+  if (max_iters < 0 || max_iters > 1000000) return fail(TQ_ERR_INVALID_ARG, "max_iters must be in [0, 1e6]");
+  uint16_t init[16];
+  if (init_table) {
+    for (int i = 0; i < 16; ++i) {
+      if (!std::isfinite(init_table[i])) return fail(TQ_ERR_INVALID_ARG, "init table entries must be finite");
+      init[i] = tq::f64_to_f16_rne((double)init_table[i]);
+      if ((init[i] & 0x7c00u) == 0x7c00u) return fail(TQ_ERR_INVALID_ARG, "init table entry overflows fp16");
+    }
+    for (int i = 0; i < 15; ++i)
+      if (!(tq::f16_to_f64(init[i]) < tq::f16_to_f64(init[i + 1])))
+        return fail(TQ_ERR_INVALID_ARG, "init table must be strictly ascending after rounding to fp16");
+  } else {
+    tq_default_key_table(init);
+  }
+  if (num_layers == 0) return TQ_OK;
+  if (!tables_f16) return fail(TQ_ERR_INVALID_ARG, "tables_f16 is NULL");
+  if (rows > 0 && !k) return fail(TQ_ERR_INVALID_ARG, "k is NULL");
+  if (!workspace || workspace_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_calibrate_workspace_bytes (" + std::to_string(need) + ")");
+  const float rsqrt_d = (float)(1.0 / std::sqrt((double)head_dim));
+  hipError_t e = tq::launch_calibrate(head_dim, num_layers, rows, static_cast<const uint16_t *>(k), init, max_iters,
+                                      rsqrt_d, workspace, tables_f16, levels, mse, updates,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "calibrate launch");
+  return TQ_OK;
+}
+
+tq_status tq_select_layers(const double *mse, int32_t num_layers, int32_t percent, uint8_t *chosen) {
+  if (num_layers < 0) return fail(TQ_ERR_INVALID_ARG, "num_layers must be >= 0");
+  if (percent < 0 || percent > 100) return fail(TQ_ERR_INVALID_ARG, "percent must be in [0, 100]");
+  if (num_layers == 0) return TQ_OK;
+  if (!mse || !chosen) return fail(TQ_ERR_INVALID_ARG, "mse or chosen is NULL");
+  for (int i = 0; i < num_layers; ++i)
+    if (std::isnan(mse[i])) return fail(TQ_ERR_INVALID_ARG, "mse holds a NaN");
+  // rank of layer i: layers with a larger MSE, or an equal MSE and a lower index
+  for (int i = 0; i < num_layers; ++i) {
+    int64_t rank = 0;
+    for (int j = 0; j < num_layers; ++j)
+      if (mse[j] > mse[i] || (mse[j] == mse[i] && j < i)) ++rank;
+    chosen[i] = 100 * rank < (int64_t)percent * num_layers ? 1 : 0;
+  }
+  return TQ_OK;
+}
+
 void tq_free(tq_cache *cache) {
   if (!cache) return;
   (void)hipDeviceSynchronize();

@@ -58,6 +58,10 @@ hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
+size_t calibrate_workspace_bytes(int64_t layers, int64_t rows, int d);
+hipError_t launch_calibrate(int d, int layers, int64_t rows, const uint16_t *k, const uint16_t init_f16[16],
+                            int max_iters, float rsqrt_d, void *workspace, uint16_t *tables, double *levels,
+                            double *mse, int32_t *updates, hipStream_t stream);
 
 // Host table construction (pure C++, no HIP calls).
 void lloyd_max_gaussian16(double out[16]);

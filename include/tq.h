@@ -161,6 +161,50 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
                               int32_t batch, int32_t num_q_heads, int32_t max_context_len, float softmax_scale,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Calibrated key tables ([UQ] "方法怎麼做，白話講": the 16-entry key table is
+ * refit on captured activations, about 20 vectors per rotated layer, and used
+ * only on the tenth of the layers with the highest per-element key MSE).
+ *
+ * For each layer l the samples are the unit coordinates u = y / s of the rows
+ * k[l] whose scale s is nonzero, computed exactly as the TQ4/4 key coder does
+ * (fp32, see "key codes" above).  Lloyd's iteration runs in fp64 from the
+ * initial table c: cell(u) = #{ j : u > (c_j + c_{j+1}) / 2 }; c_j = mean of
+ * cell j's samples (an empty cell keeps c_j; a zero mean is +0); it stops when
+ * an update changes no entry or after max_iters updates.
+ *
+ * Per layer it also reports the per-element mean squared key error of the
+ * layer's rows coded with the initial table and with the fitted fp16 table:
+ * codes by the coder's fp32 rule, k_hat = c[code] * s, compared with the exact
+ * rotation H_D k in fp64 (equal to the error in the key's own coordinates,
+ * H_D being orthonormal); all rows * head_dim elements count.
+ *
+ * k: device bf16 [num_layers][rows][head_dim] (rows = calibration tokens x
+ * kv-heads, any order).  head_dim 64 or 128; num_layers 0 .. 65535 (0 is a
+ * no-op); rows 0 .. 2^30 / head_dim.  init_table: host, 16 finite values,
+ * strictly ascending after fp16 rounding (RNE), or NULL for the default table.
+ * max_iters 0 .. 1e6.  Outputs, all device:
+ *   tables_f16  uint16 [num_layers][16]  fitted entries rounded to fp16 (RNE)
+ *                                        (required; pass them to
+ *                                        tq_create_cache, which checks them)
+ *   levels      double [num_layers][16]  fitted entries in fp64, or NULL
+ *   mse         double [num_layers][2]   (initial table, fitted table), or NULL
+ *   updates     int32  [num_layers]      Lloyd updates performed, or NULL
+ * workspace: device buffer of at least tq_calibrate_workspace_bytes.
+ * Asynchronous. */
+tq_status tq_calibrate_workspace_bytes(int32_t num_layers, int64_t rows, int32_t head_dim, size_t *bytes);
+tq_status tq_calibrate_key_tables(const void *k, int32_t num_layers, int64_t rows, int32_t head_dim,
+                                  const float *init_table, int32_t max_iters, uint16_t *tables_f16,
+                                  double *levels, double *mse, int32_t *updates, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* The layers that get a fitted table ([UQ] "方法怎麼做，白話講": the tenth
+ * with the highest MSE).  Host only: mse is a host array [num_layers] (no
+ * NaN); layers are ranked by it, largest first, an equal value ranking the
+ * lower index first; layer i is chosen (chosen[i] = 1, else 0) when its rank
+ * r satisfies 100 * r < percent * num_layers.  percent 0 .. 100. */
+tq_status tq_select_layers(const double *mse, int32_t num_layers, int32_t percent, uint8_t *chosen);
+
 /* Free the handle (NULL-safe).  Synchronises the device first; frees the
  * library-owned pool if the library allocated it. */
 void tq_free(tq_cache *cache);

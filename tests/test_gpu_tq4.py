@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_common import TOL, Case, describe_record_diff, row_rel_err, say
+from gpu_common import TOL, Case, check_case as _check_case, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -23,32 +23,6 @@ def _split_env():
         os.environ.pop(k, None)
         if v is not None:
             os.environ[k] = v
-
-
-def _check_case(case, seqs=None, rows=None, step=0):
-    c = case.cfg
-    seqs = list(range(c.batch)) if seqs is None else seqs
-    ranges = case.write_ranges()
-    case.quantize(ranges)
-    gpu = case.pool_np()
-    writer = case.w.prefix_writer()
-    op = case.oracle_pool([r for r in ranges if r[0] in seqs or r[0] == writer])
-    blocks = case.blocks_of(seqs)
-    mism = np.nonzero(np.any(gpu[blocks] != op.pool[blocks], axis=-1))
-    if mism[0].size:
-        bi, hi = blocks[mism[0][0]], mism[1][0]
-        rows_of = [(b, t) for b in range(c.batch) for t in range(int(case.w.total_lens[b]))
-                   if case.w.block_table[b, t // 16] == bi]
-        msg = describe_record_diff(gpu[bi, hi], op.pool[bi, hi], c.head_dim, c.fmt)
-        raise AssertionError(f"{mism[0].size} records differ; block {bi} head {hi} holds tokens "
-                             f"{rows_of[:3]}..{rows_of[-3:]}: {msg}")
-    out = case.decode(step)
-    rows = rows if rows is not None else [(b, h) for b in seqs for h in range(c.num_q_heads)]
-    ref = case.oracle_decode(op, rows, step)
-    err = row_rel_err(np.array([out[b, h] for b, h in rows]), np.array([ref[b, h] for b, h in rows]))
-    say(f"  {c.name}: {len(blocks)} blocks byte-identical, {len(rows)} rows, max rel err {err:.2e}")
-    assert err <= TOL
-    return out, ref
 
 
 def test_tiny_config():

@@ -87,3 +87,32 @@ def test_key_table_validation_happens_before_any_device_call():
     with pytest.raises(T.TqError) as e:
         T.tq_create_cache(T.TQ_FORMAT_MXFP4, 128, 1, 4, key_table=list(range(16)))
     assert e.value.status == 1
+
+
+def test_layer_choice_matches_oracle():
+    _ensure_built()
+    import bit_quantized_kv_amd as T
+    from oracle import calibrate
+    g = np.random.default_rng(3)
+    for n in (0, 1, 7, 10, 30, 32, 64, 101):
+        mse = g.random(n)
+        if n > 4:
+            mse[1] = mse[3]                      # a tie
+        for pct in (0, 10, 25, 100):
+            assert T.tq_select_layers(mse.tolist(), pct) == calibrate.select_layers(mse, pct).tolist()
+    with pytest.raises(T.TqError):
+        T.tq_select_layers([0.1, float("nan")])
+    with pytest.raises(T.TqError):
+        T.tq_select_layers([0.1], 101)
+
+
+def test_calibration_sizes_and_validation():
+    _ensure_built()
+    import bit_quantized_kv_amd as T
+    n = 32 * 160 * 128
+    assert T.tq_calibrate_workspace_bytes(32, 160, 128) == n * 8 + n * 4 + 32 * 160 * 4
+    assert T.tq_calibrate_workspace_bytes(0, 0, 64) == 0
+    for args, status in (((1, 1, 96), 2), ((-1, 1, 128), 1), ((1, -1, 128), 1), ((1, 1 << 24, 128), 1)):
+        with pytest.raises(T.TqError) as e:
+            T.tq_calibrate_workspace_bytes(*args)
+        assert e.value.status == status
