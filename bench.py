@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="llama8b", choices=["llama8b", "agentic", "longprefix", "fp4"])
+    p.add_argument("--config", default="llama8b", choices=["llama8b", "agentic", "longprefix", "fp4", "calib"],
+                   help="calib: the calibrated key-table fit of a 32-layer stack (its own JSON line)")
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -295,6 +296,90 @@ def timed(torch, stream, launches, enqueue):
     return a.elapsed_time(b) / launches
 
 
+FP64_VALU_PEAK_TFLOPS = 78.6
+
+
+def calib_cpu_baseline(kbits, max_iters, budget_s=10.0):
+    """The oracle's fit of as many layers as fit in about ``budget_s``."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    import workloads
+    from oracle import calibrate, lloyd_max
+    k = workloads.bf16_bits_to_f32(kbits)
+    init = lloyd_max.default_key_table_f16()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        n = 0
+        for layer in range(k.shape[0]):
+            calibrate.fit_table(k[layer], init, max_iters)
+            calibrate.key_mse(k[layer], init)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": n / dt, "unit": "layers/s", "cores": 1, "kind": "oracle",
+            "sample": f"calib: {n} of {k.shape[0]} layers fitted ({max_iters} updates at most) with the "
+                      f"initial-table MSE, {dt:.2f} s (numpy fp64, BLAS limited to 1 thread)"}
+
+
+def bench_calib(args):
+    """Calibrated key-table fit: 32 layers x 20 tokens x 8 kv-heads x D 128,
+    at most 100 Lloyd updates, one launch per stack."""
+    import torch
+
+    import workloads
+    from bit_quantized_kv_amd import calibrate_key_tables
+    torch.cuda.set_device(0)
+    kbits = workloads.calibration_keys()
+    layers, rows, d = kbits.shape
+    max_iters = 100
+    k = torch.from_numpy(np.ascontiguousarray(kbits).view(np.int16)).view(torch.bfloat16).cuda()
+    stream = torch.cuda.current_stream()
+    out = calibrate_key_tables(k, None, max_iters)
+    for _ in range(args.warmup):
+        calibrate_key_tables(k, None, max_iters)
+    torch.cuda.synchronize()
+    updates = out[3].cpu().numpy()
+    ms = timed(torch, stream, args.steps, lambda j: calibrate_key_tables(k, None, max_iters))
+    # algorithmic fp64 work: per sample and Lloyd pass, a 4-compare search of
+    # the 15 midpoints and one add into its cell's sum; passes = updates + 1
+    samples = rows * d
+    ops = float(np.sum(updates + 1)) * samples * 5
+    achieved = ops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "calibrated key-table fit: layers per second",
+        "value": round(layers / (ms * 1e-3), 1),
+        "unit": "layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (seeded; Student-t keys with per-layer outlier channels)",
+        "config": {"workload": f"calib: {layers} layers x {rows} rows (20 tokens x 8 kv-heads) x head_dim {d}, "
+                               f"at most {max_iters} Lloyd updates",
+                   "updates_mean": float(np.mean(updates))},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 4), "peak": FP64_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP64_VALU_PEAK_TFLOPS, 6), "traffic": None,
+                     "kernel": "calibrate", "avg_launch_us": round(ms * 1e3, 2)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = calib_cpu_baseline(kbits, max_iters)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -303,6 +388,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.config == "calib":
+        bench_calib(args)
         return
     import torch
     import workloads
