@@ -18,10 +18,16 @@ formula; the reading is standard softmax attention:
   kernels store it);
 * T_b = 0 gives a zero row; no other mask (the new token is already cached).
 
+Several query tokens per sequence (``multi_token``: chunked prefill, or the
+verification of proposed tokens) take the standard causal reading: the query
+tokens are the last ones of the context, and each sees the keys up to its own
+position.
+
 All arithmetic is fp64.  Pinned by tests/test_oracle_attention.py: weights sum
 to 1, brute-force loops on tiny inputs, T = 1, equal logits, merge of any
 partition equals the single pass, GQA with g = 1 equals per-head MHA, block
-table permutation invariance.
+table permutation invariance; multi_token against decode over each causal
+prefix and against an explicitly masked softmax matrix.
 """
 import numpy as np
 
@@ -63,6 +69,48 @@ def decode(pool, q, block_table, context_lens, scale, rows=None):
             cache[key] = pool.sequence_tokens(block_table[b], int(context_lens[b]), kvh)
         k_rot, v_hat = cache[key]
         out[b, h] = softmax_attention(rotated_query(pool, q[b, h]), k_rot, v_hat, scale)[0]
+    return out
+
+
+def multi_token(pool, q, q_start, block_table, context_lens, scale, rows=None):
+    """Attention of several query tokens per sequence over the cache: chunked
+    prefill of new tokens, or the verification of several proposed tokens.
+
+    Sequence b's query tokens are q[q_start[b] : q_start[b+1]], the last
+    M_b = q_start[b+1] - q_start[b] tokens of its context of T_b tokens
+    (their keys and values are already in the cache).  Query token i of the
+    sequence sits at position T_b - M_b + i and, causally, sees the keys at
+    positions t < T_b - M_b + i + 1.  Each row is ``softmax_attention`` over
+    that prefix; M_b = 1 is ``decode``.
+
+    ``q`` fp32 [total_q, Hq, D] holding bf16 values; ``rows`` a list of
+    (query token index into q, head) or None for all.  Returns fp64
+    [total_q, Hq, D] (rows not requested are NaN)."""
+    q = np.asarray(q, dtype=np.float32)
+    total, hq, d = q.shape
+    if hq % pool.hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    g = hq // pool.hkv
+    q_start = np.asarray(q_start, dtype=np.int64)
+    seq_of = np.zeros(total, dtype=np.int64)
+    for b in range(len(q_start) - 1):
+        seq_of[q_start[b]:q_start[b + 1]] = b
+    out = np.full((total, hq, d), np.nan)
+    want = rows if rows is not None else [(i, h) for i in range(total) for h in range(hq)]
+    cache = {}
+    for qi, h in want:
+        b = int(seq_of[qi])
+        tb = int(context_lens[b])
+        mb = int(q_start[b + 1] - q_start[b])
+        visible = tb - mb + (qi - int(q_start[b])) + 1
+        if visible < 1 or visible > tb:
+            raise ValueError("each query token must lie inside its sequence's context")
+        kvh = h // g
+        key = (b, kvh)
+        if key not in cache:
+            cache[key] = pool.sequence_tokens(block_table[b], tb, kvh)
+        k_rot, v_hat = cache[key]
+        out[qi, h] = softmax_attention(rotated_query(pool, q[qi, h]), k_rot[:visible], v_hat[:visible], scale)[0]
     return out
 
 

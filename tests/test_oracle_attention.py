@@ -138,3 +138,54 @@ def test_context_zero_gives_zero_row():
     q = workloads.bf16_bits_to_f32(w.query_bits())
     out = attention.decode(pool, q, w.block_table, np.zeros(1, np.int32), cfg.scale)
     assert np.all(out == 0)
+
+
+def _multi_token_case(seed, lens_m, d=64, hq=8, hkv=2):
+    cfg = workloads.small_config(batch=len(lens_m), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                 ctx_range=(20, 90), seed=seed)
+    w, pool = _filled_pool(cfg)
+    m = np.array([min(x, int(t)) for x, t in zip(lens_m, w.total_lens)])
+    q_start = np.concatenate([[0], np.cumsum(m)])
+    rng = np.random.default_rng(seed)
+    q = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(
+        rng.standard_normal((int(q_start[-1]), hq, d)).astype(np.float32)))
+    return cfg, w, pool, m, q_start, q
+
+
+def test_multi_token_rows_equal_decode_over_each_causal_prefix():
+    cfg, w, pool, m, q_start, q = _multi_token_case(29, [1, 5, 17])
+    T = w.total_lens
+    out = attention.multi_token(pool, q, q_start, w.block_table, T, cfg.scale)
+    for b in range(cfg.batch):
+        for i in range(int(m[b])):
+            qi = int(q_start[b]) + i
+            ctx = np.array([int(T[b]) - int(m[b]) + i + 1])
+            ref = attention.decode(pool, q[qi][None], w.block_table[b:b + 1], ctx, cfg.scale)
+            assert np.array_equal(out[qi], ref[0])
+
+
+def test_multi_token_against_masked_softmax_matrix():
+    from scipy.special import softmax
+    cfg, w, pool, m, q_start, q = _multi_token_case(30, [9], hq=2, hkv=1)
+    T, M = int(w.total_lens[0]), int(m[0])
+    out = attention.multi_token(pool, q, q_start, w.block_table, w.total_lens, cfg.scale)
+    k, v = pool.sequence_tokens(w.block_table[0], T, 0)
+    for h in range(2):
+        qr = wht.wht_f64(q[:, h].astype(np.float64))                  # [M, D]
+        s = cfg.scale * qr @ k.T                                        # [M, T]
+        pos = np.arange(T)[None, :]
+        s = np.where(pos > (T - M + np.arange(M))[:, None], -np.inf, s)
+        ref = softmax(s, axis=1) @ v
+        assert np.allclose(out[:, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_multi_token_prefill_from_the_first_token():
+    # M = T: the first query token sees only token 0, so its output is v_hat[0]
+    cfg, w, pool, m, q_start, q = _multi_token_case(31, [10 ** 6, 3])
+    T0 = int(w.total_lens[0])
+    assert int(m[0]) == T0
+    out = attention.multi_token(pool, q, q_start, w.block_table, w.total_lens, cfg.scale,
+                                rows=[(0, h) for h in range(cfg.num_q_heads)])
+    for h in range(cfg.num_q_heads):
+        _, v = pool.sequence_tokens(w.block_table[0], T0, h // 4)
+        assert np.array_equal(out[0, h], v[0])
