@@ -21,7 +21,7 @@ EXPORTS = (
     "tq_record_bytes", "tq_pool_bytes", "tq_create_cache", "tq_cache_info", "tq_default_key_table",
     "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_free",
     "tq_status_string", "tq_last_error", "tq_calibrate_workspace_bytes", "tq_calibrate_key_tables",
-    "tq_select_layers",
+    "tq_select_layers", "tq_multitoken_workspace_bytes", "tq_multitoken_attention",
 )
 
 
@@ -64,6 +64,11 @@ def _load():
                                      ctypes.c_size_t, P], ctypes.c_int),
         "tq_select_layers": ([ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
                               ctypes.POINTER(ctypes.c_uint8)], ctypes.c_int),
+        "tq_multitoken_workspace_bytes": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, sz], ctypes.c_int),
+        "tq_multitoken_attention": ([P, P, P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32,
+                                     P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P,
+                                     ctypes.c_size_t, P], ctypes.c_int),
         "tq_free": ([P], None),
         "tq_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
@@ -164,6 +169,26 @@ def tq_decode_attention(cache, q, out, block_table, context_lens, max_context_le
     _check(LIB.tq_decode_attention(cache, _ptr(q), _ptr(out), out_dtype, _ptr(block_table),
                                    int(block_table.shape[1]), _ptr(context_lens), b, hq, int(max_context_len),
                                    float(softmax_scale), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def tq_multitoken_workspace_bytes(cache, batch, num_q_heads, num_tokens, max_query_len, max_context_len):
+    out = ctypes.c_size_t()
+    _check(LIB.tq_multitoken_workspace_bytes(cache, batch, num_q_heads, num_tokens, max_query_len,
+                                             max_context_len, ctypes.byref(out)))
+    return out.value
+
+
+def tq_multitoken_attention(cache, q, out, q_start, max_query_len, block_table, context_lens, max_context_len,
+                            softmax_scale, workspace=None, stream=None):
+    """q: device bf16 [num_tokens, Hq, D]; q_start: device int32 [batch + 1]."""
+    n, hq, _ = q.shape
+    batch = int(q_start.numel()) - 1
+    out_dtype = TQ_OUT_BF16 if str(out.dtype) == "torch.bfloat16" else TQ_OUT_F32
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(LIB.tq_multitoken_attention(cache, _ptr(q), _ptr(out), out_dtype, _ptr(q_start), n, int(max_query_len),
+                                       _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch, hq,
+                                       int(max_context_len), float(softmax_scale), _ptr(workspace), wbytes,
+                                       _stream(stream)))
 
 
 def tq_calibrate_workspace_bytes(num_layers, rows, head_dim):

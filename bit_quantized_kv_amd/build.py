@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["tq_host.cpp", "tq_tables.cpp", "tq4_quantize.hip", "tq4_decode.hip", "mxfp4.hip", "calibrate.hip"]
+SOURCES = ["tq_host.cpp", "tq_tables.cpp", "tq4_quantize.hip", "tq4_decode.hip", "mxfp4.hip", "calibrate.hip", "tq4_multitoken.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

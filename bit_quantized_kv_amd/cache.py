@@ -13,6 +13,7 @@ class Cache:
         self.handle = B.tq_create_cache(fmt, head_dim, num_kv_heads, num_blocks, key_table, self.pool)
         self.record_bytes = B.tq_record_bytes(fmt, head_dim, num_kv_heads, num_blocks)
         self._ws = None
+        self._mt_ws = None
 
     def quantize_append(self, k, v, slot_mapping, stream=None):
         assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int32
@@ -54,6 +55,26 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+    def multitoken(self, q, q_start, max_query_len, block_table, context_lens, max_context_len, softmax_scale,
+                   out=None, out_dtype=None, stream=None):
+        """Causal attention of q [num_tokens, Hq, D] (sequence b's tokens are
+        q[q_start[b]:q_start[b+1]], the last ones of its context)."""
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == self.head_dim
+        assert q_start.dtype == torch.int32 and context_lens.dtype == torch.int32
+        n, hq, d = q.shape
+        batch = int(q_start.numel()) - 1
+        if out is None:
+            out = torch.empty((n, hq, d), dtype=out_dtype or torch.float32, device=q.device)
+        need = B.tq_multitoken_workspace_bytes(self.handle, batch, hq, n, max_query_len, max_context_len)
+        ws = None
+        if need:
+            if self._mt_ws is None or self._mt_ws.numel() < need:
+                self._mt_ws = torch.empty(need, dtype=torch.uint8, device=self.pool.device)
+            ws = self._mt_ws
+        B.tq_multitoken_attention(self.handle, q, out, q_start, max_query_len, block_table, context_lens,
+                                  max_context_len, softmax_scale, ws, stream)
+        return out
 
 
 def calibrate_key_tables(k, init_table=None, max_iters=100, stream=None):

@@ -211,4 +211,102 @@ __device__ __forceinline__ void write_zero_rows(const DecodeArgs &a, int b, int 
   }
 }
 
+// Combine the split partials of one output row (one work-group of 256 threads).
+// Thread (cq, sl) takes channels 4*cq .. 4*cq+3 of splits sl, sl + SL, ...,
+// in chunks of 8 splits whose loads (maxima, sums, accumulators) are all
+// issued before any is used; the first chunk's loads go out before the
+// largest partial maximum M is found (every wave on its own: lane-strided
+// loads and a wave reduction, no barrier).  The weights are 2^(m_s - M); the
+// SL slices are added in LDS.
+struct MergeView {
+  const float *part_ml;   // [rows][nsplit][2]: (max, sum) in log2 units
+  const float *part_acc;  // [rows][nsplit][d]
+  void *out;              // fp32 / bf16 [rows][d]
+  int32_t nsplit;         // partial slots per row
+  int32_t out_bf16;
+};
+
+// ns: splits that hold this row's tokens (0: the row attends to nothing and is
+// written as zeros).
+template <int D>
+__device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int ns) {
+  constexpr int CQ = D / 4;          // channel quads
+  constexpr int SL = 256 / CQ;       // split lanes
+  constexpr int CH = 8;              // splits per thread per chunk
+  __shared__ float s_l[SL][CQ];
+  __shared__ float4 s_acc[SL][CQ];
+  const int tid = threadIdx.x, lane = tid & 63, cq = tid % CQ, sl = tid / CQ;
+  if (ns == 0) {  // no tokens: a zero row (no partial exists to read)
+    for (int c = tid; c < D; c += 256) {
+      if (v.out_bf16) reinterpret_cast<uint16_t *>(v.out)[row * D + c] = 0;
+      else reinterpret_cast<float *>(v.out)[row * D + c] = 0.f;
+    }
+    return;
+  }
+  const float2 *ml = reinterpret_cast<const float2 *>(v.part_ml + row * v.nsplit * 2);
+  const float *pa = v.part_acc + row * v.nsplit * D;
+  // first chunk of this thread's partials, loaded before the maximum is known
+  float2 c_ml[CH];
+  float4 c_v[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int sp = min(sl + j * SL, ns - 1);  // clamped: valid split of this row
+    c_ml[j] = ml[sp];
+    c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
+  }
+  float M = kNegInf;
+  for (int sp = lane; sp < ns; sp += 64) M = __builtin_fmaxf(M, ml[sp].x);
+  M = __builtin_fmaxf(M, xor1(M));
+  M = __builtin_fmaxf(M, xor2(M));
+  M = __builtin_fmaxf(M, xor4(M));
+  M = __builtin_fmaxf(M, xor8(M));
+  M = __builtin_fmaxf(M, xor16(M));
+  M = __builtin_fmaxf(M, xor32(M));
+  float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int base = 0; base < ns; base += CH * SL) {
+    if (base) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int sp = min(base + sl + j * SL, ns - 1);
+        c_ml[j] = ml[sp];
+        c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool in = base + sl + j * SL < ns;
+      const float f = (!in || c_ml[j].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(c_ml[j].x - M);
+      den += f * c_ml[j].y;
+      num.x += f * c_v[j].x;
+      num.y += f * c_v[j].y;
+      num.z += f * c_v[j].z;
+      num.w += f * c_v[j].w;
+    }
+  }
+  s_l[sl][cq] = den;
+  s_acc[sl][cq] = num;
+  __syncthreads();
+  if (sl == 0) {
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      L += s_l[i][cq];
+      o.x += s_acc[i][cq].x;
+      o.y += s_acc[i][cq].y;
+      o.z += s_acc[i][cq].z;
+      o.w += s_acc[i][cq].w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t oi = row * D + 4 * cq + c;
+      if (v.out_bf16) reinterpret_cast<uint16_t *>(v.out)[oi] = f32_to_bf16(ov[c]);
+      else reinterpret_cast<float *>(v.out)[oi] = ov[c];
+    }
+  }
+}
+
 }  // namespace tq

@@ -287,96 +287,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 }
 
 // One work-group per (sequence, query head): combine the split partials.
-// Thread (cq, sl) takes channels 4*cq .. 4*cq+3 of splits sl, sl + SL, ...,
-// in chunks of 8 splits whose loads (maxima, sums, accumulators) are all
-// issued before any is used; the first chunk's loads go out before the
-// largest partial maximum M is found (every wave on its own: lane-strided
-// loads and a wave reduction, no barrier).  The weights are 2^(m_s - M); the
-// SL slices are added in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int CQ = D / 4;          // channel quads
-  constexpr int SL = 256 / CQ;       // split lanes
-  constexpr int CH = 8;              // splits per thread per chunk
-  __shared__ float s_l[SL][CQ];
-  __shared__ float4 s_acc[SL][CQ];
   const int64_t row = blockIdx.x;
   const int b = (int)(row / a.hq);
   const int T = a.ctx[b];
   const int nblk = (T + 15) >> 4;
   const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
-  const int tid = threadIdx.x, lane = tid & 63, cq = tid % CQ, sl = tid / CQ;
-  if (ns == 0) {  // no tokens: a zero row (no partial exists to read)
-    for (int c = tid; c < D; c += 256) {
-      if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[row * D + c] = 0;
-      else reinterpret_cast<float *>(a.out)[row * D + c] = 0.f;
-    }
-    return;
-  }
-  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml + row * a.nsplit * 2);
-  const float *pa = a.part_acc + row * a.nsplit * D;
-  // first chunk of this thread's partials, loaded before the maximum is known
-  float2 c_ml[CH];
-  float4 c_v[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int sp = min(sl + j * SL, ns - 1);  // clamped: valid split of this row
-    c_ml[j] = ml[sp];
-    c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
-  }
-  float M = kNegInf;
-  for (int sp = lane; sp < ns; sp += 64) M = __builtin_fmaxf(M, ml[sp].x);
-  M = __builtin_fmaxf(M, xor1(M));
-  M = __builtin_fmaxf(M, xor2(M));
-  M = __builtin_fmaxf(M, xor4(M));
-  M = __builtin_fmaxf(M, xor8(M));
-  M = __builtin_fmaxf(M, xor16(M));
-  M = __builtin_fmaxf(M, xor32(M));
-  float den = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = 0; base < ns; base += CH * SL) {
-    if (base) {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int sp = min(base + sl + j * SL, ns - 1);
-        c_ml[j] = ml[sp];
-        c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const bool in = base + sl + j * SL < ns;
-      const float f = (!in || c_ml[j].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(c_ml[j].x - M);
-      den += f * c_ml[j].y;
-      num.x += f * c_v[j].x;
-      num.y += f * c_v[j].y;
-      num.z += f * c_v[j].z;
-      num.w += f * c_v[j].w;
-    }
-  }
-  s_l[sl][cq] = den;
-  s_acc[sl][cq] = num;
-  __syncthreads();
-  if (sl == 0) {
-    float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      L += s_l[i][cq];
-      o.x += s_acc[i][cq].x;
-      o.y += s_acc[i][cq].y;
-      o.z += s_acc[i][cq].z;
-      o.w += s_acc[i][cq].w;
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t oi = row * D + 4 * cq + c;
-      if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(ov[c]);
-      else reinterpret_cast<float *>(a.out)[oi] = ov[c];
-    }
-  }
+  merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.nsplit, a.out_bf16}, row, ns);
 }
 
 template <int D>

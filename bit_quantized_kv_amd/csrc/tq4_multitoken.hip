@@ -1,0 +1,417 @@
+// TQ4/4 attention of several query tokens per sequence over the 4-bit paged
+// cache: chunked prefill of new tokens, or the verification of proposed tokens.
+// The query tokens are the last M_b of sequence b's context of T_b tokens and
+// see the keys causally: query token i sees positions t < T_b - M_b + i + 1.
+//
+// Rows are (query token, query head) pairs of one kv-head, token-major.  A
+// work-group of 8 waves takes 128 rows (16 per wave, one MFMA column each) of
+// one (sequence, kv-head) and one split of the key blocks.  The key blocks are
+// dequantized once per work-group and shared through LDS:
+//   * stage k: wave w loads block 8k + w of the split (a ring of four blocks
+//     of 128-bit loads in flight per wave), dequantizes it into the
+//     work-group's LDS stage buffer (keys: the fp16 table entries, in the QK
+//     MFMA's A-operand order; values: code * scale + min in fp16, in the PV
+//     MFMA's A-operand order; key scales), and after one barrier every wave
+//     runs its 16 rows against the 8 blocks of the stage.  Two stage buffers
+//     alternate, so one barrier per stage suffices;
+//   * per block and wave: logits = K_hat (16 tokens x D) times the rotated
+//     query rows (D x 16 rows) with v_mfma_f32_16x16x32_f16, the query split
+//     into fp16 high and low parts (two MFMAs into one accumulator); the key
+//     scale; the causal mask; online softmax in log2 units with lazy rescale;
+//     out^T (channels x rows) += V_hat^T P with v_mfma_f32_16x16x16f16, P
+//     again as fp16 high and low parts.
+// With one split a wave writes its rows; otherwise split partials (max, sum,
+// acc) go to the workspace and a merge kernel combines them per row.
+#include "decode_common.h"
+
+namespace tq {
+namespace {
+
+constexpr int kMtWaves = 8;
+constexpr int kMtRows = 16 * kMtWaves;  // rows per work-group
+// A running maximum that starts finite, so that a column whose tokens are all
+// masked so far gets p = 2^(-inf - m) = 0 rather than 2^(-inf + inf).
+constexpr float kMtFloor = -1.0e30f;
+
+template <int D>
+struct MtTile;
+template <>
+struct MtTile<128> {
+  typedef uint4 T;
+};
+template <>
+struct MtTile<64> {
+  typedef uint2 T;
+};
+
+__device__ __forceinline__ uint32_t mt_word(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t mt_word(const uint2 &v, int i) { return i == 0 ? v.x : v.y; }
+
+template <bool HI_WORD>
+__device__ __forceinline__ half2v mt_codes_f16(uint32_t bytes) {
+  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
+}
+
+template <int D>
+struct MtBlk {
+  typename MtTile<D>::T kq;
+  uint2 ks;
+  typename MtTile<D>::T vq;
+  uint32_t vmw;
+};
+
+template <int D>
+__device__ __forceinline__ void mt_load_blk(MtBlk<D> &o, const uint8_t *rec, int lane) {
+  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
+  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
+  const int r = lane >> 4, c = lane & 15;
+  o.kq = *reinterpret_cast<const typename MtTile<D>::T *>(rec + lane * Q);
+  o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
+  o.vq = *reinterpret_cast<const typename MtTile<D>::T *>(rec + OFF_VC + lane * (4 * G));
+  o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
+}
+
+// LDS image of one dequantized block (per lane: its MFMA A operands).
+template <int D>
+struct MtSlot {
+  uint4 k[D / 32][64];   // QK A operand of k-step s: 8 fp16 table entries
+  uint2 v[D / 16][64];   // PV A operand of tile t: 4 fp16 values
+  uint2 ks[4];           // fp16 key scales of tokens 4r .. 4r+3
+};
+
+struct MtTask {
+  int b, kvh, rt, sp;
+};
+
+__device__ __forceinline__ MtTask mt_task(const MultiTokenArgs &a) {
+  // row tiles fastest, then splits, sequences, kv-heads; each XCD gets a
+  // contiguous range, so the work-groups that read the same blocks share an L2
+  const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+  MtTask t;
+  t.rt = (int)(wg % (uint32_t)a.row_tiles);
+  uint32_t rest = wg / (uint32_t)a.row_tiles;
+  t.sp = (int)(rest % (uint32_t)a.nsplit);
+  rest /= (uint32_t)a.nsplit;
+  t.b = (int)(rest % (uint32_t)a.batch);
+  t.kvh = (int)(rest / (uint32_t)a.batch);
+  return t;
+}
+
+// Producer: dequantize this wave's loaded block into its LDS slot.
+template <int D>
+__device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtSlot<D> &slot, const uint32_t *s_lut,
+                                           uint32_t *vm_slot, int lane, bool tail, uint32_t vm_keep) {
+  constexpr int G = D / 32, KS = D / 32;
+  uint32_t vmw = bk.vmw;
+  if (tail) {
+    __asm__ volatile("");
+    vmw &= vm_keep;
+  }
+  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = vmw;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint32_t w = mt_word(bk.kq, s);
+    uint4 e;
+    e.x = s_lut[w & 0xFF];
+    e.y = s_lut[(w >> 8) & 0xFF];
+    e.z = s_lut[(w >> 16) & 0xFF];
+    e.w = s_lut[w >> 24];
+    slot.k[s][lane] = e;
+  }
+  if ((lane & 15) == 0) slot.ks[lane >> 4] = bk.ks;
+  const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
+#pragma unroll
+  for (int gp = 0; gp < G; ++gp) {
+    const uint32_t w = mt_word(bk.vq, gp);
+    const uint4 vm = vm_row[gp];
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const half2v sc01 = as_h2(vm.x), sc23 = as_h2(vm.y);
+    const half2v mn01 = as_h2(vm.z), mn23 = as_h2(vm.w);
+    const half2v e01 = __builtin_elementwise_fma(mt_codes_f16<false>(lo), sc01, mn01);
+    const half2v e23 = __builtin_elementwise_fma(mt_codes_f16<true>(lo), sc23, mn23);
+    const half2v o01 = __builtin_elementwise_fma(mt_codes_f16<false>(hi), sc01, mn01);
+    const half2v o23 = __builtin_elementwise_fma(mt_codes_f16<true>(hi), sc23, mn23);
+    slot.v[2 * gp][lane] = make_uint2(as_u(e01), as_u(e23));
+    slot.v[2 * gp + 1][lane] = make_uint2(as_u(o01), as_u(o23));
+  }
+}
+
+// Consumer: this wave's 16 rows against one block.  lim: this lane's
+// column's visible-key count; masked: the block reaches past some column's
+// limit.
+template <int D>
+__device__ __forceinline__ void mt_consume(const MtSlot<D> &slot, const half8v (&bq_hi)[D / 32],
+                                           const half8v (&bq_lo)[D / 32], WaveState<D / 16> &st, int lane,
+                                           int tok0, int lim, bool masked) {
+  constexpr int KS = D / 32, NT = D / 16;
+  const int r = lane >> 4;
+  float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const half8v ka = __builtin_bit_cast(half8v, slot.k[s][lane]);
+    qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_hi[s], qk, 0, 0, 0);
+    qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_lo[s], qk, 0, 0, 0);
+  }
+  const uint2 ksw = slot.ks[r];
+  const half2v s01 = as_h2(ksw.x), s23 = as_h2(ksw.y);
+  float x[4];
+  x[0] = __builtin_fmaf(qk[0], (float)s01[0], 0.0f);
+  x[1] = __builtin_fmaf(qk[1], (float)s01[1], 0.0f);
+  x[2] = __builtin_fmaf(qk[2], (float)s23[0], 0.0f);
+  x[3] = __builtin_fmaf(qk[3], (float)s23[1], 0.0f);
+  if (masked) {
+    __asm__ volatile("");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (tok0 + 4 * r + i >= lim) x[i] = kNegInf;
+  }
+  float p[4];
+  softmax_block<NT>(x, st, p);
+  half4v ph, pl;
+  {
+    const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
+    const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
+    const half2v l01 = __builtin_bit_cast(
+        half2v, __builtin_amdgcn_cvt_pkrtz(p[0] - (float)h01[0], p[1] - (float)h01[1]));
+    const half2v l23 = __builtin_bit_cast(
+        half2v, __builtin_amdgcn_cvt_pkrtz(p[2] - (float)h23[0], p[3] - (float)h23[1]));
+    ph = (half4v){h01[0], h01[1], h23[0], h23[1]};
+    pl = (half4v){l01[0], l01[1], l23[0], l23[1]};
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const half4v va = __builtin_bit_cast(half4v, slot.v[t][lane]);
+    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, st.acc[t], 0, 0, 0);
+    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, st.acc[t], 0, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiTokenArgs a) {
+  constexpr int G = D / 32, KS = D / 32, NT = D / 16;
+  constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
+  constexpr int NW = kMtWaves;
+
+  __shared__ uint32_t s_lut[256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_vm[NW][64];
+  // two stage buffers of NW block slots; the query staging area overlays them
+  __shared__ __attribute__((aligned(16))) MtSlot<D> s_stage[2][NW];
+  static_assert(sizeof(s_stage) >= (size_t)NW * 32 * D * sizeof(_Float16), "query staging overlay");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const MtTask task = mt_task(a);
+  const int b = task.b, kvh = task.kvh, sp = task.sp;
+
+  const int q0 = a.q_start[b];
+  const int M = a.q_start[b + 1] - q0;
+  const int T = a.ctx[b];
+  const int R = M * a.g;
+  const int row0 = task.rt * kMtRows;
+  if (row0 >= R) return;
+  const int rlast = min(R, row0 + kMtRows) - 1;
+  const int lmax_wg = T - M + rlast / a.g + 1;  // keys the work-group's last row sees
+  const int nblk = (lmax_wg + 15) >> 4;
+  const int blk0 = sp * a.split_blocks;
+  if (blk0 >= nblk) return;
+  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  const int nb = blk1 - blk0;
+
+  // this lane's column (row) and its visible-key count; rows past R see none
+  const int n = lane & 15, r = lane >> 4;
+  const int myrow = row0 + 16 * wv + n;
+  const bool row_ok = myrow < R;
+  const int lim = row_ok ? T - M + myrow / a.g + 1 : 0;
+  // the wave's smallest and largest visible-key counts (its first and last rows)
+  const int w_first = row0 + 16 * wv;
+  const int w_last = min(R, w_first + 16) - 1;
+  const int lmin_w = w_first < R ? T - M + w_first / a.g + 1 : 0;
+  const int lmax_w = w_first < R ? T - M + w_last / a.g + 1 : 0;
+
+  // ---- block ids and the first loads ---------------------------------------------
+  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
+  const int my_id_raw = btab[min(blk0 + wv + lane * NW, a.max_blocks - 1)];
+  const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
+  __asm__ volatile("" ::: "memory");
+  const uint8_t *base = a.pool + (int64_t)kvh * REC;
+  const int64_t stride = (int64_t)a.hkv * REC;
+  const int mine = nb > wv ? (nb - wv + NW - 1) / NW : 0;
+  const int my_id = settled(my_id_raw);
+  // block k of this wave (k >= mine: its last block again, an L2 hit; a wave
+  // with no block of this split refills from block 0's record, never used)
+  auto rec_of = [&](int k) {
+    const int kk = k < mine ? k : mine - 1;
+    return kk < 0 ? base : base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
+  };
+  const int seq_nblk = (T + 15) >> 4;
+  const int tail_blk = (T & 15) ? seq_nblk - 1 : seq_nblk;
+  uint32_t tail_keep;
+  {
+    const int rr = 4 * (lane >> 4), w = lane & 3;
+    const int ta = (T & 15) - (rr + 2 * (w & 1)), tb = ta - 1;
+    tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
+  }
+  MtBlk<D> b0, b1, b2, b3;
+  if (mine > 0) {
+    mt_load_blk<D>(b0, rec_of(0), lane);
+    __asm__ volatile("" ::: "memory");
+    mt_load_blk<D>(b1, rec_of(1), lane);
+    __asm__ volatile("" ::: "memory");
+    mt_load_blk<D>(b2, rec_of(2), lane);
+    __asm__ volatile("" ::: "memory");
+    mt_load_blk<D>(b3, rec_of(3), lane);
+  }
+
+  // ---- the wave's 16 rotated, scaled query rows: fp16 high and low parts -------
+  if (tid < 256) s_lut[tid] = lut_w;
+  _Float16(*s_q)[2][16][D] = reinterpret_cast<_Float16(*)[2][16][D]>(&s_stage[0][0]);
+  uint32_t qw[16];  // all 16 query loads in flight before the first rotation
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int row = min(w_first + j, R - 1);
+    const int64_t qrow = (int64_t)(q0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
+    qw[j] = load_query_word<D>(a.q + qrow * D, lane);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float x0 = 0.f, x1 = 0.f;
+    if (w_first + j < R) rotate_row<D>(qw[j], lane, x0, x1);
+#pragma unroll
+    for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
+      const float xs = (e ? x1 : x0) * a.qscale;
+      const _Float16 hi = (_Float16)xs;
+      const _Float16 lo = (_Float16)(xs - (float)hi);
+      const int c = rotated_channel<D>(lane, e);
+      s_q[wv][0][j][c] = hi;
+      s_q[wv][1][j][c] = lo;
+    }
+  }
+  __syncthreads();
+  half8v bq_hi[KS], bq_lo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bq_hi[s] = *reinterpret_cast<const half8v *>(&s_q[wv][0][n][r * (D / 4) + 8 * s]);
+    bq_lo[s] = *reinterpret_cast<const half8v *>(&s_q[wv][1][n][r * (D / 4) + 8 * s]);
+  }
+  __syncthreads();  // the staging area becomes stage buffer 0
+
+  WaveState<NT> st;
+  st.m = kMtFloor;
+  st.l = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) st.acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  uint32_t *vm_slot = s_vm[wv];
+  const int nstage = (nb + NW - 1) / NW;
+  auto stage = [&](MtBlk<D> &buf, int k) {
+    MtSlot<D>(&cur)[NW] = s_stage[k & 1];
+    if (k < mine) {
+      const int blk = blk0 + wv + k * NW;
+      mt_produce<D>(buf, cur[wv], s_lut, vm_slot, lane, blk == tail_blk, tail_keep);
+    }
+    mt_load_blk<D>(buf, rec_of(k + 4), lane);
+    __syncthreads();
+    const int first = blk0 + k * NW;
+    const int cnt = min(NW, blk1 - first);
+#pragma unroll 1
+    for (int j = 0; j < cnt; ++j) {
+      const int tok0 = (first + j) * 16;
+      if (tok0 >= lmax_w) break;  // this block and the later ones are masked for every row
+      mt_consume<D>(cur[j], bq_hi, bq_lo, st, lane, tok0, lim, tok0 + 16 > lmin_w);
+    }
+  };
+#pragma unroll 1
+  for (int k = 0; k < nstage; k += 4) {
+    stage(b0, k);
+    if (k + 1 < nstage) stage(b1, k + 1);
+    if (k + 2 < nstage) stage(b2, k + 2);
+    if (k + 3 < nstage) stage(b3, k + 3);
+  }
+
+  // ---- this wave's rows: output, or the split partial ------------------------------
+  float l = st.l;
+  l += xor16(l);
+  l += xor32(l);
+  if (!row_ok) return;
+  const int64_t orow = (int64_t)(q0 + myrow / a.g) * a.hq + kvh * a.g + myrow % a.g;
+  if (a.nsplit == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = st.acc[2 * gp][i] * inv;
+        o[2 * i + 1] = st.acc[2 * gp + 1][i] * inv;
+      }
+      const int64_t oi = orow * D + 32 * gp + 8 * r;
+      if (a.out_bf16) {
+        uint4 w;
+        w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+        w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + oi) = w;
+      } else {
+        float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + oi);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    }
+  } else {
+    const int64_t pi = orow * a.nsplit + sp;
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      float4 *dst = reinterpret_cast<float4 *>(a.part_acc + pi * D + 32 * gp + 8 * r);
+      dst[0] = make_float4(st.acc[2 * gp][0], st.acc[2 * gp + 1][0], st.acc[2 * gp][1], st.acc[2 * gp + 1][1]);
+      dst[1] = make_float4(st.acc[2 * gp][2], st.acc[2 * gp + 1][2], st.acc[2 * gp][3], st.acc[2 * gp + 1][3]);
+    }
+    if (r == 0) {
+      // a row none of whose keys fall in this split keeps the floor maximum
+      // and a zero sum; the merge gives it weight 0
+      a.part_ml[pi * 2] = st.m;
+      a.part_ml[pi * 2 + 1] = l;
+    }
+  }
+}
+
+// One work-group per (sequence, query token, query head) slot: combine the
+// split partials of the row, if the slot holds a query token.
+template <int D>
+__global__ __launch_bounds__(256) void multitoken_merge_kernel(MultiTokenArgs a) {
+  const int64_t slot = blockIdx.x;
+  const int h = (int)(slot % a.hq);
+  const int64_t rest = slot / a.hq;
+  const int i = (int)(rest % a.max_query_len);
+  const int b = (int)(rest / a.max_query_len);
+  const int q0 = a.q_start[b];
+  const int M = a.q_start[b + 1] - q0;
+  if (i >= M) return;
+  const int T = a.ctx[b];
+  const int lim = T - M + i + 1;
+  const int nblk = (lim + 15) >> 4;
+  const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
+  const int64_t row = (int64_t)(q0 + i) * a.hq + h;
+  merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.nsplit, a.out_bf16}, row, ns);
+}
+
+template <int D>
+hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
+  const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
+  hipLaunchKernelGGL(tq4_multitoken_kernel<D>, dim3((unsigned)wgs), dim3(kMtWaves * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const int64_t rows = (int64_t)a.batch * a.max_query_len * a.hq;
+  hipLaunchKernelGGL(multitoken_merge_kernel<D>, dim3((unsigned)rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tq4_multitoken(int d, const MultiTokenArgs &a, hipStream_t s) {
+  return d == 128 ? launch_mt<128>(a, s) : launch_mt<64>(a, s);
+}
+
+}  // namespace tq

@@ -1,5 +1,6 @@
 // C-ABI of the 4-bit KV-cache library: argument checks, handle and table
 // management, launch planning.  Every compute step runs in the HIP kernels.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -264,6 +265,104 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
     e = tq::launch_decode_merge(d, a, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
+  return TQ_OK;
+}
+
+namespace {
+
+struct MtPlan {
+  tq::SplitPlan split;
+  int row_tiles;
+};
+
+tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads, int64_t num_tokens,
+                          int32_t max_query_len, int32_t max_context_len, MtPlan *p) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (cache->desc.format != TQ_FORMAT_TQ4)
+    return fail(TQ_ERR_UNSUPPORTED, "multi-token attention is built for the TQ4/4 format");
+  const int hkv = cache->desc.num_kv_heads;
+  if (batch < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0)
+    return fail(TQ_ERR_INVALID_ARG, "batch, num_tokens, max_query_len and max_context_len must be >= 0");
+  if (num_q_heads < hkv || num_q_heads % hkv)
+    return fail(TQ_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (max_query_len > max_context_len)
+    return fail(TQ_ERR_INVALID_ARG, "max_query_len must be <= max_context_len");
+  if (num_tokens > (int64_t)batch * max_query_len)
+    return fail(TQ_ERR_INVALID_ARG, "num_tokens must be <= batch * max_query_len");
+  const int64_t g = num_q_heads / hkv;
+  const int64_t row_tiles = ((int64_t)max_query_len * g + 127) / 128;
+  const tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
+                                                     max_context_len);
+  if ((int64_t)batch * hkv * row_tiles * sp.nsplit >= (int64_t(1) << 31) ||
+      (int64_t)batch * max_query_len * num_q_heads >= (int64_t(1) << 31))
+    return fail(TQ_ERR_INVALID_ARG, "launch grid too large");
+  p->split = sp;
+  p->row_tiles = (int)row_tiles;
+  return TQ_OK;
+}
+
+}  // namespace
+
+tq_status tq_multitoken_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
+                                        int64_t num_tokens, int32_t max_query_len, int32_t max_context_len,
+                                        size_t *bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  MtPlan p;
+  tq_status st = multitoken_plan(cache, batch, num_q_heads, num_tokens, max_query_len, max_context_len, &p);
+  if (st != TQ_OK) return st;
+  const size_t rows = (size_t)num_tokens * num_q_heads * p.split.nsplit;
+  *bytes = p.split.nsplit > 1 ? ((rows * 2 * 4 + 255) / 256) * 256 + rows * (size_t)cache->desc.head_dim * 4 : 0;
+  return TQ_OK;
+}
+
+tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                                  const int32_t *q_start, int64_t num_tokens, int32_t max_query_len,
+                                  const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                                  int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                  float softmax_scale, void *workspace, size_t workspace_bytes, void *stream) {
+  MtPlan p;
+  tq_status st = multitoken_plan(cache, batch, num_q_heads, num_tokens, max_query_len, max_context_len, &p);
+  if (st != TQ_OK) return st;
+  if (batch == 0 || num_tokens == 0 || max_query_len == 0) return TQ_OK;
+  if (!q || !out || !q_start || !block_table || !context_lens)
+    return fail(TQ_ERR_INVALID_ARG, "q, out, q_start, block_table and context_lens must be non-NULL");
+  if (out_dtype != TQ_OUT_F32 && out_dtype != TQ_OUT_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
+  if (max_blocks < (max_context_len + 15) / 16 || max_blocks < 1)
+    return fail(TQ_ERR_INVALID_ARG, "max_blocks must cover max_context_len");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(TQ_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  size_t need = 0;
+  tq_multitoken_workspace_bytes(cache, batch, num_q_heads, num_tokens, max_query_len, max_context_len, &need);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(TQ_ERR_WORKSPACE,
+                "workspace smaller than tq_multitoken_workspace_bytes (" + std::to_string(need) + ")");
+  const int d = cache->desc.head_dim;
+  tq::MultiTokenArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.out = out;
+  a.q_start = q_start;
+  a.block_table = block_table;
+  a.ctx = context_lens;
+  a.pool = cache->pool;
+  a.tables = cache->tables;
+  if (p.split.nsplit > 1) {
+    a.part_ml = static_cast<float *>(workspace);
+    a.part_acc = a.part_ml + (((size_t)num_tokens * num_q_heads * p.split.nsplit * 2 + 63) / 64) * 64;
+  }
+  const double log2e = 1.4426950408889634074;
+  a.qscale = (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)));
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = cache->desc.num_kv_heads;
+  a.g = num_q_heads / a.hkv;
+  a.max_query_len = max_query_len;
+  a.row_tiles = p.row_tiles;
+  a.split_blocks = p.split.split_blocks;
+  a.nsplit = p.split.nsplit;
+  a.out_bf16 = out_dtype == TQ_OUT_BF16;
+  hipError_t e = tq::launch_tq4_multitoken(d, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "multi-token attention launch");
   return TQ_OK;
 }
 

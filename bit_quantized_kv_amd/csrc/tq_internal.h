@@ -52,12 +52,31 @@ struct DecodeArgs {
   int32_t out_bf16;
 };
 
+struct MultiTokenArgs {
+  const uint16_t *q;             // bf16 [num_tokens][hq][d]
+  void *out;                     // fp32 / bf16 [num_tokens][hq][d]
+  const int32_t *q_start;        // [batch + 1]: query tokens of sequence b are q_start[b] .. q_start[b+1]-1
+  const int32_t *block_table;    // [batch][max_blocks]
+  const int32_t *ctx;            // [batch]: context lengths, query tokens included
+  const uint8_t *pool;
+  const DeviceTables *tables;
+  float *part_ml;                // [num_tokens][hq][nsplit][2]
+  float *part_acc;               // [num_tokens][hq][nsplit][d]
+  float qscale;                  // softmax_scale * log2(e) * fp32(1/sqrt(d))
+  int32_t max_blocks, batch, hq, hkv, g;
+  int32_t max_query_len;         // bound on q_start[b+1] - q_start[b]
+  int32_t row_tiles;             // 128-row tiles per (sequence, kv-head)
+  int32_t split_blocks, nsplit;
+  int32_t out_bf16;
+};
+
 // Launchers (defined next to their kernels).
 hipError_t launch_tq4_quantize(int d, const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_tq4_multitoken(int d, const MultiTokenArgs &a, hipStream_t s);
 size_t calibrate_workspace_bytes(int64_t layers, int64_t rows, int d);
 hipError_t launch_calibrate(int d, int layers, int64_t rows, const uint16_t *k, const uint16_t init_f16[16],
                             int max_iters, float rsqrt_d, void *workspace, uint16_t *tables, double *levels,
@@ -80,5 +99,9 @@ struct SplitPlan {
   int split_blocks, nsplit;
 };
 SplitPlan plan_split(int batch, int hkv, int max_context_len);
+// Multi-token attention: `units` work-groups per split (sequences x kv-heads x
+// row tiles); splits only when the units alone leave compute units idle, at
+// most 512 blocks per work-group.
+SplitPlan plan_split_multitoken(int64_t units, int max_context_len);
 
 }  // namespace tq

@@ -162,6 +162,36 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Multi-token attention over the compressed cache (TQ4/4): chunked prefill of
+ * new tokens, or the verification of several proposed tokens.  The time to
+ * first token that the pages report ([TQ-AMD] section 1; [UQ] "它實際證明了
+ * 什麼") comes from prefilling over the cache; the operation is the causal
+ * reading of attention over the cached context:
+ *   out[q_start[b] + i, h] = sum_{t < T_b - M_b + i + 1} softmax_t(scale *
+ *                            <q~, k_hat_t>) v_hat_t,   i < M_b,
+ * with M_b = q_start[b+1] - q_start[b] query tokens of sequence b, the last
+ * M_b tokens of its context of T_b = context_lens[b] tokens (their keys and
+ * values already appended), q~ = H_D q, kv-head h / g as in decode.
+ * q: device bf16 [num_tokens][num_q_heads][head_dim]; out: device fp32 or
+ * bf16 (out_dtype) of the same shape; q_start: device int32 [batch + 1],
+ * nondecreasing, q_start[0] = 0, q_start[batch] = num_tokens, each M_b in
+ * [1, max_query_len] (or 0: the sequence has no query token) and M_b <= T_b
+ * <= max_context_len, ceil(T_b / 16) <= max_blocks (all trusted, not checked
+ * on the device).  num_q_heads a multiple of num_kv_heads (any ratio).
+ * Host-checked: max_query_len <= max_context_len, num_tokens <= batch *
+ * max_query_len.  workspace: device buffer of at least
+ * tq_multitoken_workspace_bytes (NULL allowed when that is 0).  MX-FP4 caches
+ * return TQ_ERR_UNSUPPORTED.  Asynchronous. */
+tq_status tq_multitoken_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
+                                        int64_t num_tokens, int32_t max_query_len, int32_t max_context_len,
+                                        size_t *bytes);
+tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                                  const int32_t *q_start, int64_t num_tokens, int32_t max_query_len,
+                                  const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                                  int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                  float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Calibrated key tables ([UQ] "方法怎麼做，白話講": the 16-entry key table is
  * refit on captured activations, about 20 vectors per rotated layer, and used
  * only on the tenth of the layers with the highest per-element key MSE).

@@ -1,0 +1,137 @@
+"""GPU parity of multi-token attention over the TQ4/4 cache (chunked prefill,
+verification) against the CPU oracle, through the C ABI: max over rows of
+||o - o_ref||_inf / ||o_ref||_inf within 2e-3, rows computed by the oracle's
+exact fp64 causal attention over the same (byte-identical) cache."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import TOL, Case, row_rel_err, say, to_dev_bf16, to_dev_i32
+from oracle import attention
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _split_env():
+    saved = os.environ.pop("TQ_SPLIT_BLOCKS", None)
+    yield
+    os.environ.pop("TQ_SPLIT_BLOCKS", None)
+    if saved is not None:
+        os.environ["TQ_SPLIT_BLOCKS"] = saved
+
+
+def _run(case, m, rows=None, seqs=None):
+    """Quantize the workload, run multi-token attention for ``m`` query tokens
+    per sequence, compare ``rows`` (or all) with the oracle."""
+    c = case.cfg
+    w = case.w
+    ranges = case.write_ranges(w.total_lens)
+    case.quantize(ranges)
+    gpu_pool = case.pool_np()
+    seqs = list(range(c.batch)) if seqs is None else seqs
+    writer = w.prefix_writer()
+    op = case.oracle_pool([r for r in ranges if r[0] in seqs or r[0] == writer])
+    blocks = case.blocks_of(seqs)
+    assert np.array_equal(gpu_pool[blocks], op.pool[blocks]), "cache records differ from the oracle's"
+    qbits, q_start = w.multi_queries(m)
+    mq = int(np.max(np.diff(q_start))) if c.batch else 0
+    ctx = w.total_lens.astype(np.int32)
+    out = case.cache.multitoken(to_dev_bf16(qbits), to_dev_i32(q_start), max(mq, 1), case.table_dev,
+                                to_dev_i32(ctx), int(ctx.max()), c.scale)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    if rows is None:
+        rows = [(i, h) for b in seqs for i in range(int(q_start[b]), int(q_start[b + 1]))
+                for h in range(c.num_q_heads)]
+    q = workloads.bf16_bits_to_f32(qbits)
+    ref = attention.multi_token(op, q, q_start, w.block_table, ctx, c.scale, rows=rows)
+    o = np.array([out[i, h] for i, h in rows])
+    r = np.array([ref[i, h] for i, h in rows])
+    err = row_rel_err(o, r)
+    say(f"  {c.name}: {len(rows)} rows, max rel err {err:.2e}")
+    assert err <= TOL
+    return out, q_start
+
+
+@pytest.mark.parametrize("d,g,hkv,seed,mmax,split", [
+    (128, 4, 2, 201, 40, None), (128, 8, 1, 202, 20, 8), (128, 1, 2, 203, 150, None), (128, 2, 3, 204, 70, 12),
+    (64, 4, 2, 205, 40, None), (64, 8, 1, 206, 33, 4), (64, 1, 1, 207, 130, 16),
+])
+def test_small_ragged(d, g, hkv, seed, mmax, split):
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=5, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                 ctx_range=(1, 700), seed=seed)
+    rng = np.random.default_rng(seed)
+    m = rng.integers(1, mmax + 1, size=5)
+    say(f"case: multi-token small ragged d={d} g={g} hkv={hkv} seed={seed} m={m.tolist()} split={split}")
+    _run(Case(cfg), m)
+
+
+def test_prefill_from_the_first_token_and_empty_sequences():
+    cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(30, 300),
+                                 seed=208)
+    case = Case(cfg)
+    m = np.array([10 ** 6, 0, 17, 10 ** 6])     # whole contexts, none, a chunk
+    say("case: multi-token prefill of whole contexts with an empty sequence")
+    _run(case, m)
+
+
+def _bf16_of(case, m, split):
+    """bf16 output of the same call: must be the RNE rounding of its fp32 output."""
+    w, c = case.w, case.cfg
+    qbits, q_start = w.multi_queries(m)
+    ctx = w.total_lens.astype(np.int32)
+    args = (to_dev_bf16(qbits), to_dev_i32(q_start), int(np.max(np.diff(q_start))), case.table_dev, to_dev_i32(ctx),
+            int(ctx.max()), c.scale)
+    o32 = case.cache.multitoken(*args, out_dtype=torch.float32)
+    o16 = case.cache.multitoken(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = workloads.f32_to_bf16_bits(o32.cpu().numpy())
+    got = o16.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want), f"split {split}: bf16 output is not the rounded fp32 output"
+
+
+def test_bf16_output_and_split_invariance():
+    cfg = workloads.small_config(batch=3, num_q_heads=16, num_kv_heads=2, head_dim=128, ctx_range=(900, 2000),
+                                 seed=209)
+    say("case: multi-token split invariance and bf16 output (one split, then 8-block splits)")
+    case = Case(cfg)
+    a, _ = _run(case, 24)
+    _bf16_of(case, 24, None)
+    os.environ["TQ_SPLIT_BLOCKS"] = "8"
+    b, _ = _run(Case(cfg), 24)
+    _bf16_of(case, 24, 8)
+    assert np.max(np.abs(a - b)) <= 2e-3 * np.max(np.abs(a))
+
+
+def test_one_query_token_matches_decode():
+    cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(50, 900),
+                                 seed=210)
+    case = Case(cfg)
+    out, q_start = _run(case, 1)
+    qbits, _ = case.w.multi_queries(1)
+    ctx = case.w.total_lens.astype(np.int32)
+    dec = case.cache.decode(to_dev_bf16(qbits), case.table_dev, to_dev_i32(ctx), int(ctx.max()), cfg.scale)
+    torch.cuda.synchronize()
+    assert row_rel_err(out, dec.cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["verify", "prefill"])
+def test_full_size_sampled(name):
+    cfg = workloads.MT_CONFIGS[name]
+    m = workloads.MT_QUERY_TOKENS[name]
+    case = Case(cfg)
+    rng = np.random.default_rng(211)
+    seqs = sorted(rng.choice(cfg.batch, size=min(2, cfg.batch), replace=False).tolist())
+    qbits, q_start = case.w.multi_queries(m)
+    rows = []
+    for b in seqs:
+        toks = rng.choice(np.arange(int(q_start[b]), int(q_start[b + 1])), size=min(4, m), replace=False)
+        rows += [(int(i), int(h)) for i in toks for h in rng.choice(cfg.num_q_heads, size=3, replace=False)]
+    say(f"case: multi-token full size {name}: sampled sequences {seqs}, {len(rows)} rows")
+    _run(case, m, rows=rows, seqs=seqs)

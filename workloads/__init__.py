@@ -69,6 +69,21 @@ CONFIGS = {
 }
 
 
+# Multi-token attention workloads (chunked prefill, verification).  The query
+# tokens are the last ``query_tokens`` of each sequence's context; their keys
+# and values are part of the sequence's cached tokens.
+MT_CONFIGS = {
+    # verification of 8 proposed tokens per sequence on the agentic shape
+    "verify": Config("verify", batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                     ctx_range=(4096, 25600), shared_seqs=16, shared_tokens=24576,
+                     outliers=4, bias_std=0.5, seed=1007),
+    # a 512-token prefill chunk per sequence on top of a 25088-token cached prefix
+    "prefill": Config("prefill", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, context=25600,
+                      outliers=4, bias_std=0.5, seed=1008),
+}
+MT_QUERY_TOKENS = {"verify": 8, "prefill": 512}
+
+
 def f32_to_bf16_bits(x):
     """fp32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -196,6 +211,20 @@ class Workload:
 
     def query_bits(self, step=0):
         return self.q_bits[step]
+
+    def multi_queries(self, m):
+        """Query tokens of a multi-token attention step: ``m`` (an int or one
+        count per sequence, each clipped to the sequence's length) query tokens
+        per sequence, N(0,1) in bf16.  Returns (q bits [sum m, Hq, D],
+        q_start [batch + 1]).  Drawn from a stream of their own, so the other
+        draws are unchanged."""
+        c = self.cfg
+        m = np.broadcast_to(np.asarray(m, dtype=np.int64), (c.batch,))
+        m = np.minimum(m, self.total_lens)
+        q_start = np.concatenate([[0], np.cumsum(m)]).astype(np.int32)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([c.seed, 0x6D74])))
+        qf = g.standard_normal(size=(int(q_start[-1]), c.num_q_heads, c.head_dim), dtype=np.float32)
+        return f32_to_bf16_bits(qf), q_start
 
     def context_lens_at(self, step=0):
         """Context lengths seen by decode step ``step`` (its token appended)."""
