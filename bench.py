@@ -43,8 +43,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="llama8b", choices=["llama8b", "agentic", "longprefix", "fp4", "calib"],
-                   help="calib: the calibrated key-table fit of a 32-layer stack (its own JSON line)")
+    p.add_argument("--config", default="llama8b",
+                   choices=["llama8b", "agentic", "longprefix", "fp4", "calib", "verify", "prefill"],
+                   help="calib: the calibrated key-table fit of a 32-layer stack; verify / prefill: multi-token "
+                        "attention over the cache (each its own JSON line)")
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -380,6 +382,200 @@ def bench_calib(args):
     print(json.dumps(res))
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+class MtBench:
+    """Multi-token attention: each sequence's last M tokens are the query
+    tokens.  A step appends their keys and values (quantize) and runs the
+    causal multi-token attention over the whole cached context."""
+
+    def __init__(self, name, copies):
+        import torch
+
+        import workloads
+        from bit_quantized_kv_amd import Cache
+        self.torch = torch
+        cfg = workloads.MT_CONFIGS[name]
+        self.m = workloads.MT_QUERY_TOKENS[name]
+        self.w = w = workloads.make(cfg)
+        self.cfg = c = w.cfg
+        dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        qbits, q_start = w.multi_queries(self.m)
+        self.q = dev(qbits)
+        self.q_start_np = q_start
+        self.q_start = i32(q_start)
+        self.ctx_np = w.total_lens.astype(np.int32)
+        self.ctx = i32(self.ctx_np)
+        self.max_q = int(np.max(np.diff(q_start)))
+        self.max_ctx = int(self.ctx_np.max())
+        self.table = i32(w.block_table)
+        rec = Cache(c.fmt, c.head_dim, c.num_kv_heads, 1).record_bytes
+        self.row_bytes = rec // 16
+        pool_bytes = rec * c.num_kv_heads * w.num_blocks
+        self.copies = copies if copies > 0 else max(3, -(-2 * 256 * 2 ** 20 // pool_bytes))
+        self.caches = [Cache(c.fmt, c.head_dim, c.num_kv_heads, w.num_blocks) for _ in range(self.copies)]
+        # the whole context quantized once into every copy (set-up, untimed)
+        plan = w.write_plan(w.total_lens)
+        ks, vs, ss, ka, va, sa = [], [], [], [], [], []
+        for b, t0, t1 in plan:
+            k, v = w.sequence_kv(b)
+            ks.append(k[t0:t1])
+            vs.append(v[t0:t1])
+            ss.append(w.slots(b, t0, t1))
+        for b in range(c.batch):
+            k, v = w.sequence_kv(b)
+            t1 = int(w.total_lens[b])
+            t0 = t1 - int(q_start[b + 1] - q_start[b])
+            ka.append(k[t0:t1])
+            va.append(v[t0:t1])
+            sa.append(w.slots(b, t0, t1))
+        k0, v0, s0 = dev(np.concatenate(ks)), dev(np.concatenate(vs)), i32(np.concatenate(ss))
+        for cache in self.caches:
+            cache.quantize_append(k0, v0, s0)
+        del k0, v0, s0
+        self.ka, self.va, self.sa = dev(np.concatenate(ka)), dev(np.concatenate(va)), i32(np.concatenate(sa))
+        self.n_new = int(self.sa.numel())
+        self.out = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
+        for cache in self.caches:
+            self.attend(cache)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+
+    def attend(self, cache):
+        c = self.cfg
+        cache.multitoken(self.q, self.q_start, self.max_q, self.table, self.ctx, self.max_ctx, c.scale, out=self.out)
+
+    def append(self, i):
+        self.caches[i % self.copies].quantize_append(self.ka, self.va, self.sa)
+
+    def attention(self, i):
+        self.attend(self.caches[i % self.copies])
+
+    def step(self, i):
+        self.append(i)
+        self.attention(i)
+
+    def work(self):
+        """Algorithmic bytes and flops of one attention call: every cached
+        token-head read once (shared blocks once), q read, out written; 4 D
+        flops (QK and PV multiply-adds) per visible key of every row."""
+        c, w = self.cfg, self.w
+        ids = {}
+        for b in range(c.batch):
+            n = -(-int(self.ctx_np[b]) // 16)
+            for j, bid in enumerate(w.block_table[b, :n].tolist()):
+                ids[bid] = max(ids.get(bid, 0), min(16, int(self.ctx_np[b]) - 16 * j))
+        kv = sum(ids.values()) * c.num_kv_heads * self.row_bytes
+        nq = int(self.q.shape[0])
+        byts = kv + nq * c.num_q_heads * c.head_dim * (2 + 4) + (c.batch + 1) * 4 * 2
+        flops = 0
+        for b in range(c.batch):
+            mb = int(self.q_start_np[b + 1] - self.q_start_np[b])
+            t = int(self.ctx_np[b])
+            vis = sum(t - mb + i + 1 for i in range(mb))
+            flops += 4 * c.head_dim * vis * c.num_q_heads
+        return byts, flops, kv
+
+
+def bench_multitoken(args):
+    import torch
+    torch.cuda.set_device(0)
+    mb = MtBench(args.config, args.copies)
+    c = mb.cfg
+    for i in range(args.warmup + mb.copies):
+        mb.step(i)
+    torch.cuda.synchronize()
+    base = args.warmup + mb.copies
+    step_ms = timed(torch, mb.stream, args.steps, lambda j: mb.step(base + j))
+    a_ms = timed(torch, mb.stream, args.steps, lambda j: mb.attention(base + j))
+    q_ms = timed(torch, mb.stream, args.steps, lambda j: mb.append(base + j))
+    byts, flops, kv = mb.work()
+    t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        ach = flops / (a_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4)}
+    else:
+        ach = byts / (a_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    roof.update({"traffic": None, "kernel": "multitoken", "bytes_per_launch": byts, "flops_per_launch": flops,
+                 "avg_launch_us": round(a_ms * 1e3, 2)})
+    nq = int(mb.q.shape[0])
+    res = {
+        "metric": "multi-token attention over the 4-bit cache: query tokens per second",
+        "value": round(nq / (a_ms * 1e-3), 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes; f16 MFMA, f32 softmax",
+        "data": "synthetic (seeded; shapes of the pages' agentic workloads)",
+        "config": {"workload": f"{c.name}: batch {c.batch}, {mb.m} query tokens per sequence, "
+                               f"{c.num_q_heads}/{c.num_kv_heads} heads, head_dim {c.head_dim}, "
+                               f"context up to {mb.max_ctx}",
+                   "pool_copies": mb.copies},
+        "attention_us": round(a_ms * 1e3, 2),
+        "append_us": round(q_ms * 1e3, 2),
+        "effective_kv_GBps": round(kv / (a_ms * 1e-3) / 1e9, 1),
+        "roofline": roof,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = mt_cpu_baseline(mb)
+    print(json.dumps(res))
+
+
+def mt_cpu_baseline(mb, budget_s=10.0):
+    """The oracle on a bounded sample: sequence 0's cache (one kv-head) built
+    by the oracle, then its query rows of that kv-head until ~budget_s."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    import workloads
+    from oracle import attention, paged
+    c, w = mb.cfg, mb.w
+    g = c.num_q_heads // c.num_kv_heads
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        T = int(mb.ctx_np[0])
+        k, v = w.sequence_kv(0)
+        pool = paged.PagedPool(c.fmt, w.num_blocks, 1, c.head_dim)
+        pool.append(workloads.bf16_bits_to_f32(k[:T, :1]), workloads.bf16_bits_to_f32(v[:T, :1]), w.slots(0, 0, T))
+        q = workloads.bf16_bits_to_f32(mb.q.view(torch_int16()).cpu().numpy().view(np.uint16))
+        t0 = time.perf_counter()
+        n = 0
+        m0 = int(mb.q_start_np[1])
+        for i in range(m0):
+            attention.multi_token(pool, q[:, :g], mb.q_start_np, w.block_table, mb.ctx_np, c.scale,
+                                  rows=[(i, h) for h in range(g)])
+            n += g
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": n / g / dt, "unit": "query tokens/s (one kv-head's g heads each)", "cores": 1, "kind": "oracle",
+            "sample": f"{c.name}: sequence 0, kv-head 0: {n} query rows ({n // g} tokens x {g} heads) over a "
+                      f"{T}-token context, {dt:.2f} s (numpy fp64, BLAS limited to 1 thread)"}
+
+
+def torch_int16():
+    import torch
+    return torch.int16
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -391,6 +587,9 @@ def main():
         return
     if args.config == "calib":
         bench_calib(args)
+        return
+    if args.config in ("verify", "prefill"):
+        bench_multitoken(args)
         return
     import torch
     import workloads

@@ -28,7 +28,6 @@ namespace tq {
 namespace {
 
 constexpr int kMtWaves = 8;
-constexpr int kMtRows = 16 * kMtWaves;  // rows per work-group
 // A running maximum that starts finite, so that a column whose tokens are all
 // masked so far gets p = 2^(-inf - m) = 0 rather than 2^(-inf + inf).
 constexpr float kMtFloor = -1.0e30f;
@@ -138,70 +137,127 @@ __device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtSlot<D> &slot, 
   }
 }
 
-// Consumer: this wave's 16 rows against one block.  lim: this lane's
-// column's visible-key count; masked: the block reaches past some column's
+// Online softmax over a pair of blocks (8 logits per lane: tokens 4r..4r+3 of
+// each block, column n = lane % 16), with the lazy rescale of softmax_block.
+template <int NT>
+__device__ __forceinline__ void mt_softmax8(const float (&x)[8], WaveState<NT> &st, float (&p)[8]) {
+  float lm = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3])),
+                             __builtin_fmaxf(__builtin_fmaxf(x[4], x[5]), __builtin_fmaxf(x[6], x[7])));
+  if (__builtin_amdgcn_ballot_w64(lm > st.m + kLazyRescale) != 0) {
+    float bm = __builtin_fmaxf(lm, xor16(lm));
+    bm = __builtin_fmaxf(bm, xor32(bm));
+    const bool raise = bm > st.m + kLazyRescale;
+    const float m_new = raise ? bm : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.acc[t] *= alpha;
+    st.m = m_new;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
+// Consumer: this wave's 16 rows against a pair of blocks A, B (B = A with
+// has_b false: a lone last block, whose second half gets p = 0).  The PV
+// product contracts over the 32 tokens of the pair on v_mfma_f32_16x16x32_f16:
+// operand index 8r + j is token 4r + j of block A for j < 4, token 4r + j - 4
+// of block B otherwise, which is how both the QK accumulators (B operand) and
+// the LDS value slots (A operand) already hold them.  lim: this lane's
+// column's visible-key count; masked: the pair reaches past some column's
 // limit.
 template <int D>
-__device__ __forceinline__ void mt_consume(const MtSlot<D> &slot, const half8v (&bq_hi)[D / 32],
-                                           const half8v (&bq_lo)[D / 32], WaveState<D / 16> &st, int lane,
-                                           int tok0, int lim, bool masked) {
+__device__ __forceinline__ void mt_consume_pair(const MtSlot<D> &sa, const MtSlot<D> &sb, bool has_b,
+                                                const half8v (&bq_hi)[D / 32], const half8v (&bq_lo)[D / 32],
+                                                WaveState<D / 16> &st, int lane, int tok0, int lim,
+                                                bool masked) {
   constexpr int KS = D / 32, NT = D / 16;
   const int r = lane >> 4;
-  float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
+  float4v qa = (float4v){0.f, 0.f, 0.f, 0.f}, qb = qa;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const half8v ka = __builtin_bit_cast(half8v, slot.k[s][lane]);
-    qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_hi[s], qk, 0, 0, 0);
-    qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_lo[s], qk, 0, 0, 0);
+    const half8v ka = __builtin_bit_cast(half8v, sa.k[s][lane]);
+    qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_hi[s], qa, 0, 0, 0);
+    qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_lo[s], qa, 0, 0, 0);
   }
-  const uint2 ksw = slot.ks[r];
-  const half2v s01 = as_h2(ksw.x), s23 = as_h2(ksw.y);
-  float x[4];
-  x[0] = __builtin_fmaf(qk[0], (float)s01[0], 0.0f);
-  x[1] = __builtin_fmaf(qk[1], (float)s01[1], 0.0f);
-  x[2] = __builtin_fmaf(qk[2], (float)s23[0], 0.0f);
-  x[3] = __builtin_fmaf(qk[3], (float)s23[1], 0.0f);
+  if (has_b) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const half8v kb = __builtin_bit_cast(half8v, sb.k[s][lane]);
+      qb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq_hi[s], qb, 0, 0, 0);
+      qb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq_lo[s], qb, 0, 0, 0);
+    }
+  }
+  const uint2 ka_s = sa.ks[r], kb_s = sb.ks[r];
+  const half2v a01 = as_h2(ka_s.x), a23 = as_h2(ka_s.y), b01 = as_h2(kb_s.x), b23 = as_h2(kb_s.y);
+  float x[8];
+  x[0] = __builtin_fmaf(qa[0], (float)a01[0], 0.0f);
+  x[1] = __builtin_fmaf(qa[1], (float)a01[1], 0.0f);
+  x[2] = __builtin_fmaf(qa[2], (float)a23[0], 0.0f);
+  x[3] = __builtin_fmaf(qa[3], (float)a23[1], 0.0f);
+  x[4] = __builtin_fmaf(qb[0], (float)b01[0], 0.0f);
+  x[5] = __builtin_fmaf(qb[1], (float)b01[1], 0.0f);
+  x[6] = __builtin_fmaf(qb[2], (float)b23[0], 0.0f);
+  x[7] = __builtin_fmaf(qb[3], (float)b23[1], 0.0f);
+  if (!has_b) {
+    __asm__ volatile("");
+#pragma unroll
+    for (int i = 4; i < 8; ++i) x[i] = kNegInf;
+  }
   if (masked) {
     __asm__ volatile("");
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (tok0 + 4 * r + i >= lim) x[i] = kNegInf;
+    for (int i = 0; i < 8; ++i)
+      if (tok0 + (i >> 2) * 16 + 4 * r + (i & 3) >= lim) x[i] = kNegInf;
   }
-  float p[4];
-  softmax_block<NT>(x, st, p);
-  half4v ph, pl;
-  {
-    const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
-    const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
-    const half2v l01 = __builtin_bit_cast(
-        half2v, __builtin_amdgcn_cvt_pkrtz(p[0] - (float)h01[0], p[1] - (float)h01[1]));
-    const half2v l23 = __builtin_bit_cast(
-        half2v, __builtin_amdgcn_cvt_pkrtz(p[2] - (float)h23[0], p[3] - (float)h23[1]));
-    ph = (half4v){h01[0], h01[1], h23[0], h23[1]};
-    pl = (half4v){l01[0], l01[1], l23[0], l23[1]};
+  float p[8];
+  mt_softmax8<NT>(x, st, p);
+  half8v ph, pl;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
+    const half2v l = __builtin_bit_cast(
+        half2v, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)h[0], p[i + 1] - (float)h[1]));
+    ph[i] = h[0];
+    ph[i + 1] = h[1];
+    pl[i] = l[0];
+    pl[i + 1] = l[1];
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const half4v va = __builtin_bit_cast(half4v, slot.v[t][lane]);
-    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, st.acc[t], 0, 0, 0);
-    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, st.acc[t], 0, 0, 0);
+    const uint2 va = sa.v[t][lane], vb = sb.v[t][lane];
+    const half8v v8 = __builtin_bit_cast(half8v, make_uint4(va.x, va.y, vb.x, vb.y));
+    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, ph, st.acc[t], 0, 0, 0);
+    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, pl, st.acc[t], 0, 0, 0);
   }
 }
 
-template <int D>
+// NRG row groups of 16 rows (one per wave of a row group) times NBG = 8 / NRG
+// block groups: wave w takes rows 16 * (w % NRG) .. +15 of the work-group's
+// tile and, of the four block pairs of every stage, those with index
+// w / NRG (mod NBG); the block groups of a row group are merged in LDS at the
+// end.  Every wave loads and dequantizes one block per stage.
+template <int D, int NRG>
 __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiTokenArgs a) {
   constexpr int G = D / 32, KS = D / 32, NT = D / 16;
   constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
   constexpr int NW = kMtWaves;
+  constexpr int NBG = NW / NRG;
+  constexpr int RW = 16 * NRG;  // rows per work-group
 
   __shared__ uint32_t s_lut[256];
   __shared__ __attribute__((aligned(16))) uint32_t s_vm[NW][64];
-  // two stage buffers of NW block slots; the query staging area overlays them
+  // two stage buffers of NW block slots; the query staging area and the final
+  // block-group merge overlay them
   __shared__ __attribute__((aligned(16))) MtSlot<D> s_stage[2][NW];
-  static_assert(sizeof(s_stage) >= (size_t)NW * 32 * D * sizeof(_Float16), "query staging overlay");
+  __shared__ float s_fm[NW][16], s_fl[NW][16];
+  static_assert(sizeof(s_stage) >= (size_t)NRG * 32 * D * sizeof(_Float16), "query staging overlay");
+  static_assert(sizeof(s_stage) >= (size_t)NW * NT * 64 * sizeof(float4v), "merge overlay");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wv % NRG, bg = wv / NRG;
   const MtTask task = mt_task(a);
   const int b = task.b, kvh = task.kvh, sp = task.sp;
 
@@ -209,9 +265,9 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   const int M = a.q_start[b + 1] - q0;
   const int T = a.ctx[b];
   const int R = M * a.g;
-  const int row0 = task.rt * kMtRows;
+  const int row0 = task.rt * RW;
   if (row0 >= R) return;
-  const int rlast = min(R, row0 + kMtRows) - 1;
+  const int rlast = min(R, row0 + RW) - 1;
   const int lmax_wg = T - M + rlast / a.g + 1;  // keys the work-group's last row sees
   const int nblk = (lmax_wg + 15) >> 4;
   const int blk0 = sp * a.split_blocks;
@@ -221,11 +277,11 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
 
   // this lane's column (row) and its visible-key count; rows past R see none
   const int n = lane & 15, r = lane >> 4;
-  const int myrow = row0 + 16 * wv + n;
+  const int w_first = row0 + 16 * rg;
+  const int myrow = w_first + n;
   const bool row_ok = myrow < R;
   const int lim = row_ok ? T - M + myrow / a.g + 1 : 0;
   // the wave's smallest and largest visible-key counts (its first and last rows)
-  const int w_first = row0 + 16 * wv;
   const int w_last = min(R, w_first + 16) - 1;
   const int lmin_w = w_first < R ? T - M + w_first / a.g + 1 : 0;
   const int lmax_w = w_first < R ? T - M + w_last / a.g + 1 : 0;
@@ -264,36 +320,38 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     mt_load_blk<D>(b3, rec_of(3), lane);
   }
 
-  // ---- the wave's 16 rotated, scaled query rows: fp16 high and low parts -------
+  // ---- the row group's 16 rotated, scaled query rows: fp16 high and low parts ----
   if (tid < 256) s_lut[tid] = lut_w;
   _Float16(*s_q)[2][16][D] = reinterpret_cast<_Float16(*)[2][16][D]>(&s_stage[0][0]);
-  uint32_t qw[16];  // all 16 query loads in flight before the first rotation
+  if (bg == 0) {
+    uint32_t qw[16];  // all 16 query loads in flight before the first rotation
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int row = min(w_first + j, R - 1);
-    const int64_t qrow = (int64_t)(q0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
-    qw[j] = load_query_word<D>(a.q + qrow * D, lane);
-  }
+    for (int j = 0; j < 16; ++j) {
+      const int row = min(w_first + j, R - 1);
+      const int64_t qrow = (int64_t)(q0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
+      qw[j] = load_query_word<D>(a.q + qrow * D, lane);
+    }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float x0 = 0.f, x1 = 0.f;
-    if (w_first + j < R) rotate_row<D>(qw[j], lane, x0, x1);
+    for (int j = 0; j < 16; ++j) {
+      float x0 = 0.f, x1 = 0.f;
+      if (w_first + j < R) rotate_row<D>(qw[j], lane, x0, x1);
 #pragma unroll
-    for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
-      const float xs = (e ? x1 : x0) * a.qscale;
-      const _Float16 hi = (_Float16)xs;
-      const _Float16 lo = (_Float16)(xs - (float)hi);
-      const int c = rotated_channel<D>(lane, e);
-      s_q[wv][0][j][c] = hi;
-      s_q[wv][1][j][c] = lo;
+      for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
+        const float xs = (e ? x1 : x0) * a.qscale;
+        const _Float16 hi = (_Float16)xs;
+        const _Float16 lo = (_Float16)(xs - (float)hi);
+        const int c = rotated_channel<D>(lane, e);
+        s_q[rg][0][j][c] = hi;
+        s_q[rg][1][j][c] = lo;
+      }
     }
   }
   __syncthreads();
   half8v bq_hi[KS], bq_lo[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    bq_hi[s] = *reinterpret_cast<const half8v *>(&s_q[wv][0][n][r * (D / 4) + 8 * s]);
-    bq_lo[s] = *reinterpret_cast<const half8v *>(&s_q[wv][1][n][r * (D / 4) + 8 * s]);
+    bq_hi[s] = *reinterpret_cast<const half8v *>(&s_q[rg][0][n][r * (D / 4) + 8 * s]);
+    bq_lo[s] = *reinterpret_cast<const half8v *>(&s_q[rg][1][n][r * (D / 4) + 8 * s]);
   }
   __syncthreads();  // the staging area becomes stage buffer 0
 
@@ -316,10 +374,12 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     const int first = blk0 + k * NW;
     const int cnt = min(NW, blk1 - first);
 #pragma unroll 1
-    for (int j = 0; j < cnt; ++j) {
+    for (int j = 2 * bg; j < cnt; j += 2 * NBG) {
       const int tok0 = (first + j) * 16;
-      if (tok0 >= lmax_w) break;  // this block and the later ones are masked for every row
-      mt_consume<D>(cur[j], bq_hi, bq_lo, st, lane, tok0, lim, tok0 + 16 > lmin_w);
+      if (tok0 >= lmax_w) break;  // this pair and the later ones are masked for every row
+      const bool has_b = j + 1 < cnt;
+      mt_consume_pair<D>(cur[j], cur[has_b ? j + 1 : j], has_b, bq_hi, bq_lo, st, lane, tok0, lim,
+                         tok0 + 32 > lmin_w);
     }
   };
 #pragma unroll 1
@@ -330,10 +390,40 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     if (k + 3 < nstage) stage(b3, k + 3);
   }
 
-  // ---- this wave's rows: output, or the split partial ------------------------------
+  // ---- merge the block groups of each row group ---------------------------------
   float l = st.l;
   l += xor16(l);
   l += xor32(l);
+  if constexpr (NBG > 1) {
+    float4v(*s_fa)[NT][64] = reinterpret_cast<float4v(*)[NT][64]>(&s_stage[0][0]);
+    __syncthreads();  // every wave is done with the stage buffers
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s_fa[wv][t][lane] = st.acc[t];
+    if (r == 0) {
+      s_fm[wv][n] = st.m;
+      s_fl[wv][n] = l;
+    }
+    __syncthreads();
+    if (bg != 0) return;
+    float mx = st.m;
+#pragma unroll
+    for (int q = 1; q < NBG; ++q) mx = __builtin_fmaxf(mx, s_fm[rg + NRG * q][n]);
+    const float f0 = __builtin_amdgcn_exp2f(st.m - mx);
+    l *= f0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.acc[t] *= f0;
+#pragma unroll
+    for (int q = 1; q < NBG; ++q) {
+      const int w2 = rg + NRG * q;
+      const float f = __builtin_amdgcn_exp2f(s_fm[w2][n] - mx);
+      l += f * s_fl[w2][n];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st.acc[t] += f * s_fa[w2][t][lane];
+    }
+    st.m = mx;
+  }
+
+  // ---- this wave's rows: output, or the split partial ------------------------------
   if (!row_ok) return;
   const int64_t orow = (int64_t)(q0 + myrow / a.g) * a.hq + kvh * a.g + myrow % a.g;
   if (a.nsplit == 1) {
@@ -400,7 +490,13 @@ __global__ __launch_bounds__(256) void multitoken_merge_kernel(MultiTokenArgs a)
 template <int D>
 hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
-  hipLaunchKernelGGL(tq4_multitoken_kernel<D>, dim3((unsigned)wgs), dim3(kMtWaves * 64), 0, s, a);
+  const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
+  switch (a.rows_per_wg) {
+    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t rows = (int64_t)a.batch * a.max_query_len * a.hq;

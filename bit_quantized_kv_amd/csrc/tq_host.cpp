@@ -272,6 +272,7 @@ namespace {
 
 struct MtPlan {
   tq::SplitPlan split;
+  int rows_per_wg;
   int row_tiles;
 };
 
@@ -290,13 +291,18 @@ tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_he
   if (num_tokens > (int64_t)batch * max_query_len)
     return fail(TQ_ERR_INVALID_ARG, "num_tokens must be <= batch * max_query_len");
   const int64_t g = num_q_heads / hkv;
-  const int64_t row_tiles = ((int64_t)max_query_len * g + 127) / 128;
+  // rows of one (sequence, kv-head): up to 32 in one work-group of 2 row
+  // groups x 4 block groups, up to 64 in 4 x 2, more in tiles of 128 (8 x 1)
+  const int64_t rows = (int64_t)max_query_len * g;
+  const int rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+  const int64_t row_tiles = (rows + rows_per_wg - 1) / rows_per_wg;
   const tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
                                                      max_context_len);
   if ((int64_t)batch * hkv * row_tiles * sp.nsplit >= (int64_t(1) << 31) ||
       (int64_t)batch * max_query_len * num_q_heads >= (int64_t(1) << 31))
     return fail(TQ_ERR_INVALID_ARG, "launch grid too large");
   p->split = sp;
+  p->rows_per_wg = rows_per_wg;
   p->row_tiles = (int)row_tiles;
   return TQ_OK;
 }
@@ -357,6 +363,7 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
   a.hkv = cache->desc.num_kv_heads;
   a.g = num_q_heads / a.hkv;
   a.max_query_len = max_query_len;
+  a.rows_per_wg = p.rows_per_wg;
   a.row_tiles = p.row_tiles;
   a.split_blocks = p.split.split_blocks;
   a.nsplit = p.split.nsplit;
