@@ -27,7 +27,8 @@ All arithmetic is fp64.  Pinned by tests/test_oracle_attention.py: weights sum
 to 1, brute-force loops on tiny inputs, T = 1, equal logits, merge of any
 partition equals the single pass, GQA with g = 1 equals per-head MHA, block
 table permutation invariance; multi_token against decode over each causal
-prefix and against an explicitly masked softmax matrix.
+prefix and against an explicitly masked softmax matrix; cascade_decode
+against decode.
 """
 import numpy as np
 
@@ -111,6 +112,44 @@ def multi_token(pool, q, q_start, block_table, context_lens, scale, rows=None):
             cache[key] = pool.sequence_tokens(block_table[b], tb, kvh)
         k_rot, v_hat = cache[key]
         out[qi, h] = softmax_attention(rotated_query(pool, q[qi, h]), k_rot[:visible], v_hat[:visible], scale)[0]
+    return out
+
+
+def cascade_decode(pool, q, block_table, context_lens, scale, groups, rows=None):
+    """Decode attention computed the cascade way, for sequences that share
+    their leading blocks ([UQ] "它實際證明了什麼" and [TQ-AMD] spec table:
+    agentic sessions with long shared prefixes).
+
+    ``groups``: list of (member sequences, shared leading blocks P).  For a
+    member b, the partial state (max, sum, acc) of its rows over the P * 16
+    shared tokens (read once for the whole group) and the state over its own
+    tokens P * 16 .. T_b - 1 are combined by ``merge``; other sequences are
+    plain ``decode`` rows.  By the merge identity the result equals ``decode``.
+    Returns fp64 [B, Hq, D] (rows not requested are NaN)."""
+    q = np.asarray(q, dtype=np.float32)
+    bsz, hq, d = q.shape
+    g = hq // pool.hkv
+    prefix = {}
+    for members, pblocks in groups:
+        for b in members:
+            prefix[int(b)] = (int(pblocks), int(members[0]))
+    out = np.full((bsz, hq, d), np.nan)
+    want = rows if rows is not None else [(b, h) for b in range(bsz) for h in range(hq)]
+    for b, h in want:
+        tb = int(context_lens[b])
+        kvh = h // g
+        k_rot, v_hat = pool.sequence_tokens(block_table[b], tb, kvh)
+        qr = rotated_query(pool, q[b, h])
+        pblocks, first = prefix.get(b, (0, b))
+        npre = 16 * pblocks
+        if npre == 0:
+            out[b, h] = softmax_attention(qr, k_rot, v_hat, scale)[0]
+            continue
+        # the shared tokens, read through the group's first member's table
+        k_sh, v_sh = pool.sequence_tokens(block_table[first], npre, kvh)
+        states = [partial_state(scale * (k_sh @ qr), v_sh),
+                  partial_state(scale * (k_rot[npre:] @ qr), v_hat[npre:])]
+        out[b, h] = merge(states)
     return out
 
 

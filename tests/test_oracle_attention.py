@@ -189,3 +189,17 @@ def test_multi_token_prefill_from_the_first_token():
     for h in range(cfg.num_q_heads):
         _, v = pool.sequence_tokens(w.block_table[0], T0, h // 4)
         assert np.array_equal(out[0, h], v[0])
+
+
+def test_cascade_decode_equals_decode():
+    cfg = workloads.small_config(batch=5, num_q_heads=8, num_kv_heads=2, head_dim=64, ctx_range=(70, 200),
+                                 shared_seqs=3, shared_tokens=64, seed=32)
+    w, pool = _filled_pool(cfg)
+    assert np.array_equal(w.block_table[0, :4], w.block_table[2, :4])
+    q = workloads.bf16_bits_to_f32(w.query_bits())
+    ctx = w.context_lens_at()
+    ref = attention.decode(pool, q, w.block_table, ctx, cfg.scale)
+    # the true sharing (4 blocks), a shorter claimed prefix, and a one-member group
+    for groups in ([([0, 1, 2], 4)], [([0, 1, 2], 2), ([4], 3)]):
+        out = attention.cascade_decode(pool, q, w.block_table, ctx, cfg.scale, groups)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
