@@ -21,7 +21,8 @@ EXPORTS = (
     "tq_record_bytes", "tq_pool_bytes", "tq_create_cache", "tq_cache_info", "tq_default_key_table",
     "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_free",
     "tq_status_string", "tq_last_error", "tq_calibrate_workspace_bytes", "tq_calibrate_key_tables",
-    "tq_select_layers", "tq_multitoken_workspace_bytes", "tq_multitoken_attention",
+    "tq_select_layers", "tq_multitoken_workspace_bytes", "tq_multitoken_attention", "tq_cascade_workspace_bytes",
+    "tq_cascade_decode_attention",
 )
 
 
@@ -44,7 +45,7 @@ class CacheDesc(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_kv_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python bit_quantized_kv_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     sz = ctypes.POINTER(ctypes.c_size_t)
@@ -69,6 +70,12 @@ def _load():
         "tq_multitoken_attention": ([P, P, P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32,
                                      P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P,
                                      ctypes.c_size_t, P], ctypes.c_int),
+        "tq_cascade_workspace_bytes": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, sz], ctypes.c_int),
+        "tq_cascade_decode_attention": ([P, P, P, ctypes.c_int32, P, ctypes.c_int32, P, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                         ctypes.c_size_t, P], ctypes.c_int),
         "tq_free": ([P], None),
         "tq_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
@@ -189,6 +196,28 @@ def tq_multitoken_attention(cache, q, out, q_start, max_query_len, block_table, 
                                        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch, hq,
                                        int(max_context_len), float(softmax_scale), _ptr(workspace), wbytes,
                                        _stream(stream)))
+
+
+def tq_cascade_workspace_bytes(cache, batch, num_q_heads, max_context_len, num_groups, max_group_size,
+                               max_group_blocks, max_depth):
+    out = ctypes.c_size_t()
+    _check(LIB.tq_cascade_workspace_bytes(cache, batch, num_q_heads, max_context_len, num_groups, max_group_size,
+                                          max_group_blocks, max_depth, ctypes.byref(out)))
+    return out.value
+
+
+def tq_cascade_decode_attention(cache, q, out, block_table, context_lens, max_context_len, softmax_scale, groups,
+                                workspace, stream=None):
+    """``groups``: a CascadeGroups of device int32 tensors (see cache.py)."""
+    b, hq, _ = q.shape
+    out_dtype = TQ_OUT_BF16 if str(out.dtype) == "torch.bfloat16" else TQ_OUT_F32
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(LIB.tq_cascade_decode_attention(
+        cache, _ptr(q), _ptr(out), out_dtype, _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), b,
+        hq, int(max_context_len), float(softmax_scale), _ptr(groups.seq_prefix_blocks), _ptr(groups.seq_depth),
+        _ptr(groups.group_start), _ptr(groups.group_seqs), _ptr(groups.group_blocks), _ptr(groups.group_depth),
+        groups.num_groups, groups.max_group_size, groups.max_group_blocks, groups.max_depth, _ptr(workspace),
+        wbytes, _stream(stream)))
 
 
 def tq_calibrate_workspace_bytes(num_layers, rows, head_dim):

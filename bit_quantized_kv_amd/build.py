@@ -1,6 +1,6 @@
 """Build the HIP library ``libtq.so`` in-tree for gfx950.
 
-Usage: ``python -m bit_quantized_kv_amd.build`` (or ``build()`` from Python).
+Usage: ``python bit_quantized_kv_amd/build.py`` (or ``__graft_entry__.build()``).
 Every source is compiled on each call; objects go to ``_build/`` at the
 repository root and the shared library next to this file.
 """

@@ -14,6 +14,7 @@ class Cache:
         self.record_bytes = B.tq_record_bytes(fmt, head_dim, num_kv_heads, num_blocks)
         self._ws = None
         self._mt_ws = None
+        self._cas_ws = None
 
     def quantize_append(self, k, v, slot_mapping, stream=None):
         assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int32
@@ -75,6 +76,57 @@ class Cache:
         B.tq_multitoken_attention(self.handle, q, out, q_start, max_query_len, block_table, context_lens,
                                   max_context_len, softmax_scale, ws, stream)
         return out
+
+    def cascade_decode(self, q, block_table, context_lens, max_context_len, softmax_scale, groups, out=None,
+                       out_dtype=torch.float32, stream=None):
+        """Decode attention reading each group's shared blocks once
+        (``groups``: a CascadeGroups)."""
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == self.head_dim
+        assert block_table.dtype == torch.int32 and context_lens.dtype == torch.int32
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        need = B.tq_cascade_workspace_bytes(self.handle, q.shape[0], q.shape[1], max_context_len, groups.num_groups,
+                                            groups.max_group_size, groups.max_group_blocks, groups.max_depth)
+        if self._cas_ws is None or self._cas_ws.numel() < need:
+            self._cas_ws = torch.empty(need, dtype=torch.uint8, device=self.pool.device)
+        B.tq_cascade_decode_attention(self.handle, q, out, block_table, context_lens, max_context_len, softmax_scale,
+                                      groups, self._cas_ws, stream)
+        return out
+
+
+class CascadeGroups:
+    """Shared-block groups for cascade decode, as device int32 tensors.
+    ``groups``: list of (member sequences, lo, hi) block ranges whose members'
+    block tables agree on blocks lo .. hi - 1; the groups of a sequence must
+    cover its first blocks contiguously from 0.  Marshalling only: depths,
+    per-sequence block counts and the bounds follow from the list."""
+
+    def __init__(self, batch, groups, device="cuda"):
+        i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=device)
+        pb = [0] * batch
+        depth = [0] * batch
+        starts, seqs, blocks, gdepth = [0], [], [], []
+        for members, lo, hi in sorted(groups, key=lambda g: g[1]):
+            d = depth[members[0]]
+            for b in members:
+                if pb[b] != lo or depth[b] != d:
+                    raise ValueError("a sequence's groups must cover its blocks contiguously from 0")
+                pb[b] = hi
+                depth[b] = d + 1
+            seqs += list(members)
+            starts.append(len(seqs))
+            blocks += [lo, hi]
+            gdepth.append(d)
+        self.num_groups = len(groups)
+        self.max_group_size = max([len(g[0]) for g in groups] + [1])
+        self.max_group_blocks = max([g[2] - g[1] for g in groups] + [0])
+        self.max_depth = max(depth + [0]) if groups else 0
+        self.seq_prefix_blocks = i32(pb)
+        self.seq_depth = i32(depth)
+        self.group_start = i32(starts)
+        self.group_seqs = i32(seqs or [0])
+        self.group_blocks = i32(blocks or [0, 0])
+        self.group_depth = i32(gdepth or [0])
 
 
 def calibrate_key_tables(k, init_table=None, max_iters=100, stream=None):

@@ -142,8 +142,9 @@ __device__ __forceinline__ void softmax_block(const float (&x)[4], WaveState<G2>
 }
 
 // Combine the NW waves of a work-group and write either the output (single
-// split) or a split partial.  s_m / s_l / s_acc are LDS scratch.
-template <int D, int GQ, int NW>
+// split) or a split partial.  s_m / s_l / s_acc are LDS scratch.  CASCADE:
+// always a partial, at slot sp of rows of a.part_stride slots.
+template <int D, int GQ, int NW, bool CASCADE = false>
 __device__ __forceinline__ void finish_workgroup(const DecodeArgs &a, WaveState<2 * D / 32> &st, int b, int qh0,
                                                  int sp, float (*s_m)[GQ], float (*s_l)[GQ],
                                                  float (*s_acc)[GQ][D]) {
@@ -187,12 +188,12 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs &a, WaveState<
       den += f * s_l[w][hh];
     }
     const int64_t row = (int64_t)b * a.hq + qh0 + hh;
-    if (a.nsplit == 1) {
+    if (!CASCADE && a.nsplit == 1) {
       const float o = den > 0.f ? num / den : 0.f;
       if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[row * D + c] = f32_to_bf16(o);
       else reinterpret_cast<float *>(a.out)[row * D + c] = o;
     } else {
-      const int64_t pi = row * a.nsplit + sp;
+      const int64_t pi = row * (CASCADE ? a.part_stride : a.nsplit) + sp;
       a.part_acc[pi * D + c] = num;
       if (c == 0) {
         a.part_ml[pi * 2] = mx;
@@ -226,10 +227,21 @@ struct MergeView {
   int32_t out_bf16;
 };
 
-// ns: splits that hold this row's tokens (0: the row attends to nothing and is
-// written as zeros).
-template <int D>
-__device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int ns) {
+// The partial slots of a row in order: the first ns (plain split-K).
+struct SlotsDirect {
+  __device__ __forceinline__ int operator()(int k) const { return k; }
+};
+// Two runs of slots: [0, n0), then [lo1, lo1 + ns - n0) (cascade: the
+// sequence's own splits, then its shared-prefix splits).
+struct SlotsTwoRuns {
+  int n0, lo1;
+  __device__ __forceinline__ int operator()(int k) const { return k < n0 ? k : lo1 + (k - n0); }
+};
+
+// ns: partials that hold this row's tokens (0: the row attends to nothing and
+// is written as zeros); slot(k) is the slot of the k-th.
+template <int D, typename Slots = SlotsDirect>
+__device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int ns, Slots slot = Slots()) {
   constexpr int CQ = D / 4;          // channel quads
   constexpr int SL = 256 / CQ;       // split lanes
   constexpr int CH = 8;              // splits per thread per chunk
@@ -251,11 +263,11 @@ __device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int n
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int sp = min(sl + j * SL, ns - 1);  // clamped: valid split of this row
-    c_ml[j] = ml[sp];
-    c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
+    c_ml[j] = ml[slot(sp)];
+    c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)slot(sp) * D + 4 * cq);
   }
   float M = kNegInf;
-  for (int sp = lane; sp < ns; sp += 64) M = __builtin_fmaxf(M, ml[sp].x);
+  for (int sp = lane; sp < ns; sp += 64) M = __builtin_fmaxf(M, ml[slot(sp)].x);
   M = __builtin_fmaxf(M, xor1(M));
   M = __builtin_fmaxf(M, xor2(M));
   M = __builtin_fmaxf(M, xor4(M));
@@ -269,8 +281,8 @@ __device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int n
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const int sp = min(base + sl + j * SL, ns - 1);
-        c_ml[j] = ml[sp];
-        c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)sp * D + 4 * cq);
+        c_ml[j] = ml[slot(sp)];
+        c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)slot(sp) * D + 4 * cq);
       }
     }
 #pragma unroll

@@ -161,7 +161,7 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
   }
 }
 
-template <int D, int GQ>
+template <int D, int GQ, bool CASCADE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void tq4_decode_kernel(
     DecodeArgs a) {
   constexpr int G = D / 32, KS = D / 32;
@@ -184,7 +184,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   // this wave's block ids, fetched before the context length is known (the
   // index is clamped into the table row; entries past the context are never
   // used): blocks blk0 + wv + k * NW, lane k holds the id of the k-th
-  const int blk0 = sp * a.split_blocks;
+  // cascade: the splits start at the sequence's first block of its own
+  const int blk0 = (CASCADE ? a.first_blk[b] : 0) + sp * a.split_blocks;
   const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
   const int my_id_raw = btab[min(blk0 + wv + lane * NW, a.max_blocks - 1)];
   // set-up loads next (table word, query word): they complete while the block
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   __asm__ volatile("" ::: "memory");
   const int nblk = (T + 15) >> 4;
   if (nblk == 0) {
-    if (a.nsplit == 1 && sp == 0) write_zero_rows<D>(a, b, qh0, GQ);
+    if (!CASCADE && a.nsplit == 1 && sp == 0) write_zero_rows<D>(a, b, qh0, GQ);
     return;
   }
   if (blk0 >= nblk) return;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     run(b3, k + 3);
   }
 
-  finish_workgroup<D, GQ, NW>(a, st, b, qh0, sp, s_m, s_l, s_acc);
+  finish_workgroup<D, GQ, NW, CASCADE>(a, st, b, qh0, sp, s_m, s_l, s_acc);
 }
 
 // One work-group per (sequence, query head): combine the split partials.
@@ -297,15 +298,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.nsplit, a.out_bf16}, row, ns);
 }
 
+// Cascade: one work-group per (sequence, query head) combines the row's own
+// splits (slots 0 .. its split count - 1) with the splits of the shared-block
+// groups it is in (slots nsplit + d * prefix_nsplit + k for depth d; empty
+// splits hold empty partials).
 template <int D>
+__global__ __launch_bounds__(256) void cascade_merge_kernel(DecodeArgs a) {
+  const int64_t row = blockIdx.x;
+  const int b = (int)(row / a.hq);
+  const int T = a.ctx[b];
+  const int fb = a.first_blk[b];
+  const int nblk = (T + 15) >> 4;
+  const int own = nblk > fb ? (nblk - fb + a.split_blocks - 1) / a.split_blocks : 0;
+  const int pre = a.depth[b] * a.prefix_nsplit;
+  merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.part_stride, a.out_bf16}, row, own + pre,
+               SlotsTwoRuns{own, a.nsplit});
+}
+
+template <int D, bool CASCADE>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kWaves * 64);
   switch (a.g) {
-    case 1: hipLaunchKernelGGL((tq4_decode_kernel<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((tq4_decode_kernel<D, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((tq4_decode_kernel<D, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((tq4_decode_kernel<D, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((tq4_decode_kernel<D, 1, CASCADE>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((tq4_decode_kernel<D, 2, CASCADE>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((tq4_decode_kernel<D, 4, CASCADE>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((tq4_decode_kernel<D, 8, CASCADE>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -314,7 +332,18 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s) {
-  return d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+  return d == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
+}
+
+hipError_t launch_tq4_cascade_decode(int d, const DecodeArgs &a, hipStream_t s) {
+  return d == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
+}
+
+hipError_t launch_cascade_merge(int d, const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.batch * a.hq)), block(256);
+  if (d == 128) hipLaunchKernelGGL(cascade_merge_kernel<128>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(cascade_merge_kernel<64>, grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s) {

@@ -238,7 +238,12 @@ __device__ __forceinline__ void mt_consume_pair(const MtSlot<D> &sa, const MtSlo
 // tile and, of the four block pairs of every stage, those with index
 // w / NRG (mod NBG); the block groups of a row group are merged in LDS at the
 // end.  Every wave loads and dequantizes one block per stage.
-template <int D, int NRG>
+//
+// PREFIX (the shared-prefix pass of cascade decode): the work-group's rows are
+// the (member sequence, query head) pairs of one group of sequences that share
+// their leading blocks; every row sees all the shared tokens, which are read
+// once for the whole group; the results are always partials.
+template <int D, int NRG, bool PREFIX>
 __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiTokenArgs a) {
   constexpr int G = D / 32, KS = D / 32, NT = D / 16;
   constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
@@ -261,17 +266,46 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   const MtTask task = mt_task(a);
   const int b = task.b, kvh = task.kvh, sp = task.sp;
 
-  const int q0 = a.q_start[b];
-  const int M = a.q_start[b + 1] - q0;
-  const int T = a.ctx[b];
+  // causal: b is a sequence, its query tokens q0 .. q0 + M - 1; prefix: b is a
+  // group, q0 its first member's index into group_seqs, M its size
+  int q0, M, T, tab_seq, blk_lo = 0, slot = sp;
+  if constexpr (PREFIX) {
+    q0 = a.group_start[b];
+    M = a.group_start[b + 1] - q0;
+    if (M <= 0) return;
+    tab_seq = a.group_seqs[q0];
+    blk_lo = a.group_blocks[2 * b];
+    T = 16 * a.group_blocks[2 * b + 1];
+    slot = a.slot0 + a.group_depth[b] * a.nsplit + sp;
+  } else {
+    q0 = a.q_start[b];
+    M = a.q_start[b + 1] - q0;
+    T = a.ctx[b];
+    tab_seq = b;
+  }
   const int R = M * a.g;
   const int row0 = task.rt * RW;
   if (row0 >= R) return;
   const int rlast = min(R, row0 + RW) - 1;
-  const int lmax_wg = T - M + rlast / a.g + 1;  // keys the work-group's last row sees
+  // keys the work-group's last row sees (prefix: every row sees all T)
+  const int lmax_wg = PREFIX ? T : T - M + rlast / a.g + 1;
   const int nblk = (lmax_wg + 15) >> 4;
-  const int blk0 = sp * a.split_blocks;
-  if (blk0 >= nblk) return;
+  const int blk0 = blk_lo + sp * a.split_blocks;
+  if (blk0 >= nblk) {
+    if constexpr (PREFIX) {
+      // an empty split of the group: its rows get empty partials (max -inf,
+      // sum 0), which the merge weighs 0
+      for (int i = threadIdx.x; i < RW * (D + 2); i += NW * 64) {
+        const int row = row0 + i / (D + 2), c = i % (D + 2);
+        if (row >= R) continue;
+        const int who = row / a.g, j = row % a.g;
+        const int64_t pi = ((int64_t)a.group_seqs[q0 + who] * a.hq + kvh * a.g + j) * a.part_stride + slot;
+        if (c < D) a.part_acc[pi * D + c] = 0.f;
+        else a.part_ml[pi * 2 + (c - D)] = c == D ? kNegInf : 0.f;
+      }
+    }
+    return;
+  }
   const int blk1 = min(nblk, blk0 + a.split_blocks);
   const int nb = blk1 - blk0;
 
@@ -280,14 +314,20 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   const int w_first = row0 + 16 * rg;
   const int myrow = w_first + n;
   const bool row_ok = myrow < R;
-  const int lim = row_ok ? T - M + myrow / a.g + 1 : 0;
+  const int lim = row_ok ? (PREFIX ? T : T - M + myrow / a.g + 1) : 0;
   // the wave's smallest and largest visible-key counts (its first and last rows)
   const int w_last = min(R, w_first + 16) - 1;
-  const int lmin_w = w_first < R ? T - M + w_first / a.g + 1 : 0;
-  const int lmax_w = w_first < R ? T - M + w_last / a.g + 1 : 0;
+  const int lmin_w = w_first < R ? (PREFIX ? T : T - M + w_first / a.g + 1) : 0;
+  const int lmax_w = w_first < R ? (PREFIX ? T : T - M + w_last / a.g + 1) : 0;
+  // query / output row of tile row `row`: (token or member, head)
+  auto q_row = [&](int row) -> int64_t {
+    const int who = row / a.g, j = row % a.g;
+    const int64_t tok = PREFIX ? (int64_t)a.group_seqs[q0 + who] : (int64_t)(q0 + who);
+    return tok * a.hq + kvh * a.g + j;
+  };
 
   // ---- block ids and the first loads ---------------------------------------------
-  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
+  const int32_t *btab = a.block_table + (int64_t)tab_seq * a.max_blocks;
   const int my_id_raw = btab[min(blk0 + wv + lane * NW, a.max_blocks - 1)];
   const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
   __asm__ volatile("" ::: "memory");
@@ -327,9 +367,7 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     uint32_t qw[16];  // all 16 query loads in flight before the first rotation
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int row = min(w_first + j, R - 1);
-      const int64_t qrow = (int64_t)(q0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
-      qw[j] = load_query_word<D>(a.q + qrow * D, lane);
+      qw[j] = load_query_word<D>(a.q + q_row(min(w_first + j, R - 1)) * D, lane);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -425,8 +463,8 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
 
   // ---- this wave's rows: output, or the split partial ------------------------------
   if (!row_ok) return;
-  const int64_t orow = (int64_t)(q0 + myrow / a.g) * a.hq + kvh * a.g + myrow % a.g;
-  if (a.nsplit == 1) {
+  const int64_t orow = q_row(myrow);
+  if (!PREFIX && a.nsplit == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int gp = 0; gp < G; ++gp) {
@@ -451,7 +489,7 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
       }
     }
   } else {
-    const int64_t pi = orow * a.nsplit + sp;
+    const int64_t pi = orow * a.part_stride + slot;
 #pragma unroll
     for (int gp = 0; gp < G; ++gp) {
       float4 *dst = reinterpret_cast<float4 *>(a.part_acc + pi * D + 32 * gp + 8 * r);
@@ -492,9 +530,9 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, false>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, false>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, false>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -504,10 +542,27 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_prefix(const MultiTokenArgs &a, hipStream_t s) {
+  const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
+  const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
+  switch (a.rows_per_wg) {
+    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, true>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, true>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, true>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_tq4_multitoken(int d, const MultiTokenArgs &a, hipStream_t s) {
   return d == 128 ? launch_mt<128>(a, s) : launch_mt<64>(a, s);
+}
+
+hipError_t launch_prefix_attention(int d, const MultiTokenArgs &a, hipStream_t s) {
+  return d == 128 ? launch_prefix<128>(a, s) : launch_prefix<64>(a, s);
 }
 
 }  // namespace tq

@@ -367,9 +367,163 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
   a.row_tiles = p.row_tiles;
   a.split_blocks = p.split.split_blocks;
   a.nsplit = p.split.nsplit;
+  a.part_stride = p.split.nsplit;
+  a.slot0 = 0;
   a.out_bf16 = out_dtype == TQ_OUT_BF16;
   hipError_t e = tq::launch_tq4_multitoken(d, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "multi-token attention launch");
+  return TQ_OK;
+}
+
+namespace {
+
+struct CascadePlan {
+  tq::SplitPlan own, prefix;
+  int rows_per_wg, row_tiles;
+  int part_stride;
+};
+
+tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                       int32_t num_groups, int32_t max_group_size, int32_t max_group_blocks, int32_t max_depth,
+                       CascadePlan *p) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (cache->desc.format != TQ_FORMAT_TQ4)
+    return fail(TQ_ERR_UNSUPPORTED, "cascade decode is built for the TQ4/4 format");
+  const int hkv = cache->desc.num_kv_heads;
+  if (batch < 0 || max_context_len < 0 || num_groups < 0 || max_group_blocks < 0 || max_depth < 0)
+    return fail(TQ_ERR_INVALID_ARG,
+                "batch, max_context_len, num_groups, max_group_blocks and max_depth must be >= 0");
+  if (num_q_heads < hkv || num_q_heads % hkv)
+    return fail(TQ_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  const int g = num_q_heads / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "query heads per kv-head must be 1, 2, 4 or 8");
+  if (num_groups > 0 && (max_group_size < 1 || max_group_size > batch))
+    return fail(TQ_ERR_INVALID_ARG, "max_group_size must be in [1, batch]");
+  if (num_groups > 0 && (max_depth < 1 || max_depth > num_groups))
+    return fail(TQ_ERR_INVALID_ARG, "max_depth must be in [1, num_groups]");
+  if ((int64_t)16 * max_group_blocks > max_context_len)
+    return fail(TQ_ERR_INVALID_ARG, "16 * max_group_blocks must be <= max_context_len");
+  p->own = tq::plan_split(batch, hkv, max_context_len);
+  const int64_t rows = (int64_t)std::max(1, max_group_size) * g;
+  p->rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+  p->row_tiles = (int)((rows + p->rows_per_wg - 1) / p->rows_per_wg);
+  p->prefix = tq::plan_split_multitoken((int64_t)std::max(1, num_groups) * hkv * p->row_tiles,
+                                        16 * max_group_blocks);
+  const int64_t stride = (int64_t)p->own.nsplit + (int64_t)(num_groups > 0 ? max_depth : 0) * p->prefix.nsplit;
+  if (stride > (1 << 20)) return fail(TQ_ERR_INVALID_ARG, "too many partial slots per row");
+  p->part_stride = (int)stride;
+  return TQ_OK;
+}
+
+}  // namespace
+
+tq_status tq_cascade_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
+                                     int32_t max_group_blocks, int32_t max_depth, size_t *bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  CascadePlan p;
+  tq_status st = cascade_plan(cache, batch, num_q_heads, max_context_len, num_groups, max_group_size,
+                              max_group_blocks, max_depth, &p);
+  if (st != TQ_OK) return st;
+  const size_t rows = (size_t)batch * num_q_heads * p.part_stride;
+  *bytes = ((rows * 2 * 4 + 255) / 256) * 256 + rows * (size_t)cache->desc.head_dim * 4;
+  return TQ_OK;
+}
+
+tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                                      const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                                      int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                      float softmax_scale, const int32_t *seq_prefix_blocks,
+                                      const int32_t *seq_depth, const int32_t *group_start,
+                                      const int32_t *group_seqs, const int32_t *group_blocks,
+                                      const int32_t *group_depth, int32_t num_groups, int32_t max_group_size,
+                                      int32_t max_group_blocks, int32_t max_depth, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  CascadePlan p;
+  tq_status st = cascade_plan(cache, batch, num_q_heads, max_context_len, num_groups, max_group_size,
+                              max_group_blocks, max_depth, &p);
+  if (st != TQ_OK) return st;
+  if (batch == 0) return TQ_OK;
+  if (!q || !out || !block_table || !context_lens || !seq_prefix_blocks || !seq_depth)
+    return fail(TQ_ERR_INVALID_ARG,
+                "q, out, block_table, context_lens, seq_prefix_blocks and seq_depth must be non-NULL");
+  if (num_groups > 0 && (!group_start || !group_seqs || !group_blocks || !group_depth))
+    return fail(TQ_ERR_INVALID_ARG, "group_start, group_seqs, group_blocks and group_depth must be non-NULL");
+  if (out_dtype != TQ_OUT_F32 && out_dtype != TQ_OUT_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
+  if (max_blocks < (max_context_len + 15) / 16 || max_blocks < 1)
+    return fail(TQ_ERR_INVALID_ARG, "max_blocks must cover max_context_len");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(TQ_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  size_t need = 0;
+  tq_cascade_workspace_bytes(cache, batch, num_q_heads, max_context_len, num_groups, max_group_size,
+                             max_group_blocks, max_depth, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_cascade_workspace_bytes (" + std::to_string(need) + ")");
+  const int d = cache->desc.head_dim;
+  const int hkv = cache->desc.num_kv_heads;
+  float *part_ml = static_cast<float *>(workspace);
+  float *part_acc = part_ml + (((size_t)batch * num_q_heads * p.part_stride * 2 + 63) / 64) * 64;
+  const double log2e = 1.4426950408889634074;
+  const float qscale = (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  if (num_groups > 0) {
+    tq::MultiTokenArgs m{};
+    m.q = static_cast<const uint16_t *>(q);
+    m.block_table = block_table;
+    m.pool = cache->pool;
+    m.tables = cache->tables;
+    m.part_ml = part_ml;
+    m.part_acc = part_acc;
+    m.qscale = qscale;
+    m.max_blocks = max_blocks;
+    m.batch = num_groups;
+    m.hq = num_q_heads;
+    m.hkv = hkv;
+    m.g = num_q_heads / hkv;
+    m.max_query_len = max_group_size;
+    m.rows_per_wg = p.rows_per_wg;
+    m.row_tiles = p.row_tiles;
+    m.split_blocks = p.prefix.split_blocks;
+    m.nsplit = p.prefix.nsplit;
+    m.group_start = group_start;
+    m.group_seqs = group_seqs;
+    m.group_blocks = group_blocks;
+    m.group_depth = group_depth;
+    m.part_stride = p.part_stride;
+    m.slot0 = p.own.nsplit;
+    e = tq::launch_prefix_attention(d, m, s);
+    if (e != hipSuccess) return hip_fail(e, "shared-block attention launch");
+  }
+  tq::DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.out = out;
+  a.block_table = block_table;
+  a.ctx = context_lens;
+  a.pool = cache->pool;
+  a.tables = cache->tables;
+  a.part_ml = part_ml;
+  a.part_acc = part_acc;
+  a.qscale = qscale;
+  a.rsqrt_d = (float)(1.0 / std::sqrt((double)d));
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = hkv;
+  a.g = num_q_heads / hkv;
+  a.split_blocks = p.own.split_blocks;
+  a.nsplit = p.own.nsplit;
+  a.out_bf16 = out_dtype == TQ_OUT_BF16;
+  a.first_blk = seq_prefix_blocks;
+  a.depth = seq_depth;
+  a.part_stride = p.part_stride;
+  a.prefix_nsplit = num_groups > 0 ? p.prefix.nsplit : 0;
+  e = tq::launch_tq4_cascade_decode(d, a, s);
+  if (e != hipSuccess) return hip_fail(e, "cascade decode launch");
+  e = tq::launch_cascade_merge(d, a, s);
+  if (e != hipSuccess) return hip_fail(e, "cascade merge launch");
   return TQ_OK;
 }
 

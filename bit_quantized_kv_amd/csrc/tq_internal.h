@@ -50,6 +50,12 @@ struct DecodeArgs {
   int32_t split_blocks;          // blocks per work-group
   int32_t nsplit;                // splits per (sequence, kv-head)
   int32_t out_bf16;
+  // cascade decode only: the sequence's first block of its own (after the
+  // shared prefix), and partial slots per row (own splits, then the prefix's)
+  const int32_t *first_blk;      // [batch]
+  const int32_t *depth;          // [batch]: shared-block groups the sequence is in
+  int32_t part_stride;
+  int32_t prefix_nsplit;         // partial slots per group depth
 };
 
 struct MultiTokenArgs {
@@ -69,6 +75,18 @@ struct MultiTokenArgs {
   int32_t row_tiles;             // row tiles per (sequence, kv-head)
   int32_t split_blocks, nsplit;
   int32_t out_bf16;
+  // shared-prefix mode (the prefix pass of cascade decode): work-groups walk
+  // groups instead of sequences (batch = number of groups, max_query_len =
+  // largest group); group i's members are group_seqs[group_start[i] ..
+  // group_start[i+1]), its shared blocks group_blocks[2i] .. group_blocks[2i+1]
+  // - 1 of its first member's table, its depth group_depth[i]; the partial
+  // of split sp goes to slot slot0 + depth * nsplit + sp of rows of
+  // part_stride slots (an empty split writes an empty partial)
+  const int32_t *group_start;
+  const int32_t *group_seqs;
+  const int32_t *group_blocks;
+  const int32_t *group_depth;
+  int32_t part_stride, slot0;
 };
 
 // Launchers (defined next to their kernels).
@@ -78,6 +96,9 @@ hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_tq4_multitoken(int d, const MultiTokenArgs &a, hipStream_t s);
+hipError_t launch_prefix_attention(int d, const MultiTokenArgs &a, hipStream_t s);
+hipError_t launch_tq4_cascade_decode(int d, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_cascade_merge(int d, const DecodeArgs &a, hipStream_t s);
 size_t calibrate_workspace_bytes(int64_t layers, int64_t rows, int d);
 hipError_t launch_calibrate(int d, int layers, int64_t rows, const uint16_t *k, const uint16_t init_f16[16],
                             int max_iters, float rsqrt_d, void *workspace, uint16_t *tables, double *levels,

@@ -192,6 +192,49 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
                                   float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Shared-prefix (cascade) decode attention (TQ4/4).  The same result as
+ * tq_decode_attention, computed so that blocks shared by several sequences
+ * are read once: the pages' agentic workloads keep long prefixes resident and
+ * shared between sessions ([TQ-AMD] spec table; [UQ] "它實際證明了什麼"), and
+ * paged blocks are what the sequences share ([ST]).
+ * A group is a set of sequences whose block tables agree on a block range
+ * [lo, hi): for every row (member b, head h) the partial softmax state over
+ * the group's 16 (hi - lo) tokens is computed once for the whole group (all
+ * members' heads of a kv-head together, each shared block read once), the
+ * state over the sequence's own tokens separately, and all are combined by
+ * the log-sum-exp merge.  Groups nest: the groups a sequence is in cover its
+ * first P_b blocks contiguously, from block 0, in order of depth (the group
+ * at depth d covers the blocks after those of depth d - 1); its own part is
+ * tokens 16 P_b .. T_b - 1.
+ * Arguments as tq_decode_attention, plus (all device, trusted):
+ *   seq_prefix_blocks  int32 [batch]: P_b (0 for a sequence in no group),
+ *                      16 P_b <= context_lens[b]
+ *   seq_depth          int32 [batch]: the number of groups sequence b is in
+ *   group_start        int32 [num_groups + 1], group_seqs int32 [...]: group
+ *                      i's members are group_seqs[group_start[i] ..
+ *                      group_start[i+1]) (at most max_group_size); the
+ *                      shared blocks are read through the first member's table
+ *   group_blocks       int32 [num_groups][2]: lo, hi (hi - lo <= max_group_blocks)
+ *   group_depth        int32 [num_groups]: the group's depth (< max_depth)
+ *   host: num_groups >= 0; when > 0, max_group_size in [1, batch] and
+ *   max_depth in [1, num_groups]; 16 * max_group_blocks <= max_context_len.
+ * num_q_heads / num_kv_heads must be 1, 2, 4 or 8.  workspace: device buffer
+ * of at least tq_cascade_workspace_bytes (always needed).  MX-FP4 caches
+ * return TQ_ERR_UNSUPPORTED.  Asynchronous. */
+tq_status tq_cascade_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
+                                     int32_t max_group_blocks, int32_t max_depth, size_t *bytes);
+tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                                      const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                                      int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                      float softmax_scale, const int32_t *seq_prefix_blocks,
+                                      const int32_t *seq_depth, const int32_t *group_start,
+                                      const int32_t *group_seqs, const int32_t *group_blocks,
+                                      const int32_t *group_depth, int32_t num_groups, int32_t max_group_size,
+                                      int32_t max_group_blocks, int32_t max_depth, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Calibrated key tables ([UQ] "方法怎麼做，白話講": the 16-entry key table is
  * refit on captured activations, about 20 vectors per rotated layer, and used
  * only on the tenth of the layers with the highest per-element key MSE).

@@ -117,22 +117,24 @@ def multi_token(pool, q, q_start, block_table, context_lens, scale, rows=None):
 
 def cascade_decode(pool, q, block_table, context_lens, scale, groups, rows=None):
     """Decode attention computed the cascade way, for sequences that share
-    their leading blocks ([UQ] "它實際證明了什麼" and [TQ-AMD] spec table:
-    agentic sessions with long shared prefixes).
+    leading blocks ([UQ] "它實際證明了什麼" and [TQ-AMD] spec table: agentic
+    sessions with long shared prefixes).
 
-    ``groups``: list of (member sequences, shared leading blocks P).  For a
-    member b, the partial state (max, sum, acc) of its rows over the P * 16
-    shared tokens (read once for the whole group) and the state over its own
-    tokens P * 16 .. T_b - 1 are combined by ``merge``; other sequences are
-    plain ``decode`` rows.  By the merge identity the result equals ``decode``.
-    Returns fp64 [B, Hq, D] (rows not requested are NaN)."""
+    ``groups``: list of (member sequences, lo, hi): the members' tables agree
+    on blocks lo .. hi - 1, and a sequence's groups cover its first blocks
+    contiguously from 0.  For a row of member b, the partial state (max, sum,
+    acc) over each of its groups' tokens (read through the group's first
+    member's table, once for the group) and the state over its own remaining
+    tokens are combined by ``merge``; other sequences are plain ``decode``
+    rows.  By the merge identity the result equals ``decode``.  Returns fp64
+    [B, Hq, D] (rows not requested are NaN)."""
     q = np.asarray(q, dtype=np.float32)
     bsz, hq, d = q.shape
     g = hq // pool.hkv
-    prefix = {}
-    for members, pblocks in groups:
+    of_seq = {}
+    for members, lo, hi in groups:
         for b in members:
-            prefix[int(b)] = (int(pblocks), int(members[0]))
+            of_seq.setdefault(int(b), []).append((int(lo), int(hi), int(members[0])))
     out = np.full((bsz, hq, d), np.nan)
     want = rows if rows is not None else [(b, h) for b in range(bsz) for h in range(hq)]
     for b, h in want:
@@ -140,15 +142,14 @@ def cascade_decode(pool, q, block_table, context_lens, scale, groups, rows=None)
         kvh = h // g
         k_rot, v_hat = pool.sequence_tokens(block_table[b], tb, kvh)
         qr = rotated_query(pool, q[b, h])
-        pblocks, first = prefix.get(b, (0, b))
-        npre = 16 * pblocks
-        if npre == 0:
-            out[b, h] = softmax_attention(qr, k_rot, v_hat, scale)[0]
-            continue
-        # the shared tokens, read through the group's first member's table
-        k_sh, v_sh = pool.sequence_tokens(block_table[first], npre, kvh)
-        states = [partial_state(scale * (k_sh @ qr), v_sh),
-                  partial_state(scale * (k_rot[npre:] @ qr), v_hat[npre:])]
+        states, own = [], 0
+        for lo, hi, first in sorted(of_seq.get(b, [])):
+            if lo != own:
+                raise ValueError("a sequence's groups must cover its blocks contiguously from 0")
+            k_sh, v_sh = pool.sequence_tokens(block_table[first], 16 * hi, kvh)
+            states.append(partial_state(scale * (k_sh[16 * lo:] @ qr), v_sh[16 * lo:]))
+            own = hi
+        states.append(partial_state(scale * (k_rot[16 * own:] @ qr), v_hat[16 * own:]))
         out[b, h] = merge(states)
     return out
 

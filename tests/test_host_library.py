@@ -4,6 +4,7 @@ key table) behaves as documented.  No kernel is launched."""
 import ctypes
 import os
 import re
+import sys
 
 import numpy as np
 import pytest
@@ -14,8 +15,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _ensure_built():
     path = os.path.join(ROOT, "bit_quantized_kv_amd", "libtq.so")
     if not os.path.exists(path):
-        from bit_quantized_kv_amd import build as b
-        b.build()
+        sys.path.insert(0, ROOT)
+        import __graft_entry__
+        __graft_entry__._build_module().build()
     return path
 
 

@@ -199,7 +199,9 @@ def test_cascade_decode_equals_decode():
     q = workloads.bf16_bits_to_f32(w.query_bits())
     ctx = w.context_lens_at()
     ref = attention.decode(pool, q, w.block_table, ctx, cfg.scale)
-    # the true sharing (4 blocks), a shorter claimed prefix, and a one-member group
-    for groups in ([([0, 1, 2], 4)], [([0, 1, 2], 2), ([4], 3)]):
+    # the true sharing (4 blocks), a shorter claimed prefix, nested groups and
+    # a one-member group
+    for groups in ([([0, 1, 2], 0, 4)], [([0, 1, 2], 0, 2), ([4], 0, 3)],
+                   [([0, 1, 2], 0, 1), ([0, 2], 1, 3), ([2], 3, 4)]):
         out = attention.cascade_decode(pool, q, w.block_table, ctx, cfg.scale, groups)
         assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)

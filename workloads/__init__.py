@@ -204,6 +204,23 @@ class Workload:
                 plan.append((b, t0, t1))
         return plan
 
+    def shared_block_groups(self, ctx=None):
+        """The nested groups of shared blocks: list of (members, lo, hi).
+        Sharer b holds P_b = floor(min(T_b, shared_tokens) / 16) full shared
+        blocks (a partly used last shared block stays its own); with the
+        distinct P values p_1 < p_2 < ..., group i covers blocks p_{i-1} ..
+        p_i - 1 for the sharers with P_b >= p_i."""
+        c = self.cfg
+        ctx = self.total_lens if ctx is None else np.asarray(ctx)
+        pb = {b: int(min(int(ctx[b]), c.shared_tokens)) // BLOCK for b in range(c.shared_seqs)}
+        levels = sorted(set(v for v in pb.values() if v > 0))
+        groups, lo = [], 0
+        for hi in levels:
+            members = [b for b in range(c.shared_seqs) if pb[b] >= hi]
+            groups.append((members, lo, hi))
+            lo = hi
+        return groups
+
     def slots(self, b, t0, t1):
         """Slot of each token t in [t0, t1) of sequence b."""
         t = np.arange(t0, t1)
