@@ -44,10 +44,13 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="llama8b",
-                   choices=["llama8b", "agentic", "longprefix", "fp4", "calib", "verify", "prefill"],
+                   choices=["llama8b", "agentic", "longprefix", "fp4", "calib", "verify", "prefill", "cascade"],
                    help="calib: the calibrated key-table fit of a 32-layer stack; verify / prefill: multi-token "
-                        "attention over the cache (each its own JSON line)")
+                        "attention over the cache; cascade: the agentic workload decoded with shared blocks "
+                        "read once per group (each its own JSON line)")
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
+    p.add_argument("--cascade-group-blocks", type=int, default=48,
+                   help="cascade: shared ranges are cut into groups of at most this many blocks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for counter calibration)")
@@ -77,7 +80,7 @@ def copy_calibration():
 
 
 class Bench:
-    def __init__(self, cfg, copies):
+    def __init__(self, cfg, copies, cascade=False, group_blocks=48):
         import torch
 
         import workloads
@@ -126,6 +129,13 @@ class Bench:
         self.out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.float32, device="cuda")
         for cache in self.caches:   # size the decode workspace outside the timed region
             cache.workspace(c.batch, c.num_q_heads, max(self.max_ctx))
+        self.cascade = None
+        if cascade:
+            from bit_quantized_kv_amd import CascadeGroups
+            self.cascade = CascadeGroups(c.batch, w.shared_block_groups(w.context_lens_at(0)), max_blocks=group_blocks)
+            for cache in self.caches:
+                cache.cascade_decode(self.q[0], self.table, self.ctx[0], self.max_ctx[0], c.scale, self.cascade,
+                                     out=self.out)
         self.stream = torch.cuda.current_stream()
 
     # algorithmic bytes ---------------------------------------------------------
@@ -163,6 +173,10 @@ class Bench:
 
     def decode(self, i, s):
         c = self.cfg
+        if self.cascade is not None:
+            self.caches[i % self.pool_copies].cascade_decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s],
+                                                             c.scale, self.cascade, out=self.out)
+            return
         self.caches[i % self.pool_copies].decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s], c.scale,
                                                  out=self.out)
 
@@ -594,7 +608,9 @@ def main():
     import torch
     import workloads
     torch.cuda.set_device(0)
-    bench = Bench(workloads.CONFIGS[args.config], args.copies)
+    cascade = args.config == "cascade"
+    cfg_name = "agentic" if cascade else args.config
+    bench = Bench(workloads.CONFIGS[cfg_name], args.copies, cascade=cascade, group_blocks=args.cascade_group_blocks)
     c = bench.cfg
     stream = bench.stream
     for i in range(args.warmup + bench.pool_copies):
@@ -625,7 +641,8 @@ def main():
     def roof(name):
         k = kernels[name]
         return {"bound": "hbm", "achieved": round(k["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(k["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(args.config, name),
+                "frac": round(k["GBps"] / HBM_PEAK_GBPS, 4),
+                "traffic": None if cascade and name == "decode" else traffic_from_profiles(cfg_name, name),
                 "kernel": name, "bytes_per_launch": k["bytes"], "avg_launch_us": round(k["avg_us"], 2)}
 
     res = {
@@ -643,7 +660,9 @@ def main():
         "data": "synthetic (seeded; shapes of the pages' agentic workloads)",
         "config": {"workload": f"{c.name}: batch {c.batch}, {c.num_q_heads}/{c.num_kv_heads} heads, "
                                f"head_dim {c.head_dim}, context {int(bench.w.context_lens_at(0).max())}, "
-                               f"format {'TQ4/4' if c.fmt == 0 else 'MX-FP4'}",
+                               f"format {'TQ4/4' if c.fmt == 0 else 'MX-FP4'}"
+                               + (f", cascade decode over {bench.cascade.num_groups} nested groups of shared blocks"
+                                  if cascade else ""),
                    "tokens_quantized_per_step": bench.n_tokens, "decode_steps_per_step": c.decode_steps,
                    "input_copies": bench.in_copies, "pool_copies": bench.pool_copies},
         "decode_hbm_frac": round(kv_unique / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -655,7 +674,7 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.config)
+        res["cpu_baseline"] = cpu_baseline(cfg_name)
     print(json.dumps(res))
 
 

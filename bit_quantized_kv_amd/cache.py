@@ -98,11 +98,18 @@ class CascadeGroups:
     """Shared-block groups for cascade decode, as device int32 tensors.
     ``groups``: list of (member sequences, lo, hi) block ranges whose members'
     block tables agree on blocks lo .. hi - 1; the groups of a sequence must
-    cover its first blocks contiguously from 0.  Marshalling only: depths,
-    per-sequence block counts and the bounds follow from the list."""
+    cover its first blocks contiguously from 0.  A range longer than
+    ``max_blocks`` is cut into chained groups of that many blocks (a group is
+    one unit of parallel work).  Marshalling only: depths, per-sequence block
+    counts and the bounds follow from the list."""
 
-    def __init__(self, batch, groups, device="cuda"):
+    def __init__(self, batch, groups, max_blocks=48, device="cuda"):
         i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=device)
+        cut = []
+        for members, lo, hi in groups:
+            for s in range(lo, hi, max_blocks):
+                cut.append((members, s, min(hi, s + max_blocks)))
+        groups = cut
         pb = [0] * batch
         depth = [0] * batch
         starts, seqs, blocks, gdepth = [0], [], [], []

@@ -299,9 +299,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // Cascade: one work-group per (sequence, query head) combines the row's own
-// splits (slots 0 .. its split count - 1) with the splits of the shared-block
-// groups it is in (slots nsplit + d * prefix_nsplit + k for depth d; empty
-// splits hold empty partials).
+// splits (slots 0 .. its split count - 1) with the partials of the
+// shared-block groups it is in (slot nsplit + d for the group at depth d).
 template <int D>
 __global__ __launch_bounds__(256) void cascade_merge_kernel(DecodeArgs a) {
   const int64_t row = blockIdx.x;
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(256) void cascade_merge_kernel(DecodeArgs a) {
   const int fb = a.first_blk[b];
   const int nblk = (T + 15) >> 4;
   const int own = nblk > fb ? (nblk - fb + a.split_blocks - 1) / a.split_blocks : 0;
-  const int pre = a.depth[b] * a.prefix_nsplit;
+  const int pre = a.depth[b];
   merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.part_stride, a.out_bf16}, row, own + pre,
                SlotsTwoRuns{own, a.nsplit});
 }

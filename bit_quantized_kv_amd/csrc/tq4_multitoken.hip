@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     tab_seq = a.group_seqs[q0];
     blk_lo = a.group_blocks[2 * b];
     T = 16 * a.group_blocks[2 * b + 1];
-    slot = a.slot0 + a.group_depth[b] * a.nsplit + sp;
+    slot = a.slot0 + a.group_depth[b];  // one split per group (split_blocks covers it)
   } else {
     q0 = a.q_start[b];
     M = a.q_start[b + 1] - q0;
@@ -293,8 +293,8 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   const int blk0 = blk_lo + sp * a.split_blocks;
   if (blk0 >= nblk) {
     if constexpr (PREFIX) {
-      // an empty split of the group: its rows get empty partials (max -inf,
-      // sum 0), which the merge weighs 0
+      // an empty group range: its rows get empty partials (max -inf, sum 0),
+      // which the merge weighs 0
       for (int i = threadIdx.x; i < RW * (D + 2); i += NW * 64) {
         const int row = row0 + i / (D + 2), c = i % (D + 2);
         if (row >= R) continue;

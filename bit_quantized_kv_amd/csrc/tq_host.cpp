@@ -18,6 +18,12 @@ struct tq_cache {
   tq::DeviceTables *tables;  // device
   tq::BinParams bins;
   uint16_t table_f16[16];
+  // cascade decode: a second stream (default priority) on which the
+  // shared-block pass runs beside the decode of the sequences' own tokens,
+  // forked from and joined to the caller's stream with two events; created on
+  // first use
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -408,9 +414,11 @@ tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads
   const int64_t rows = (int64_t)std::max(1, max_group_size) * g;
   p->rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
   p->row_tiles = (int)((rows + p->rows_per_wg - 1) / p->rows_per_wg);
-  p->prefix = tq::plan_split_multitoken((int64_t)std::max(1, num_groups) * hkv * p->row_tiles,
-                                        16 * max_group_blocks);
-  const int64_t stride = (int64_t)p->own.nsplit + (int64_t)(num_groups > 0 ? max_depth : 0) * p->prefix.nsplit;
+  // one split per group: a group is the unit of parallel work (callers cut
+  // long shared ranges into chained groups)
+  p->prefix.split_blocks = std::max(1, max_group_blocks);
+  p->prefix.nsplit = 1;
+  const int64_t stride = (int64_t)p->own.nsplit + (num_groups > 0 ? max_depth : 0);
   if (stride > (1 << 20)) return fail(TQ_ERR_INVALID_ARG, "too many partial slots per row");
   p->part_stride = (int)stride;
   return TQ_OK;
@@ -469,6 +477,12 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;
+  if (num_groups > 0 && !cache->aux) {
+    e = hipStreamCreateWithFlags(&cache->aux, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&cache->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&cache->join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "cascade stream set-up");
+  }
   if (num_groups > 0) {
     tq::MultiTokenArgs m{};
     m.q = static_cast<const uint16_t *>(q);
@@ -494,8 +508,13 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
     m.group_depth = group_depth;
     m.part_stride = p.part_stride;
     m.slot0 = p.own.nsplit;
-    e = tq::launch_prefix_attention(d, m, s);
+    e = hipEventRecord(cache->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cache->aux, cache->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "cascade fork");
+    e = tq::launch_prefix_attention(d, m, cache->aux);
     if (e != hipSuccess) return hip_fail(e, "shared-block attention launch");
+    e = hipEventRecord(cache->join, cache->aux);
+    if (e != hipSuccess) return hip_fail(e, "cascade join record");
   }
   tq::DecodeArgs a{};
   a.q = static_cast<const uint16_t *>(q);
@@ -519,9 +538,12 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
   a.first_blk = seq_prefix_blocks;
   a.depth = seq_depth;
   a.part_stride = p.part_stride;
-  a.prefix_nsplit = num_groups > 0 ? p.prefix.nsplit : 0;
   e = tq::launch_tq4_cascade_decode(d, a, s);
   if (e != hipSuccess) return hip_fail(e, "cascade decode launch");
+  if (num_groups > 0) {
+    e = hipStreamWaitEvent(s, cache->join, 0);
+    if (e != hipSuccess) return hip_fail(e, "cascade join");
+  }
   e = tq::launch_cascade_merge(d, a, s);
   if (e != hipSuccess) return hip_fail(e, "cascade merge launch");
   return TQ_OK;
@@ -591,6 +613,9 @@ tq_status tq_select_layers(const double *mse, int32_t num_layers, int32_t percen
 void tq_free(tq_cache *cache) {
   if (!cache) return;
   (void)hipDeviceSynchronize();
+  if (cache->fork) (void)hipEventDestroy(cache->fork);
+  if (cache->join) (void)hipEventDestroy(cache->join);
+  if (cache->aux) (void)hipStreamDestroy(cache->aux);
   if (cache->tables) (void)hipFree(cache->tables);
   if (cache->owns_pool && cache->pool) (void)hipFree(cache->pool);
   delete cache;

@@ -55,7 +55,6 @@ struct DecodeArgs {
   const int32_t *first_blk;      // [batch]
   const int32_t *depth;          // [batch]: shared-block groups the sequence is in
   int32_t part_stride;
-  int32_t prefix_nsplit;         // partial slots per group depth
 };
 
 struct MultiTokenArgs {
@@ -79,9 +78,9 @@ struct MultiTokenArgs {
   // groups instead of sequences (batch = number of groups, max_query_len =
   // largest group); group i's members are group_seqs[group_start[i] ..
   // group_start[i+1]), its shared blocks group_blocks[2i] .. group_blocks[2i+1]
-  // - 1 of its first member's table, its depth group_depth[i]; the partial
-  // of split sp goes to slot slot0 + depth * nsplit + sp of rows of
-  // part_stride slots (an empty split writes an empty partial)
+  // - 1 of its first member's table, its depth group_depth[i]; one split per
+  // group (split_blocks >= the largest group), whose partial goes to slot
+  // slot0 + depth of rows of part_stride slots
   const int32_t *group_start;
   const int32_t *group_seqs;
   const int32_t *group_blocks;

@@ -205,7 +205,10 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
  * the log-sum-exp merge.  Groups nest: the groups a sequence is in cover its
  * first P_b blocks contiguously, from block 0, in order of depth (the group
  * at depth d covers the blocks after those of depth d - 1); its own part is
- * tokens 16 P_b .. T_b - 1.
+ * tokens 16 P_b .. T_b - 1.  A group is one unit of parallel work (its
+ * blocks are walked by one work-group per kv-head and 16 / 32 / 64 / 128
+ * member rows), so callers cut long shared ranges into chained groups of a few
+ * dozen blocks.
  * Arguments as tq_decode_attention, plus (all device, trusted):
  *   seq_prefix_blocks  int32 [batch]: P_b (0 for a sequence in no group),
  *                      16 P_b <= context_lens[b]
@@ -220,7 +223,11 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
  *   max_depth in [1, num_groups]; 16 * max_group_blocks <= max_context_len.
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8.  workspace: device buffer
  * of at least tq_cascade_workspace_bytes (always needed).  MX-FP4 caches
- * return TQ_ERR_UNSUPPORTED.  Asynchronous. */
+ * return TQ_ERR_UNSUPPORTED.  Asynchronous: the shared-block pass runs on a
+ * second stream of the handle (created on first use, default priority),
+ * forked from `stream` and joined back to it by events before the merge, so
+ * the call is ordered on `stream` like the others; calls on one handle from
+ * several streams at once are not supported. */
 tq_status tq_cascade_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
                                      int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
                                      int32_t max_group_blocks, int32_t max_depth, size_t *bytes);
