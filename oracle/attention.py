@@ -155,7 +155,7 @@ def cascade_decode(pool, q, block_table, context_lens, scale, groups, rows=None)
 
 
 def rotated_query(pool, qrow):
-    if pool.fmt == paged.FORMAT_TQ4:
+    if pool.fmt in (paged.FORMAT_TQ4, paged.FORMAT_TQ4V2):
         return wht.wht_f64(qrow)
     return fp.e4m3_decode(mxfp4.query_fp8(qrow))
 

@@ -21,6 +21,14 @@ TQ4/4 record (D = 64 or 128), sections in this order:
                    sc(t, gp) at 2*((r*G + gp)*8 + tt),  mn(t, gp) at 2*((r*G + gp)*8 + 4 + tt)
   Record bytes: 2336 (D=128), 1184 (D=64)  = 16 * (D/2 + 2 + D/2 + G*4).
 
+TQ4/2 record (D = 64 or 128; 2-bit values), sections in this order:
+  Kc  16*P bytes  as TQ4/4
+  Ks  16*2 bytes  as TQ4/4
+  Vc2 16*P/2 B    2-bit value codes: channel 2p + par, p = 16*gp + j, of token
+                  t in byte ((r*16 + j)*(G/2) + gp//2)*4 + tt at bit 4*(gp%2) + 2*par
+  Vm  16*G*4 B    as TQ4/4
+  Record bytes: 1824 (D=128), 928 (D=64)  = 16 * (D/2 + 2 + D/4 + G*4).
+
 MX-FP4 record (D = 128 only), sections in this order:
   Kc4 16*P bytes  e2m1 key codes (rotated keys), same placement as Kc
   Ks4 16*G bytes  UE8M0 key exponents: group gp of token t at gp*16 + t
@@ -40,6 +48,11 @@ BLOCK = 16
 def tq4_record_bytes(d):
     _check_dim(d)
     return BLOCK * (d // 2 + 2 + d // 2 + (d // 32) * 4)
+
+
+def tq4v2_record_bytes(d):
+    _check_dim(d)
+    return BLOCK * (d // 2 + 2 + d // 4 + (d // 32) * 4)
 
 
 def mxfp4_record_bytes(d):
@@ -71,6 +84,18 @@ def vc_offset(t, p, d):
     return ((r * 16 + j) * g + gp) * 4 + tt
 
 
+def vc2_position(t, c, d):
+    """(byte offset in the Vc2 section, bit shift) of the 2-bit code of
+    channel c of token t."""
+    g = d // 32
+    t = np.asarray(t)
+    c = np.asarray(c)
+    r, tt = t // 4, t % 4
+    p, par = c // 2, c % 2
+    gp, j = p // 16, p % 16
+    return ((r * 16 + j) * (g // 2) + gp // 2) * 4 + tt, 4 * (gp % 2) + 2 * par
+
+
 def vm_offsets(t, gp, d):
     """(scale byte offset, min byte offset) of group gp of token t."""
     g = d // 32
@@ -98,6 +123,16 @@ def tq4_sections(d):
     ks = kc + p16
     vc = ks + 2 * BLOCK
     vm = vc + p16
+    return {"kc": kc, "ks": ks, "vc": vc, "vm": vm, "end": vm + BLOCK * (d // 32) * 4}
+
+
+def tq4v2_sections(d):
+    """Start byte of each section of a TQ4/2 record."""
+    p16 = BLOCK * (d // 2)
+    kc = 0
+    ks = kc + p16
+    vc = ks + 2 * BLOCK
+    vm = vc + p16 // 2
     return {"kc": kc, "ks": ks, "vc": vc, "vm": vm, "end": vm + BLOCK * (d // 32) * 4}
 
 
@@ -181,6 +216,55 @@ def tq4_read_block(rec, d):
         "vscale": f16_at(so),
         "vmin": f16_at(mo),
     }
+
+
+def tq4v2_write_rows(buf, base, t, d, kcode, kscale, vcode, vscale, vmin):
+    """TQ4/2 rows: as tq4_write_rows, with 2-bit value codes [n, D]."""
+    sec = tq4v2_sections(d)
+    base = np.asarray(base, dtype=np.int64).reshape(-1, 1)
+    n = base.shape[0]
+    t = np.asarray(t).reshape(n, 1)
+    p = np.arange(d // 2)[None, :]
+    buf[base + sec["kc"] + kc_offset(t, p, d)] = pack_nibbles(kcode).reshape(n, d // 2)
+    vcode = np.asarray(vcode, dtype=np.uint8).reshape(n, d)
+    if np.any(vcode > 3):
+        raise ValueError("codes must be 2-bit")
+    pos, shift = vc2_position(t, np.arange(d)[None, :], d)
+    pos = np.broadcast_to(base + sec["vc"] + pos, (n, d)).ravel()
+    shift = np.broadcast_to(shift, (n, d)).ravel()
+    # four codes of one token share a byte: assemble each byte, then store it
+    where, inv = np.unique(pos, return_inverse=True)
+    byte = np.zeros(where.shape, dtype=np.uint8)
+    np.bitwise_or.at(byte, inv, (vcode.ravel() << shift).astype(np.uint8))
+    buf[where] = byte
+    _put_f16(buf, (base + sec["ks"] + 2 * t).ravel(), np.asarray(kscale).reshape(n))
+    gp = np.arange(d // 32)[None, :]
+    so, mo = vm_offsets(t, gp, d)
+    _put_f16(buf, base + sec["vm"] + so, np.asarray(vscale).reshape(n, d // 32))
+    _put_f16(buf, base + sec["vm"] + mo, np.asarray(vmin).reshape(n, d // 32))
+
+
+def tq4v2_read_block(rec, d):
+    """As tq4_read_block for TQ4/2 records (2-bit value codes)."""
+    sec = tq4v2_sections(d)
+    rec = np.asarray(rec, dtype=np.uint8)
+    n = rec.shape[0]
+    t = np.arange(BLOCK)[:, None]
+    p = np.arange(d // 2)[None, :]
+    kb = rec[:, sec["kc"] + kc_offset(t, p, d)]
+    pos, shift = vc2_position(t, np.arange(d)[None, :], d)
+    vcode = (rec[:, sec["vc"] + pos] >> shift) & 3
+    ksb = rec[:, sec["ks"]:sec["ks"] + 2 * BLOCK].copy().view(np.float16).reshape(n, BLOCK)
+    g = d // 32
+    so, mo = vm_offsets(np.arange(BLOCK)[:, None], np.arange(g)[None, :], d)
+
+    def f16_at(off):
+        lo = rec[:, sec["vm"] + off].astype(np.uint16)
+        hi = rec[:, sec["vm"] + off + 1].astype(np.uint16)
+        return (lo | (hi << 8)).view(np.float16)
+
+    return {"kcode": unpack_nibbles(kb), "kscale": ksb, "vcode": vcode.astype(np.uint8),
+            "vscale": f16_at(so), "vmin": f16_at(mo)}
 
 
 def mxfp4_write_rows(buf, base, t, d, kcode, kexp, vcode, vexp):

@@ -22,6 +22,7 @@ from . import layout, mxfp4, tq4
 BLOCK = layout.BLOCK
 FORMAT_TQ4 = 0
 FORMAT_MXFP4 = 1
+FORMAT_TQ4V2 = 2     # 4-bit keys, 2-bit values
 
 
 class PagedPool:
@@ -30,8 +31,9 @@ class PagedPool:
         self.num_blocks = num_blocks
         self.hkv = num_kv_heads
         self.d = head_dim
-        if fmt == FORMAT_TQ4:
-            self.rec_bytes = layout.tq4_record_bytes(head_dim)
+        if fmt in (FORMAT_TQ4, FORMAT_TQ4V2):
+            self.rec_bytes = (layout.tq4_record_bytes(head_dim) if fmt == FORMAT_TQ4
+                              else layout.tq4v2_record_bytes(head_dim))
             if key_table_f16 is None:
                 from .lloyd_max import default_key_table_f16
                 key_table_f16 = default_key_table_f16()
@@ -58,6 +60,8 @@ class PagedPool:
             raise IndexError("slot outside the pool")
         if self.fmt == FORMAT_TQ4:
             enc = tq4.encode_rows(k, v, self.table)
+        elif self.fmt == FORMAT_TQ4V2:
+            enc = tq4.encode_rows(k, v, self.table, vlevels=3)
         else:
             enc = mxfp4.encode_rows(k, v)
         # a repeated slot keeps the later token
@@ -66,9 +70,10 @@ class PagedPool:
         flat = self.pool.reshape(-1)
         for h in range(self.hkv):
             base = (blk[sel] * self.hkv + h) * self.rec_bytes
-            if self.fmt == FORMAT_TQ4:
-                layout.tq4_write_rows(flat, base, row[sel], self.d, enc["kcode"][sel, h], enc["kscale"][sel, h],
-                                      enc["vcode"][sel, h], enc["vscale"][sel, h], enc["vmin"][sel, h])
+            if self.fmt in (FORMAT_TQ4, FORMAT_TQ4V2):
+                write = layout.tq4_write_rows if self.fmt == FORMAT_TQ4 else layout.tq4v2_write_rows
+                write(flat, base, row[sel], self.d, enc["kcode"][sel, h], enc["kscale"][sel, h],
+                      enc["vcode"][sel, h], enc["vscale"][sel, h], enc["vmin"][sel, h])
             else:
                 layout.mxfp4_write_rows(flat, base, row[sel], self.d, enc["kcode"][sel, h], enc["kexp"][sel, h],
                                         enc["vcode"][sel, h], enc["vexp"][sel, h])
@@ -82,8 +87,8 @@ class PagedPool:
             return np.zeros((0, self.d)), np.zeros((0, self.d))
         ids = np.asarray(block_row[:nblk], dtype=np.int64)
         recs = self.pool[ids, kv_head]
-        if self.fmt == FORMAT_TQ4:
-            sec = layout.tq4_read_block(recs, self.d)
+        if self.fmt in (FORMAT_TQ4, FORMAT_TQ4V2):
+            sec = (layout.tq4_read_block if self.fmt == FORMAT_TQ4 else layout.tq4v2_read_block)(recs, self.d)
             k = tq4.key_dequant_rot(sec["kcode"], sec["kscale"], self.table)
             v = tq4.value_dequant(sec["vcode"], sec["vscale"], sec["vmin"])
         else:

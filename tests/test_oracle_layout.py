@@ -97,3 +97,45 @@ def test_mxfp4_write_read_round_trip():
         assert np.array_equal(back["vcode"][i, i], vc[i])
         assert np.array_equal(back["kexp"][i, i], kx[i])
         assert np.array_equal(back["vexp"][i, i], vx[i])
+
+
+def test_tq4v2_sizes_and_hand_positions():
+    assert layout.tq4v2_record_bytes(128) == 1824 and layout.tq4v2_record_bytes(64) == 928
+    sec = layout.tq4v2_sections(128)
+    assert (sec["kc"], sec["ks"], sec["vc"], sec["vm"], sec["end"]) == (0, 1024, 1056, 1568, 1824)
+    # worked by hand (D = 128, G = 4): channel 0 of token 0 -> byte 0, bit 0;
+    # channel 1 -> bit 2; channel 64 (pair 32: gp 2, j 0) -> word 1 -> byte 4;
+    # token 5 (r 1, tt 1), channel 35 (pair 17: gp 1, j 1, odd) -> byte
+    # ((16 + 1) * 2 + 0) * 4 + 1 = 137, bit 4 + 2 = 6
+    assert tuple(map(int, layout.vc2_position(0, 0, 128))) == (0, 0)
+    assert tuple(map(int, layout.vc2_position(0, 1, 128))) == (0, 2)
+    assert tuple(map(int, layout.vc2_position(0, 64, 128))) == (4, 0)
+    assert tuple(map(int, layout.vc2_position(5, 35, 128))) == (137, 6)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_vc2_map_is_a_bijection(d):
+    t = np.arange(16)[:, None]
+    c = np.arange(d)[None, :]
+    pos, shift = layout.vc2_position(t, c, d)
+    slots = (pos * 8 + shift).ravel()
+    assert len(np.unique(slots)) == 16 * d
+    assert pos.min() == 0 and pos.max() == 16 * d // 4 - 1
+    assert set(np.unique(shift).tolist()) == {0, 2, 4, 6}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_tq4v2_write_read_round_trip(d):
+    rng = np.random.default_rng(41 + d)
+    n = 16
+    kc = rng.integers(0, 16, size=(n, d)).astype(np.uint8)
+    vc = rng.integers(0, 4, size=(n, d)).astype(np.uint8)
+    ks = rng.standard_normal(n).astype(np.float16)
+    vs = rng.standard_normal((n, d // 32)).astype(np.float16)
+    vm = rng.standard_normal((n, d // 32)).astype(np.float16)
+    buf = np.zeros(layout.tq4v2_record_bytes(d), np.uint8)
+    layout.tq4v2_write_rows(buf, np.zeros(n, np.int64), np.arange(n), d, kc, ks, vc, vs, vm)
+    out = layout.tq4v2_read_block(buf[None], d)
+    assert np.array_equal(out["kcode"][0], kc) and np.array_equal(out["vcode"][0], vc)
+    assert np.array_equal(out["kscale"][0], ks)
+    assert np.array_equal(out["vscale"][0], vs) and np.array_equal(out["vmin"][0], vm)

@@ -171,3 +171,34 @@ def test_value_rule_bounds_idempotence_and_exactness():
     assert np.array_equal(tq4.value_codes(vh.astype(np.float32), sc, mn), codes)
     ex, near = tq4.value_codes_exact(v, sc, mn)
     assert not np.any((ex != codes) & ~near)
+
+
+def test_hand_value_groups_2bit():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tq4_value2_hand.json")))
+    for case in g["cases"]:
+        v = np.full(32, case["pad"], dtype=np.float32)
+        v[:len(case["v"])] = case["v"]
+        codes, sc, mn = tq4.value_encode(v[None], levels=3)
+        assert float(sc[0, 0]) == case["sc"], case["name"]
+        assert float(mn[0, 0]) == case["mn"], case["name"]
+        want = np.full(32, case["pad_code"], dtype=np.uint8)
+        want[:len(case["codes"])] = case["codes"]
+        assert np.array_equal(codes[0], want), case["name"]
+
+
+def test_2bit_value_rule_bounds_and_exactness():
+    rng = np.random.default_rng(40)
+    v = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(rng.standard_normal((500, 128)).astype(np.float32)))
+    codes, sc, mn = tq4.value_encode(v, levels=3)
+    assert codes.max() <= 3
+    ex, near = tq4.value_codes_exact(v, sc, mn, levels=3)
+    assert np.array_equal(codes[~near], ex[~near])
+    vh = tq4.value_dequant(codes, sc, mn)
+    g = lambda a: a.reshape(500, 4, 32)
+    # inside the group's range the error is at most half a step (plus fp16 rounding of sc, mn)
+    err = np.abs(g(vh) - g(v)).max(-1)
+    assert np.all(err <= sc.astype(np.float64) * 0.5 * (1 + 1e-2) + np.abs(mn.astype(np.float64)) * 2 ** -10 + 1e-6)
+    # the group's extremes are reproduced up to the fp16 roundings
+    assert np.all(np.abs(g(vh).min(-1) - mn.astype(np.float64)) <= 1e-6)
