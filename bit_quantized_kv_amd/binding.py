@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libtq.so")
 
 TQ_FORMAT_TQ4 = 0
 TQ_FORMAT_MXFP4 = 1
+TQ_FORMAT_TQ4V2 = 2
 TQ_OUT_F32 = 0
 TQ_OUT_BF16 = 1
 

@@ -51,23 +51,40 @@ __device__ __forceinline__ half2v codes_f16(uint32_t bytes) {
   return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
 }
 
-template <int D>
+// Value-code words per lane: 4-bit, one per 32-channel group; 2-bit (TQ4/2),
+// one per group pair.
+template <int D, int VB>
+struct VTile {
+  typedef typename KTile<D>::T T;
+};
+template <>
+struct VTile<128, 2> {
+  typedef uint2 T;
+};
+template <>
+struct VTile<64, 2> {
+  typedef uint32_t T;
+};
+__device__ __forceinline__ uint32_t word(uint32_t v, int) { return v; }
+
+template <int D, int VB>
 struct Blk {
-  typename KTile<D>::T kq;  // key codes: this lane's A-operand bytes
-  uint2 ks;                 // key scales of tokens 4r .. 4r+3
-  typename KTile<D>::T vq;  // value codes: this lane's A-operand bytes
-  uint32_t vmw;             // one dword of the value (scale, min) tile; lane
-                            // (r, c) holds dword c of row r's 16*G bytes
+  typename KTile<D>::T kq;      // key codes: this lane's A-operand bytes
+  uint2 ks;                     // key scales of tokens 4r .. 4r+3
+  typename VTile<D, VB>::T vq;  // value codes: this lane's A-operand bytes
+  uint32_t vmw;                 // one dword of the value (scale, min) tile; lane
+                                // (r, c) holds dword c of row r's 16*G bytes
 };
 
-template <int D>
-__device__ __forceinline__ void load_blk(Blk<D> &o, const uint8_t *rec, int lane) {
+template <int D, int VB>
+__device__ __forceinline__ void load_blk(Blk<D, VB> &o, const uint8_t *rec, int lane) {
   constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
+  constexpr int VW = VB == 4 ? G : G / 2;  // value-code words per lane
+  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + 64 * 4 * VW;
   const int r = lane >> 4, c = lane & 15;
   o.kq = *reinterpret_cast<const typename KTile<D>::T *>(rec + lane * Q);
   o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
-  o.vq = *reinterpret_cast<const typename KTile<D>::T *>(rec + OFF_VC + lane * (4 * G));
+  o.vq = *reinterpret_cast<const typename VTile<D, VB>::T *>(rec + OFF_VC + lane * (4 * VW));
   o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
 }
 
@@ -78,8 +95,8 @@ __device__ __forceinline__ void load_blk(Blk<D> &o, const uint8_t *rec, int lane
 // earlier).
 // tail: the block is the partial last one of its sequence (rows past the
 // context are masked: -inf logits, zero value scale and minimum).
-template <int D, int GQ>
-__device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D / 32], const uint32_t *s_lut,
+template <int D, int GQ, int VB>
+__device__ __forceinline__ void do_block(const Blk<D, VB> &bk, const half8v (&bq)[D / 32], const uint32_t *s_lut,
                                          uint32_t *vm_slot, WaveState<2 * D / 32> &st, float lo_mask, int lane,
                                          int tok0, int T, bool tail, uint32_t vm_keep) {
   constexpr int G = D / 32, KS = D / 32;
@@ -144,10 +161,20 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
   const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
 #pragma unroll
   for (int gp = 0; gp < G; ++gp) {
-    const uint32_t w = word(bk.vq, gp);
     const uint4 vm = vm_row[gp];
-    // bytes = tokens 4r + 0..3 of one channel pair; low nibble = even channel
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // bytes = tokens 4r + 0..3 of one channel pair; lo / hi = the even / odd
+    // channel's codes, each alone in its byte (2-bit: the group pair's word,
+    // group 2w in bits 0-3 of each byte, 2w + 1 in bits 4-7)
+    uint32_t lo, hi;
+    if constexpr (VB == 4) {
+      const uint32_t w = word(bk.vq, gp);
+      lo = w & 0x0F0F0F0Fu;
+      hi = (w >> 4) & 0x0F0F0F0Fu;
+    } else {
+      const uint32_t w = word(bk.vq, gp >> 1) >> (4 * (gp & 1));
+      lo = w & 0x03030303u;
+      hi = (w >> 2) & 0x03030303u;
+    }
     const half2v sc01 = as_h2(vm.x), sc23 = as_h2(vm.y);
     const half2v mn01 = as_h2(vm.z), mn23 = as_h2(vm.w);
     const half2v e01 = __builtin_elementwise_fma(codes_f16<false>(lo), sc01, mn01);
@@ -161,11 +188,11 @@ __device__ __forceinline__ void do_block(const Blk<D> &bk, const half8v (&bq)[D 
   }
 }
 
-template <int D, int GQ, bool CASCADE>
+template <int D, int GQ, bool CASCADE, int VB = 4>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void tq4_decode_kernel(
     DecodeArgs a) {
   constexpr int G = D / 32, KS = D / 32;
-  constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
+  constexpr int REC = 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * G;
   constexpr int NW = kWaves;
 
   __shared__ uint32_t s_lut[256];
@@ -224,17 +251,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     const int ta = (T & 15) - (r0 + 2 * (w & 1)), tb = ta - 1;
     tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
   }
-  Blk<D> b0, b1, b2, b3;
+  Blk<D, VB> b0, b1, b2, b3;
   if (mine > 0) {
     // issued block by block, as the loop's refills are, so that the
     // compiler's wait counts inside the loop stay partial on its first pass
-    load_blk<D>(b0, rec_of(0), lane);
+    load_blk<D, VB>(b0, rec_of(0), lane);
     __asm__ volatile("" ::: "memory");
-    load_blk<D>(b1, rec_of(1), lane);
+    load_blk<D, VB>(b1, rec_of(1), lane);
     __asm__ volatile("" ::: "memory");
-    load_blk<D>(b2, rec_of(2), lane);
+    load_blk<D, VB>(b2, rec_of(2), lane);
     __asm__ volatile("" ::: "memory");
-    load_blk<D>(b3, rec_of(3), lane);
+    load_blk<D, VB>(b3, rec_of(3), lane);
   }
 
   // ---- LUT and the rotated, scaled query group (wave w < g rotates head w) ------
@@ -269,12 +296,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 
   // process buffer k (if it is one of this wave's blocks), then refill it
   uint32_t *vm_slot = s_vm[wv];
-  auto run = [&](Blk<D> &buf, int k) {
+  auto run = [&](Blk<D, VB> &buf, int k) {
     if (k < mine) {
       const int blk = blk0 + wv + k * NW;
-      do_block<D, GQ>(buf, bq, s_lut, vm_slot, st, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk, tail_keep);
+      do_block<D, GQ, VB>(buf, bq, s_lut, vm_slot, st, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk,
+                          tail_keep);
     }
-    load_blk<D>(buf, rec_of(k + 4), lane);
+    load_blk<D, VB>(buf, rec_of(k + 4), lane);
   };
 #pragma unroll 1
   for (int k = 0; k < mine; k += 4) {
@@ -314,15 +342,15 @@ __global__ __launch_bounds__(256) void cascade_merge_kernel(DecodeArgs a) {
                SlotsTwoRuns{own, a.nsplit});
 }
 
-template <int D, bool CASCADE>
+template <int D, bool CASCADE, int VB = 4>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kWaves * 64);
   switch (a.g) {
-    case 1: hipLaunchKernelGGL((tq4_decode_kernel<D, 1, CASCADE>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((tq4_decode_kernel<D, 2, CASCADE>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((tq4_decode_kernel<D, 4, CASCADE>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((tq4_decode_kernel<D, 8, CASCADE>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((tq4_decode_kernel<D, 1, CASCADE, VB>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((tq4_decode_kernel<D, 2, CASCADE, VB>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((tq4_decode_kernel<D, 4, CASCADE, VB>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((tq4_decode_kernel<D, 8, CASCADE, VB>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -330,7 +358,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_tq4_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s) {
+  if (vbits == 2) return d == 128 ? launch_d<128, false, 2>(a, s) : launch_d<64, false, 2>(a, s);
   return d == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }
 

@@ -1,4 +1,4 @@
-// TQ4/4 quantize-and-append kernel for gfx950.
+// TQ4/4 (and TQ4/2) quantize-and-append kernel for gfx950.
 //
 // Keys: Walsh-Hadamard rotation, per-(token, kv-head) RMS scale, nearest entry
 // of a 16-entry table; values: per-32-channel asymmetric uniform 4-bit codes
@@ -46,13 +46,16 @@ __device__ __forceinline__ uint32_t key_scale_exact(const uint4 &k0, const uint4
 
 // Quantize one token row held by the LPT lanes of this lane's token and write
 // its codes and scales into the record of (slot / 16, h).
-template <int D>
+// VB: value code bits, 4 (TQ4/4) or 2 (TQ4/2: 2-bit values, the same
+// per-group rule with 3 levels; four codes of one token per byte).
+template <int D, int VB>
 __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoad<D> &cur, int h, int lane,
                                              int li, int tq, const float2 *s_bins,
                                              const float *s_recip, float bin_a, float bin_b, float sigma) {
   constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
+  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + (VB == 4 ? P16 : P16 / 2);
   constexpr int REC = OFF_VM + 64 * G;
+  constexpr float LEVELS = VB == 4 ? 15.f : 3.f;
   const int slot = cur.valid ? cur.slot : -1;
   // ---- key scale: fp32 sum of squares, exact fp16 RMS -------------------------
   float ss = 0.f;
@@ -113,16 +116,16 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
   mn = __builtin_fminf(mn, xor1(mn));
   mx = __builtin_fmaxf(mx, xor1(mx));
   const float range = mx - mn;
-  const float qs = range * (1.0f / 15.0f);  // within 2 ulps of fp32(range / 15)
+  const float qs = range * (1.0f / LEVELS);  // within 2 ulps of fp32(range / levels)
   uint32_t scb = h_bits((_Float16)qs);
-  if (!(qs == 0.f || f16_round_safe(qs, 4))) scb = h_bits(f16_sat(__fdiv_rn(range, 15.0f)));
+  if (!(qs == 0.f || f16_round_safe(qs, 4))) scb = h_bits(f16_sat(__fdiv_rn(range, LEVELS)));
   const _Float16 mn16 = (_Float16)__builtin_amdgcn_fmed3f(mn, -65504.0f, 65504.0f);  // saturating RNE
   const float mnv = (float)mn16;
   const float inv_sc = recip_f16(scb, s_recip);
   uint32_t ve0 = 0, ve1 = 0, vo0 = 0, vo1 = 0;  // bytes: even / odd channels
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float qv = __builtin_amdgcn_fmed3f((v[e] - mnv) * inv_sc, 0.f, 15.f);
+    const float qv = __builtin_amdgcn_fmed3f((v[e] - mnv) * inv_sc, 0.f, LEVELS);
     const int bsel = (e & 7) >> 1;
     if (e < 8) {
       if (e & 1) vo0 = __builtin_amdgcn_cvt_pk_u8_f32(qv, bsel, vo0);
@@ -132,7 +135,21 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
       else ve1 = __builtin_amdgcn_cvt_pk_u8_f32(qv, bsel, ve1);
     }
   }
-  const uint32_t vc0 = ve0 | (vo0 << 4), vc1 = ve1 | (vo1 << 4);  // pairs 0..3, 4..7 of this lane
+  // byte k: pair k's codes (pairs 0..3, 4..7 of this lane).  4-bit: even |
+  // odd << 4.  2-bit: even | odd << 2 in the low nibble, and the same nibble of
+  // the other group of the group pair (lane li ^ 2) in the high nibble, so both
+  // lanes hold the full bytes (group 2w in the low nibble)
+  uint32_t vc0, vc1;
+  if constexpr (VB == 4) {
+    vc0 = ve0 | (vo0 << 4);
+    vc1 = ve1 | (vo1 << 4);
+  } else {
+    const uint32_t n0 = ve0 | (vo0 << 2), n1 = ve1 | (vo1 << 2);
+    const uint32_t p0 = xor2u(n0), p1 = xor2u(n1);
+    const bool odd_group = (li & 2) != 0;
+    vc0 = odd_group ? (p0 | (n0 << 4)) : (n0 | (p0 << 4));
+    vc1 = odd_group ? (p1 | (n1 << 4)) : (n1 | (p1 << 4));
+  }
 
   // ---- placement ----------------------------------------------------------------------
   const bool aligned = quad_aligned<D>(slot, tq);
@@ -148,10 +165,16 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
     *reinterpret_cast<uint2 *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = make_uint2(kc0, kc1);
     if (li == 0) *reinterpret_cast<uint16_t *>(rec + OFF_KS + 2 * t) = (uint16_t)sb;
     const int r = t >> 2, gp = li >> 1, j0 = 8 * (li & 1);
+    // value-code word of pair j: 4-bit, one per group; 2-bit, one per group pair
+    constexpr int VW = VB == 4 ? G : G / 2;
+    const int wi = VB == 4 ? gp : gp >> 1;
+    const bool v_store = VB == 4 || (li & 2) == 0;
     if (aligned) {
       // lane tq writes the quad's bytes of channel pairs j0 + tq and j0 + 4 + tq
-      *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + tq) * G + gp) * 4) = vt0;
-      *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + 4 + tq) * G + gp) * 4) = vt1;
+      if (v_store) {
+        *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + tq) * VW + wi) * 4) = vt0;
+        *reinterpret_cast<uint32_t *>(rec + OFF_VC + ((r * 16 + j0 + 4 + tq) * VW + wi) * 4) = vt1;
+      }
       if ((li & 1) == 0 && (tq & 1) == 0) {
         // tokens tq, tq + 1: their scales form one dword, their minima another
         uint8_t *vm = rec + OFF_VM + (r * G + gp) * 16;
@@ -160,9 +183,11 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
       }
     } else {
       const int tt = t & 3;
+      if (v_store) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        rec[OFF_VC + ((r * 16 + j0 + k) * G + gp) * 4 + tt] = (uint8_t)((k < 4 ? vc0 : vc1) >> (8 * (k & 3)));
+        for (int k = 0; k < 8; ++k)
+          rec[OFF_VC + ((r * 16 + j0 + k) * VW + wi) * 4 + tt] = (uint8_t)((k < 4 ? vc0 : vc1) >> (8 * (k & 3)));
+      }
       if ((li & 1) == 0) {
         uint16_t *vm = reinterpret_cast<uint16_t *>(rec + OFF_VM) + (r * G + gp) * 8;
         vm[tt] = (uint16_t)scb;
@@ -172,7 +197,7 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
   }
 }
 
-template <int D>
+template <int D, int VB>
 __global__ __launch_bounds__(kQuantThreads) void tq4_quantize_kernel(QuantizeArgs a) {
   using L = QLanes<D>;
   __shared__ float2 s_bins[kMaxBins];
@@ -190,7 +215,7 @@ __global__ __launch_bounds__(kQuantThreads) void tq4_quantize_kernel(QuantizeArg
                      __syncthreads();
                    },
                    [&](const RowLoad<D> &row, int h) {
-                     quantize_row<D>(a, row, h, lane, li, tq, s_bins, s_recip, bin_a, bin_b, sigma);
+                     quantize_row<D, VB>(a, row, h, lane, li, tq, s_bins, s_recip, bin_a, bin_b, sigma);
                    });
 }
 
@@ -213,16 +238,17 @@ int quantize_grid(const void *kernel, int threads, int64_t tasks) {
   return (int)(tasks < cap ? tasks : cap);
 }
 
-hipError_t launch_tq4_quantize(int d, const QuantizeArgs &a, hipStream_t s) {
+template <int D, int VB>
+void launch_q(const QuantizeArgs &a, int64_t tasks, hipStream_t s) {
+  const int grid = quantize_grid((const void *)tq4_quantize_kernel<D, VB>, kQuantThreads, tasks);
+  hipLaunchKernelGGL((tq4_quantize_kernel<D, VB>), dim3(grid), dim3(kQuantThreads), 0, s, a);
+}
+
+hipError_t launch_tq4_quantize(int d, int vbits, const QuantizeArgs &a, hipStream_t s) {
   if (a.num_tokens <= 0) return hipSuccess;
   const int64_t tasks = quantize_tasks(d, a.num_tokens, a.hkv);
-  if (d == 128) {
-    const int grid = quantize_grid((const void *)tq4_quantize_kernel<128>, kQuantThreads, tasks);
-    hipLaunchKernelGGL(tq4_quantize_kernel<128>, dim3(grid), dim3(kQuantThreads), 0, s, a);
-  } else {
-    const int grid = quantize_grid((const void *)tq4_quantize_kernel<64>, kQuantThreads, tasks);
-    hipLaunchKernelGGL(tq4_quantize_kernel<64>, dim3(grid), dim3(kQuantThreads), 0, s, a);
-  }
+  if (d == 128) vbits == 4 ? launch_q<128, 4>(a, tasks, s) : launch_q<128, 2>(a, tasks, s);
+  else vbits == 4 ? launch_q<64, 4>(a, tasks, s) : launch_q<64, 2>(a, tasks, s);
   return hipGetLastError();
 }
 

@@ -45,10 +45,10 @@ tq_status check_desc(const tq_cache_desc *d, size_t *record) {
   if (d->num_kv_heads < 1 || d->num_kv_heads > 65536)
     return fail(TQ_ERR_INVALID_ARG, "num_kv_heads must be in [1, 65536]");
   if (d->num_blocks < 1) return fail(TQ_ERR_INVALID_ARG, "num_blocks must be >= 1");
-  if (d->format == TQ_FORMAT_TQ4) {
+  if (d->format == TQ_FORMAT_TQ4 || d->format == TQ_FORMAT_TQ4V2) {
     if (d->head_dim != 64 && d->head_dim != 128)
-      return fail(TQ_ERR_UNSUPPORTED, "TQ4/4 supports head_dim 64 and 128");
-    *record = tq::tq4_record_bytes(d->head_dim);
+      return fail(TQ_ERR_UNSUPPORTED, "TQ4/4 and TQ4/2 support head_dim 64 and 128");
+    *record = d->format == TQ_FORMAT_TQ4 ? tq::tq4_record_bytes(d->head_dim) : tq::tq4v2_record_bytes(d->head_dim);
   } else if (d->format == TQ_FORMAT_MXFP4) {
     if (d->head_dim != 128) return fail(TQ_ERR_UNSUPPORTED, "MX-FP4 supports head_dim 128");
     if (d->key_table) return fail(TQ_ERR_INVALID_ARG, "MX-FP4 takes no key table");
@@ -120,7 +120,7 @@ tq_status tq_create_cache(const tq_cache_desc *desc, void *pool, size_t pool_byt
   c.record_bytes = rec;
   c.pool_bytes = need;
   tq::DeviceTables host_tables{};
-  if (desc->format == TQ_FORMAT_TQ4) {
+  if (desc->format != TQ_FORMAT_MXFP4) {
     if (desc->key_table) {
       for (int i = 0; i < 16; ++i) {
         if (!std::isfinite(desc->key_table[i])) return fail(TQ_ERR_INVALID_ARG, "key table entries must be finite");
@@ -194,7 +194,8 @@ tq_status tq_quantize_append(tq_cache *cache, const void *k, const void *v, cons
   a.bins = cache->bins;
   a.rsqrt_d = (float)(1.0 / std::sqrt((double)cache->desc.head_dim));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = cache->desc.format == TQ_FORMAT_TQ4 ? tq::launch_tq4_quantize(cache->desc.head_dim, a, s)
+  hipError_t e = cache->desc.format != TQ_FORMAT_MXFP4
+                     ? tq::launch_tq4_quantize(cache->desc.head_dim, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, s)
                                                       : tq::launch_mxfp4_quantize(a, s);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return TQ_OK;
@@ -253,7 +254,7 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
   }
   const double log2e = 1.4426950408889634074;
   a.rsqrt_d = (float)(1.0 / std::sqrt((double)d));
-  a.qscale = cache->desc.format == TQ_FORMAT_TQ4
+  a.qscale = cache->desc.format != TQ_FORMAT_MXFP4
                  ? (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)))
                  : (float)((double)softmax_scale * log2e);
   a.max_blocks = max_blocks;
@@ -265,7 +266,8 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
   a.nsplit = p.nsplit;
   a.out_bf16 = out_dtype == TQ_OUT_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = cache->desc.format == TQ_FORMAT_TQ4 ? tq::launch_tq4_decode(d, a, s) : tq::launch_mxfp4_decode(a, s);
+  hipError_t e = cache->desc.format == TQ_FORMAT_MXFP4 ? tq::launch_mxfp4_decode(a, s)
+                 : tq::launch_tq4_decode(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p.nsplit > 1) {
     e = tq::launch_decode_merge(d, a, s);

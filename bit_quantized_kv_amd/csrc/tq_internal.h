@@ -89,8 +89,8 @@ struct MultiTokenArgs {
 };
 
 // Launchers (defined next to their kernels).
-hipError_t launch_tq4_quantize(int d, const QuantizeArgs &a, hipStream_t s);
-hipError_t launch_tq4_decode(int d, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_tq4_quantize(int d, int vbits, const QuantizeArgs &a, hipStream_t s);
+hipError_t launch_tq4_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
@@ -113,6 +113,7 @@ bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *
 
 // Record sizes.
 inline size_t tq4_record_bytes(int d) { return (size_t)16 * (d / 2 + 2 + d / 2 + (d / 32) * 4); }
+inline size_t tq4v2_record_bytes(int d) { return (size_t)16 * (d / 2 + 2 + d / 4 + (d / 32) * 4); }
 inline size_t mxfp4_record_bytes(int d) { return (size_t)16 * (d / 2 + d / 32 + d / 2 + d / 32); }
 
 // Split-K plan shared by the workspace query and the launch.

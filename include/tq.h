@@ -45,6 +45,17 @@
  *     Vm  64*G B   sc(t,gp) at 2*((r*G + gp)*8 + tt),
  *                  mn(t,gp) at 2*((r*G + gp)*8 + 4 + tt)
  *
+ * TQ4/2 (format 2, D = 64 or 128; [TQ-AMD] section 2 names 2-bit variants as
+ * feasible): keys as TQ4/4; values by the same per-group rule with 2-bit codes:
+ *   sc = fp16_sat(fp32(fp32(max - min) / 3)), code = clamp(RNE(fp32(fp32(v -
+ *   mn) * fp32(1/sc))), 0, 3); v_hat = code * sc + mn.
+ *   record (1824 B at D = 128, 928 B at D = 64): Kc, Ks as TQ4/4, then
+ *     Vc2 8*P B    channel 2p + par, p = 16*gp + j, of token t: byte
+ *                  ((r*16 + j)*(G/2) + gp/2)*4 + tt, bits 4*(gp%2) + 2*par
+ *     Vm  64*G B   as TQ4/4
+ *   Supported by tq_quantize_append and tq_decode_attention (multi-token and
+ *   cascade attention return TQ_ERR_UNSUPPORTED).
+ *
  * MX-FP4 (format 1, D = 128).  Per (token, kv-head), groups of 32 channels:
  *   keys are rotated first, y = fp32(x * fp32(1/sqrt(D))), an exactly zero y
  *   stored as +0; values are not rotated (their zeros keep their sign).
@@ -84,12 +95,12 @@ typedef enum tq_status {
   TQ_ERR_HIP = 5           /* a HIP runtime call failed (see tq_last_error)     */
 } tq_status;
 
-typedef enum tq_format { TQ_FORMAT_TQ4 = 0, TQ_FORMAT_MXFP4 = 1 } tq_format;
+typedef enum tq_format { TQ_FORMAT_TQ4 = 0, TQ_FORMAT_MXFP4 = 1, TQ_FORMAT_TQ4V2 = 2 } tq_format;
 typedef enum tq_out_dtype { TQ_OUT_F32 = 0, TQ_OUT_BF16 = 1 } tq_out_dtype;
 
 typedef struct tq_cache_desc {
   int32_t format;          /* tq_format                                          */
-  int32_t head_dim;        /* TQ4: 64 or 128; MX-FP4: 128                         */
+  int32_t head_dim;        /* TQ4/4, TQ4/2: 64 or 128; MX-FP4: 128                */
   int32_t num_kv_heads;    /* 1 .. 65536                                          */
   int32_t block_size;      /* must be 16                                          */
   int64_t num_blocks;      /* >= 1                                                */

@@ -111,7 +111,7 @@ def describe_record_diff(gpu_rec, ora_rec, d, fmt=0):
     """Text naming the sections, token rows and values of differing bytes."""
     from oracle import layout
     idx = np.nonzero(gpu_rec != ora_rec)[0]
-    sec = layout.tq4_sections(d) if fmt == 0 else layout.mxfp4_sections(d)
+    sec = {0: layout.tq4_sections, 1: layout.mxfp4_sections, 2: layout.tq4v2_sections}[fmt](d)
     names = sorted(((v, k) for k, v in sec.items() if k != "end"))
     out = []
     for i in idx[:24]:
