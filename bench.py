@@ -44,10 +44,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="llama8b",
-                   choices=["llama8b", "agentic", "longprefix", "fp4", "calib", "verify", "prefill", "cascade"],
+                   choices=["llama8b", "agentic", "longprefix", "fp4", "tq4v2", "calib", "verify", "prefill",
+                            "cascade"],
                    help="calib: the calibrated key-table fit of a 32-layer stack; verify / prefill: multi-token "
                         "attention over the cache; cascade: the agentic workload decoded with shared blocks "
-                        "read once per group (each its own JSON line)")
+                        "read once per group; tq4v2: the llama8b shape with 2-bit values (each its own JSON line)")
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
     p.add_argument("--cascade-group-blocks", type=int, default=48,
                    help="cascade: shared ranges are cut into groups of at most this many blocks")
@@ -193,7 +194,7 @@ class Bench:
             self.decode(dc, s)
 
 
-def cpu_baseline(cfg_name, budget_s=10.0):
+def cpu_baseline(cfg, budget_s=10.0):
     """The CPU oracle, as it stands, on a bounded sample of the workload:
     (sequence, kv-head) units in order, each quantized and then decoded for
     its g query heads, until about ``budget_s`` seconds of CPU work."""
@@ -203,7 +204,7 @@ def cpu_baseline(cfg_name, budget_s=10.0):
         threadpool_limits = None
     import workloads
     from oracle import attention, paged
-    w = workloads.make(cfg_name)
+    w = workloads.make(cfg)
     c = w.cfg
     g = c.num_q_heads // c.num_kv_heads
     lens = w.context_lens_at(0)
@@ -237,15 +238,14 @@ def cpu_baseline(cfg_name, budget_s=10.0):
     finally:
         if ctx_mgr:
             ctx_mgr.__exit__(None, None, None)
-    row = 146 if c.head_dim == 128 else 74
-    if c.fmt == 1:
-        row = 136
+    d = c.head_dim
+    row = {0: d + 2 + d // 8, 1: d + d // 16, 2: 3 * d // 4 + 2 + d // 8}[c.fmt]   # bytes per token-head
     return {
         "value": toks * row / td / 1e9,
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{cfg_name}: {units} (sequence, kv-head) units, {toks} token-heads: quantize {tq:.2f} s, "
+        "sample": f"{c.name}: {units} (sequence, kv-head) units, {toks} token-heads: quantize {tq:.2f} s, "
                   f"decode of their {g} query heads each {td:.2f} s (numpy fp64, BLAS limited to 1 thread)",
         "quantize_tokens_per_s": toks / tq / c.num_kv_heads,
     }
@@ -270,7 +270,12 @@ def traffic_from_profiles(cfg_name, kernel):
         if kernel == "quantize":
             cands = [(int(k.split("|")[1]), e) for k, e in ents.items() if "quantize_kernel" in k]
             return round(hbm(max(cands, key=lambda x: x[0])[1])) if cands else None
-        parts = [e for k, e in ents.items() if "decode" in k]
+        if kernel == "multitoken":
+            parts = [e for k, e in ents.items() if "multitoken" in k]
+        else:
+            # the decode launch: decode kernel and merge, and for cascade decode
+            # the shared-block pass too
+            parts = [e for k, e in ents.items() if "quantize_kernel" not in k]
         return round(sum(hbm(e) for e in parts)) if parts else None
     except Exception:
         return None
@@ -516,7 +521,8 @@ def bench_multitoken(args):
         ach = byts / (a_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4)}
-    roof.update({"traffic": None, "kernel": "multitoken", "bytes_per_launch": byts, "flops_per_launch": flops,
+    roof.update({"traffic": traffic_from_profiles(args.config, "multitoken"), "kernel": "multitoken",
+                 "bytes_per_launch": byts, "flops_per_launch": flops,
                  "avg_launch_us": round(a_ms * 1e3, 2)})
     nq = int(mb.q.shape[0])
     res = {
@@ -610,7 +616,12 @@ def main():
     torch.cuda.set_device(0)
     cascade = args.config == "cascade"
     cfg_name = "agentic" if cascade else args.config
-    bench = Bench(workloads.CONFIGS[cfg_name], args.copies, cascade=cascade, group_blocks=args.cascade_group_blocks)
+    if args.config == "tq4v2":
+        import dataclasses
+        cfg = dataclasses.replace(workloads.CONFIGS["llama8b"], name="tq4v2", fmt=2)
+    else:
+        cfg = workloads.CONFIGS[cfg_name]
+    bench = Bench(cfg, args.copies, cascade=cascade, group_blocks=args.cascade_group_blocks)
     c = bench.cfg
     stream = bench.stream
     for i in range(args.warmup + bench.pool_copies):
@@ -642,7 +653,7 @@ def main():
         k = kernels[name]
         return {"bound": "hbm", "achieved": round(k["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(k["GBps"] / HBM_PEAK_GBPS, 4),
-                "traffic": None if cascade and name == "decode" else traffic_from_profiles(cfg_name, name),
+                "traffic": traffic_from_profiles(args.config, name),
                 "kernel": name, "bytes_per_launch": k["bytes"], "avg_launch_us": round(k["avg_us"], 2)}
 
     res = {
@@ -660,7 +671,7 @@ def main():
         "data": "synthetic (seeded; shapes of the pages' agentic workloads)",
         "config": {"workload": f"{c.name}: batch {c.batch}, {c.num_q_heads}/{c.num_kv_heads} heads, "
                                f"head_dim {c.head_dim}, context {int(bench.w.context_lens_at(0).max())}, "
-                               f"format {'TQ4/4' if c.fmt == 0 else 'MX-FP4'}"
+                               f"format {['TQ4/4', 'MX-FP4', 'TQ4/2'][c.fmt]}"
                                + (f", cascade decode over {bench.cascade.num_groups} nested groups of shared blocks"
                                   if cascade else ""),
                    "tokens_quantized_per_step": bench.n_tokens, "decode_steps_per_step": c.decode_steps,
@@ -674,7 +685,7 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg_name)
+        res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res))
 
 
