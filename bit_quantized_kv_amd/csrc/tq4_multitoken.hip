@@ -72,12 +72,14 @@ __device__ __forceinline__ void mt_load_blk(MtBlk<D> &o, const uint8_t *rec, int
   o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
 }
 
-// LDS image of one dequantized block (per lane: its MFMA A operands).
+// LDS image of a pair of dequantized blocks (per lane: its MFMA A operands).
+// The PV operand of a lane holds its 4 values of the first block, then its 4
+// of the second, so one 16-byte read gives the 32-token operand.
 template <int D>
-struct MtSlot {
-  uint4 k[D / 32][64];   // QK A operand of k-step s: 8 fp16 table entries
-  uint2 v[D / 16][64];   // PV A operand of tile t: 4 fp16 values
-  uint2 ks[4];           // fp16 key scales of tokens 4r .. 4r+3
+struct MtPair {
+  uint4 k[2][D / 32][64];  // QK A operand of block h, k-step s: 8 fp16 table entries
+  uint4 v[D / 16][64];     // PV A operand of tile t: 4 + 4 fp16 values
+  uint2 ks[2][4];          // fp16 key scales of tokens 4r .. 4r+3 of block h
 };
 
 struct MtTask {
@@ -98,10 +100,14 @@ __device__ __forceinline__ MtTask mt_task(const MultiTokenArgs &a) {
   return t;
 }
 
-// Producer: dequantize this wave's loaded block into its LDS slot.
+// Producer: dequantize this wave's loaded block into half `half` of its LDS
+// pair; `lone`: the block is the last of the stage and unpaired, so the other
+// half's values are cleared (their probabilities are 0, and 0 * NaN would
+// not be).
 template <int D>
-__device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtSlot<D> &slot, const uint32_t *s_lut,
-                                           uint32_t *vm_slot, int lane, bool tail, uint32_t vm_keep) {
+__device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtPair<D> &slot, int half, bool lone,
+                                           const uint32_t *s_lut, uint32_t *vm_slot, int lane, bool tail,
+                                           uint32_t vm_keep) {
   constexpr int G = D / 32, KS = D / 32;
   uint32_t vmw = bk.vmw;
   if (tail) {
@@ -117,9 +123,9 @@ __device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtSlot<D> &slot, 
     e.y = s_lut[(w >> 8) & 0xFF];
     e.z = s_lut[(w >> 16) & 0xFF];
     e.w = s_lut[w >> 24];
-    slot.k[s][lane] = e;
+    slot.k[half][s][lane] = e;
   }
-  if ((lane & 15) == 0) slot.ks[lane >> 4] = bk.ks;
+  if ((lane & 15) == 0) slot.ks[half][lane >> 4] = bk.ks;
   const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
 #pragma unroll
   for (int gp = 0; gp < G; ++gp) {
@@ -132,8 +138,15 @@ __device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtSlot<D> &slot, 
     const half2v e23 = __builtin_elementwise_fma(mt_codes_f16<true>(lo), sc23, mn23);
     const half2v o01 = __builtin_elementwise_fma(mt_codes_f16<false>(hi), sc01, mn01);
     const half2v o23 = __builtin_elementwise_fma(mt_codes_f16<true>(hi), sc23, mn23);
-    slot.v[2 * gp][lane] = make_uint2(as_u(e01), as_u(e23));
-    slot.v[2 * gp + 1][lane] = make_uint2(as_u(o01), as_u(o23));
+    uint2 *ve = reinterpret_cast<uint2 *>(&slot.v[2 * gp][lane]);
+    uint2 *vo = reinterpret_cast<uint2 *>(&slot.v[2 * gp + 1][lane]);
+    ve[half] = make_uint2(as_u(e01), as_u(e23));
+    vo[half] = make_uint2(as_u(o01), as_u(o23));
+    if (lone) {
+      __asm__ volatile("");
+      ve[1] = make_uint2(0u, 0u);
+      vo[1] = make_uint2(0u, 0u);
+    }
   }
 }
 
@@ -141,8 +154,12 @@ __device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtSlot<D> &slot, 
 // each block, column n = lane % 16), with the lazy rescale of softmax_block.
 template <int NT>
 __device__ __forceinline__ void mt_softmax8(const float (&x)[8], WaveState<NT> &st, float (&p)[8]) {
-  float lm = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), __builtin_fmaxf(x[2], x[3])),
-                             __builtin_fmaxf(__builtin_fmaxf(x[4], x[5]), __builtin_fmaxf(x[6], x[7])));
+  // v_max3 written out: the logits need no canonicalizing first
+  float lm;
+  __asm__("v_max3_f32 %0, %1, %2, %3\n\tv_max3_f32 %0, %0, %4, %5\n\tv_max3_f32 %0, %0, %6, %7\n\t"
+          "v_max_f32 %0, %0, %8"
+          : "=&v"(lm)
+          : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
   if (__builtin_amdgcn_ballot_w64(lm > st.m + kLazyRescale) != 0) {
     float bm = __builtin_fmaxf(lm, xor16(lm));
     bm = __builtin_fmaxf(bm, xor32(bm));
@@ -159,106 +176,116 @@ __device__ __forceinline__ void mt_softmax8(const float (&x)[8], WaveState<NT> &
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// Consumer: this wave's 16 rows against a pair of blocks A, B (B = A with
-// has_b false: a lone last block, whose second half gets p = 0).  The PV
-// product contracts over the 32 tokens of the pair on v_mfma_f32_16x16x32_f16:
-// operand index 8r + j is token 4r + j of block A for j < 4, token 4r + j - 4
-// of block B otherwise, which is how both the QK accumulators (B operand) and
-// the LDS value slots (A operand) already hold them.  lim: this lane's
-// column's visible-key count; masked: the pair reaches past some column's
-// limit.
-template <int D>
-__device__ __forceinline__ void mt_consume_pair(const MtSlot<D> &sa, const MtSlot<D> &sb, bool has_b,
-                                                const half8v (&bq_hi)[D / 32], const half8v (&bq_lo)[D / 32],
-                                                WaveState<D / 16> &st, int lane, int tok0, int lim,
-                                                bool masked) {
+// Consumer: this wave's TR tiles of 16 rows against a pair of blocks (has_b
+// false: a lone last block, whose second half gets p = 0).  The PV product
+// contracts over the pair's 32 tokens on v_mfma_f32_16x16x32_f16: operand
+// index 8r + j is token 4r + j of the first block for j < 4 and token
+// 4r + j - 4 of the second, which is how both the QK accumulators (B operand)
+// and the LDS value slots (A operand) hold them.  Every LDS operand read feeds
+// all TR tiles, and the tiles' and blocks' MFMA chains are independent and
+// interleaved.  lim[t]: this lane's column's visible-key count in tile t;
+// masked: the pair reaches past some column's limit.
+template <int D, int TR>
+__device__ __forceinline__ void mt_consume_pair(const MtPair<D> &sp, bool has_b,
+                                                const half8v (&bq_hi)[TR][D / 32],
+                                                const half8v (&bq_lo)[TR][D / 32], WaveState<D / 16> (&st)[TR],
+                                                int lane, int tok0, const int (&lim)[TR], bool masked) {
   constexpr int KS = D / 32, NT = D / 16;
   const int r = lane >> 4;
-  float4v qa = (float4v){0.f, 0.f, 0.f, 0.f}, qb = qa;
+  float4v qa[TR], qb[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) qa[t] = qb[t] = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const half8v ka = __builtin_bit_cast(half8v, sa.k[s][lane]);
-    qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_hi[s], qa, 0, 0, 0);
-    qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_lo[s], qa, 0, 0, 0);
-  }
-  if (has_b) {
+    const half8v ka = __builtin_bit_cast(half8v, sp.k[0][s][lane]);
+    const half8v kb = __builtin_bit_cast(half8v, sp.k[1][s][lane]);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const half8v kb = __builtin_bit_cast(half8v, sb.k[s][lane]);
-      qb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq_hi[s], qb, 0, 0, 0);
-      qb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq_lo[s], qb, 0, 0, 0);
+    for (int t = 0; t < TR; ++t) {
+      qa[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_hi[t][s], qa[t], 0, 0, 0);
+      qb[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq_hi[t][s], qb[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      qa[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq_lo[t][s], qa[t], 0, 0, 0);
+      qb[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq_lo[t][s], qb[t], 0, 0, 0);
     }
   }
-  const uint2 ka_s = sa.ks[r], kb_s = sb.ks[r];
+  const uint2 ka_s = sp.ks[0][r], kb_s = sp.ks[1][r];
   const half2v a01 = as_h2(ka_s.x), a23 = as_h2(ka_s.y), b01 = as_h2(kb_s.x), b23 = as_h2(kb_s.y);
-  float x[8];
-  x[0] = __builtin_fmaf(qa[0], (float)a01[0], 0.0f);
-  x[1] = __builtin_fmaf(qa[1], (float)a01[1], 0.0f);
-  x[2] = __builtin_fmaf(qa[2], (float)a23[0], 0.0f);
-  x[3] = __builtin_fmaf(qa[3], (float)a23[1], 0.0f);
-  x[4] = __builtin_fmaf(qb[0], (float)b01[0], 0.0f);
-  x[5] = __builtin_fmaf(qb[1], (float)b01[1], 0.0f);
-  x[6] = __builtin_fmaf(qb[2], (float)b23[0], 0.0f);
-  x[7] = __builtin_fmaf(qb[3], (float)b23[1], 0.0f);
-  if (!has_b) {
-    __asm__ volatile("");
+  half8v ph[TR], pl[TR];
 #pragma unroll
-    for (int i = 4; i < 8; ++i) x[i] = kNegInf;
+  for (int t = 0; t < TR; ++t) {
+    float x[8];
+    x[0] = __builtin_fmaf(qa[t][0], (float)a01[0], 0.0f);
+    x[1] = __builtin_fmaf(qa[t][1], (float)a01[1], 0.0f);
+    x[2] = __builtin_fmaf(qa[t][2], (float)a23[0], 0.0f);
+    x[3] = __builtin_fmaf(qa[t][3], (float)a23[1], 0.0f);
+    x[4] = __builtin_fmaf(qb[t][0], (float)b01[0], 0.0f);
+    x[5] = __builtin_fmaf(qb[t][1], (float)b01[1], 0.0f);
+    x[6] = __builtin_fmaf(qb[t][2], (float)b23[0], 0.0f);
+    x[7] = __builtin_fmaf(qb[t][3], (float)b23[1], 0.0f);
+    if (!has_b) {
+      __asm__ volatile("");
+#pragma unroll
+      for (int i = 4; i < 8; ++i) x[i] = kNegInf;
+    }
+    if (masked) {
+      __asm__ volatile("");
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (tok0 + (i >> 2) * 16 + 4 * r + (i & 3) >= lim[t]) x[i] = kNegInf;
+    }
+    float p[8];
+    mt_softmax8<NT>(x, st[t], p);
+    // P = high + low fp16 parts; the residual p - high in one v_fma_mix each
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
+      const half2v l = __builtin_bit_cast(
+          half2v, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(-1.0f, (float)h[0], p[i]),
+                                             __builtin_fmaf(-1.0f, (float)h[1], p[i + 1])));
+      ph[t][i] = h[0];
+      ph[t][i + 1] = h[1];
+      pl[t][i] = l[0];
+      pl[t][i + 1] = l[1];
+    }
   }
-  if (masked) {
-    __asm__ volatile("");
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (tok0 + (i >> 2) * 16 + 4 * r + (i & 3) >= lim) x[i] = kNegInf;
-  }
-  float p[8];
-  mt_softmax8<NT>(x, st, p);
-  half8v ph, pl;
+  for (int c = 0; c < NT; ++c) {
+    const half8v v8 = __builtin_bit_cast(half8v, sp.v[c][lane]);
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
-    const half2v l = __builtin_bit_cast(
-        half2v, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)h[0], p[i + 1] - (float)h[1]));
-    ph[i] = h[0];
-    ph[i + 1] = h[1];
-    pl[i] = l[0];
-    pl[i + 1] = l[1];
-  }
+    for (int t = 0; t < TR; ++t) st[t].acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, ph[t], st[t].acc[c], 0, 0, 0);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint2 va = sa.v[t][lane], vb = sb.v[t][lane];
-    const half8v v8 = __builtin_bit_cast(half8v, make_uint4(va.x, va.y, vb.x, vb.y));
-    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, ph, st.acc[t], 0, 0, 0);
-    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, pl, st.acc[t], 0, 0, 0);
+    for (int t = 0; t < TR; ++t) st[t].acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, pl[t], st[t].acc[c], 0, 0, 0);
   }
 }
 
-// NRG row groups of 16 rows (one per wave of a row group) times NBG = 8 / NRG
-// block groups: wave w takes rows 16 * (w % NRG) .. +15 of the work-group's
-// tile and, of the four block pairs of every stage, those with index
-// w / NRG (mod NBG); the block groups of a row group are merged in LDS at the
-// end.  Every wave loads and dequantizes one block per stage.
+// NRG row groups of 16 TR rows (TR tiles of 16 per wave) times NBG = 8 / NRG
+// block groups: wave w takes rows 16 TR (w % NRG) .. + 16 TR - 1 of the
+// work-group's tile and, of the four block pairs of every stage, those with
+// index w / NRG (mod NBG); the block groups of a row group are merged in LDS at
+// the end.  Every wave loads and dequantizes one block per stage.
 //
 // PREFIX (the shared-prefix pass of cascade decode): the work-group's rows are
 // the (member sequence, query head) pairs of one group of sequences that share
 // their leading blocks; every row sees all the shared tokens, which are read
 // once for the whole group; the results are always partials.
-template <int D, int NRG, bool PREFIX>
+template <int D, int NRG, int TR, bool PREFIX>
 __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiTokenArgs a) {
   constexpr int G = D / 32, KS = D / 32, NT = D / 16;
   constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
   constexpr int NW = kMtWaves;
   constexpr int NBG = NW / NRG;
-  constexpr int RW = 16 * NRG;  // rows per work-group
+  constexpr int RW = 16 * TR * NRG;  // rows per work-group
 
   __shared__ uint32_t s_lut[256];
   __shared__ __attribute__((aligned(16))) uint32_t s_vm[NW][64];
   // two stage buffers of NW block slots; the query staging area and the final
   // block-group merge overlay them
-  __shared__ __attribute__((aligned(16))) MtSlot<D> s_stage[2][NW];
-  __shared__ float s_fm[NW][16], s_fl[NW][16];
-  static_assert(sizeof(s_stage) >= (size_t)NRG * 32 * D * sizeof(_Float16), "query staging overlay");
-  static_assert(sizeof(s_stage) >= (size_t)NW * NT * 64 * sizeof(float4v), "merge overlay");
+  __shared__ __attribute__((aligned(16))) MtPair<D> s_stage[2][NW / 2];
+  __shared__ float s_fm[NW][TR][16], s_fl[NW][TR][16];
+  static_assert(sizeof(s_stage) >= (size_t)NRG * TR * 32 * D * sizeof(_Float16), "query staging overlay");
+  static_assert(NBG == 1 || sizeof(s_stage) >= (size_t)NW * TR * NT * 64 * sizeof(float4v), "merge overlay");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,14 +336,18 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   const int blk1 = min(nblk, blk0 + a.split_blocks);
   const int nb = blk1 - blk0;
 
-  // this lane's column (row) and its visible-key count; rows past R see none
+  // this lane's column (row) of each tile and its visible-key count; rows past
+  // R see none
   const int n = lane & 15, r = lane >> 4;
-  const int w_first = row0 + 16 * rg;
-  const int myrow = w_first + n;
-  const bool row_ok = myrow < R;
-  const int lim = row_ok ? (PREFIX ? T : T - M + myrow / a.g + 1) : 0;
+  const int w_first = row0 + 16 * TR * rg;
+  int myrow[TR], lim[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    myrow[t] = w_first + 16 * t + n;
+    lim[t] = myrow[t] < R ? (PREFIX ? T : T - M + myrow[t] / a.g + 1) : 0;
+  }
   // the wave's smallest and largest visible-key counts (its first and last rows)
-  const int w_last = min(R, w_first + 16) - 1;
+  const int w_last = min(R, w_first + 16 * TR) - 1;
   const int lmin_w = w_first < R ? (PREFIX ? T : T - M + w_first / a.g + 1) : 0;
   const int lmax_w = w_first < R ? (PREFIX ? T : T - M + w_last / a.g + 1) : 0;
   // query / output row of tile row `row`: (token or member, head)
@@ -360,64 +391,72 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     mt_load_blk<D>(b3, rec_of(3), lane);
   }
 
-  // ---- the row group's 16 rotated, scaled query rows: fp16 high and low parts ----
+  // ---- the row group's 16 TR rotated, scaled query rows: fp16 high and low ------
   if (tid < 256) s_lut[tid] = lut_w;
-  _Float16(*s_q)[2][16][D] = reinterpret_cast<_Float16(*)[2][16][D]>(&s_stage[0][0]);
+  _Float16(*s_q)[TR][2][16][D] = reinterpret_cast<_Float16(*)[TR][2][16][D]>(&s_stage[0][0]);
   if (bg == 0) {
-    uint32_t qw[16];  // all 16 query loads in flight before the first rotation
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      qw[j] = load_query_word<D>(a.q + q_row(min(w_first + j, R - 1)) * D, lane);
-    }
+    for (int t = 0; t < TR; ++t) {
+      uint32_t qw[16];  // all 16 query loads in flight before the first rotation
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float x0 = 0.f, x1 = 0.f;
-      if (w_first + j < R) rotate_row<D>(qw[j], lane, x0, x1);
+      for (int j = 0; j < 16; ++j) {
+        qw[j] = load_query_word<D>(a.q + q_row(min(w_first + 16 * t + j, R - 1)) * D, lane);
+      }
 #pragma unroll
-      for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
-        const float xs = (e ? x1 : x0) * a.qscale;
-        const _Float16 hi = (_Float16)xs;
-        const _Float16 lo = (_Float16)(xs - (float)hi);
-        const int c = rotated_channel<D>(lane, e);
-        s_q[rg][0][j][c] = hi;
-        s_q[rg][1][j][c] = lo;
+      for (int j = 0; j < 16; ++j) {
+        float x0 = 0.f, x1 = 0.f;
+        if (w_first + 16 * t + j < R) rotate_row<D>(qw[j], lane, x0, x1);
+#pragma unroll
+        for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
+          const float xs = (e ? x1 : x0) * a.qscale;
+          const _Float16 hi = (_Float16)xs;
+          const _Float16 lo = (_Float16)(xs - (float)hi);
+          const int c = rotated_channel<D>(lane, e);
+          s_q[rg][t][0][j][c] = hi;
+          s_q[rg][t][1][j][c] = lo;
+        }
       }
     }
   }
   __syncthreads();
-  half8v bq_hi[KS], bq_lo[KS];
+  half8v bq_hi[TR][KS], bq_lo[TR][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    bq_hi[s] = *reinterpret_cast<const half8v *>(&s_q[rg][0][n][r * (D / 4) + 8 * s]);
-    bq_lo[s] = *reinterpret_cast<const half8v *>(&s_q[rg][1][n][r * (D / 4) + 8 * s]);
+  for (int t = 0; t < TR; ++t) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bq_hi[t][s] = *reinterpret_cast<const half8v *>(&s_q[rg][t][0][n][r * (D / 4) + 8 * s]);
+      bq_lo[t][s] = *reinterpret_cast<const half8v *>(&s_q[rg][t][1][n][r * (D / 4) + 8 * s]);
+    }
   }
   __syncthreads();  // the staging area becomes stage buffer 0
 
-  WaveState<NT> st;
-  st.m = kMtFloor;
-  st.l = 0.f;
+  WaveState<NT> st[TR];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) st.acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TR; ++t) {
+    st[t].m = kMtFloor;
+    st[t].l = 0.f;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) st[t].acc[c] = (float4v){0.f, 0.f, 0.f, 0.f};
+  }
 
   uint32_t *vm_slot = s_vm[wv];
   const int nstage = (nb + NW - 1) / NW;
   auto stage = [&](MtBlk<D> &buf, int k) {
-    MtSlot<D>(&cur)[NW] = s_stage[k & 1];
+    MtPair<D>(&cur)[NW / 2] = s_stage[k & 1];
+    const int first = blk0 + k * NW;
+    const int cnt = min(NW, blk1 - first);
     if (k < mine) {
-      const int blk = blk0 + wv + k * NW;
-      mt_produce<D>(buf, cur[wv], s_lut, vm_slot, lane, blk == tail_blk, tail_keep);
+      const int blk = first + wv;
+      mt_produce<D>(buf, cur[wv >> 1], wv & 1, (wv & 1) == 0 && wv + 1 == cnt, s_lut, vm_slot, lane,
+                    blk == tail_blk, tail_keep);
     }
     mt_load_blk<D>(buf, rec_of(k + 4), lane);
     __syncthreads();
-    const int first = blk0 + k * NW;
-    const int cnt = min(NW, blk1 - first);
 #pragma unroll 1
     for (int j = 2 * bg; j < cnt; j += 2 * NBG) {
       const int tok0 = (first + j) * 16;
       if (tok0 >= lmax_w) break;  // this pair and the later ones are masked for every row
-      const bool has_b = j + 1 < cnt;
-      mt_consume_pair<D>(cur[j], cur[has_b ? j + 1 : j], has_b, bq_hi, bq_lo, st, lane, tok0, lim,
-                         tok0 + 32 > lmin_w);
+      mt_consume_pair<D, TR>(cur[j >> 1], j + 1 < cnt, bq_hi, bq_lo, st, lane, tok0, lim, tok0 + 32 > lmin_w);
     }
   };
 #pragma unroll 1
@@ -429,78 +468,93 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   }
 
   // ---- merge the block groups of each row group ---------------------------------
-  float l = st.l;
-  l += xor16(l);
-  l += xor32(l);
+  float l[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    l[t] = st[t].l;
+    l[t] += xor16(l[t]);
+    l[t] += xor32(l[t]);
+  }
   if constexpr (NBG > 1) {
-    float4v(*s_fa)[NT][64] = reinterpret_cast<float4v(*)[NT][64]>(&s_stage[0][0]);
+    float4v(*s_fa)[TR][NT][64] = reinterpret_cast<float4v(*)[TR][NT][64]>(&s_stage[0][0]);
     __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
-    for (int t = 0; t < NT; ++t) s_fa[wv][t][lane] = st.acc[t];
-    if (r == 0) {
-      s_fm[wv][n] = st.m;
-      s_fl[wv][n] = l;
+    for (int t = 0; t < TR; ++t) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c) s_fa[wv][t][c][lane] = st[t].acc[c];
+      if (r == 0) {
+        s_fm[wv][t][n] = st[t].m;
+        s_fl[wv][t][n] = l[t];
+      }
     }
     __syncthreads();
     if (bg != 0) return;
-    float mx = st.m;
 #pragma unroll
-    for (int q = 1; q < NBG; ++q) mx = __builtin_fmaxf(mx, s_fm[rg + NRG * q][n]);
-    const float f0 = __builtin_amdgcn_exp2f(st.m - mx);
-    l *= f0;
+    for (int t = 0; t < TR; ++t) {
+      float mx = st[t].m;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) st.acc[t] *= f0;
+      for (int q = 1; q < NBG; ++q) mx = __builtin_fmaxf(mx, s_fm[rg + NRG * q][t][n]);
+      const float f0 = __builtin_amdgcn_exp2f(st[t].m - mx);
+      l[t] *= f0;
 #pragma unroll
-    for (int q = 1; q < NBG; ++q) {
-      const int w2 = rg + NRG * q;
-      const float f = __builtin_amdgcn_exp2f(s_fm[w2][n] - mx);
-      l += f * s_fl[w2][n];
+      for (int c = 0; c < NT; ++c) st[t].acc[c] *= f0;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) st.acc[t] += f * s_fa[w2][t][lane];
+      for (int q = 1; q < NBG; ++q) {
+        const int w2 = rg + NRG * q;
+        const float f = __builtin_amdgcn_exp2f(s_fm[w2][t][n] - mx);
+        l[t] += f * s_fl[w2][t][n];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) st[t].acc[c] += f * s_fa[w2][t][c][lane];
+      }
+      st[t].m = mx;
     }
-    st.m = mx;
   }
 
   // ---- this wave's rows: output, or the split partial ------------------------------
-  if (!row_ok) return;
-  const int64_t orow = q_row(myrow);
-  if (!PREFIX && a.nsplit == 1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int gp = 0; gp < G; ++gp) {
-      float o[8];
+  for (int t = 0; t < TR; ++t) {
+    if (myrow[t] >= R) continue;
+    const int64_t orow = q_row(myrow[t]);
+    if (!PREFIX && a.nsplit == 1) {
+      const float inv = l[t] > 0.f ? 1.f / l[t] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] = st.acc[2 * gp][i] * inv;
-        o[2 * i + 1] = st.acc[2 * gp + 1][i] * inv;
+      for (int gp = 0; gp < G; ++gp) {
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = st[t].acc[2 * gp][i] * inv;
+          o[2 * i + 1] = st[t].acc[2 * gp + 1][i] * inv;
+        }
+        const int64_t oi = orow * D + 32 * gp + 8 * r;
+        if (a.out_bf16) {
+          uint4 w;
+          w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+          w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+          w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+          w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + oi) = w;
+        } else {
+          float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + oi);
+          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
       }
-      const int64_t oi = orow * D + 32 * gp + 8 * r;
-      if (a.out_bf16) {
-        uint4 w;
-        w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-        w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-        w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
-        w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + oi) = w;
-      } else {
-        float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + oi);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-      }
-    }
-  } else {
-    const int64_t pi = orow * a.part_stride + slot;
+    } else {
+      const int64_t pi = orow * a.part_stride + slot;
 #pragma unroll
-    for (int gp = 0; gp < G; ++gp) {
-      float4 *dst = reinterpret_cast<float4 *>(a.part_acc + pi * D + 32 * gp + 8 * r);
-      dst[0] = make_float4(st.acc[2 * gp][0], st.acc[2 * gp + 1][0], st.acc[2 * gp][1], st.acc[2 * gp + 1][1]);
-      dst[1] = make_float4(st.acc[2 * gp][2], st.acc[2 * gp + 1][2], st.acc[2 * gp][3], st.acc[2 * gp + 1][3]);
-    }
-    if (r == 0) {
-      // a row none of whose keys fall in this split keeps the floor maximum
-      // and a zero sum; the merge gives it weight 0
-      a.part_ml[pi * 2] = st.m;
-      a.part_ml[pi * 2 + 1] = l;
+      for (int gp = 0; gp < G; ++gp) {
+        float4 *dst = reinterpret_cast<float4 *>(a.part_acc + pi * D + 32 * gp + 8 * r);
+        dst[0] = make_float4(st[t].acc[2 * gp][0], st[t].acc[2 * gp + 1][0], st[t].acc[2 * gp][1],
+                             st[t].acc[2 * gp + 1][1]);
+        dst[1] = make_float4(st[t].acc[2 * gp][2], st[t].acc[2 * gp + 1][2], st[t].acc[2 * gp][3],
+                             st[t].acc[2 * gp + 1][3]);
+      }
+      if (r == 0) {
+        // a row none of whose keys fall in this split keeps the floor maximum
+        // and a zero sum; the merge gives it weight 0
+        a.part_ml[pi * 2] = st[t].m;
+        a.part_ml[pi * 2 + 1] = l[t];
+      }
     }
   }
 }
@@ -530,9 +584,10 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, false>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, false>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, false>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, 1, false>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, false>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, false>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 2, false>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -547,9 +602,9 @@ hipError_t launch_prefix(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, true>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, true>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, true>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, 1, true>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, true>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, true>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -300,9 +300,10 @@ tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_he
     return fail(TQ_ERR_INVALID_ARG, "num_tokens must be <= batch * max_query_len");
   const int64_t g = num_q_heads / hkv;
   // rows of one (sequence, kv-head): up to 32 in one work-group of 2 row
-  // groups x 4 block groups, up to 64 in 4 x 2, more in tiles of 128 (8 x 1)
+  // groups x 4 block groups, up to 64 in 4 x 2, up to 128 in 8 x 1, more in
+  // tiles of 256 (8 x 1, two 16-row tiles per wave)
   const int64_t rows = (int64_t)max_query_len * g;
-  const int rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+  const int rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
   const int64_t row_tiles = (rows + rows_per_wg - 1) / rows_per_wg;
   const tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
                                                      max_context_len);
