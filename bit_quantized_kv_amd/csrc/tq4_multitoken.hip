@@ -365,12 +365,20 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   const uint8_t *base = a.pool + (int64_t)kvh * REC;
   const int64_t stride = (int64_t)a.hkv * REC;
   const int mine = nb > wv ? (nb - wv + NW - 1) / NW : 0;
-  const int my_id = settled(my_id_raw);
+  // the ids of this wave's blocks 64 c .. 64 c + 63 (lane j: block 64 c + j);
+  // a split longer than 64 blocks per wave fetches the next 64 when the
+  // prefetch index reaches them (once per 64 stages: the wait is negligible)
+  int my_id = settled(my_id_raw), id_chunk = 0;
   // block k of this wave (k >= mine: its last block again, an L2 hit; a wave
   // with no block of this split refills from block 0's record, never used)
   auto rec_of = [&](int k) {
     const int kk = k < mine ? k : mine - 1;
-    return kk < 0 ? base : base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
+    if (kk < 0) return base;
+    if ((kk >> 6) != id_chunk) {
+      id_chunk = kk >> 6;
+      my_id = settled(btab[min(blk0 + wv + (64 * id_chunk + lane) * NW, a.max_blocks - 1)]);
+    }
+    return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk & 63) * stride;
   };
   const int seq_nblk = (T + 15) >> 4;
   const int tail_blk = (T & 15) ? seq_nblk - 1 : seq_nblk;
@@ -559,11 +567,17 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   }
 }
 
-// One work-group per (sequence, query token, query head) slot: combine the
-// split partials of the row, if the slot holds a query token.
+// One wave per (sequence, query token, query head) slot, four per work-group:
+// combine the split partials of the row, if the slot holds a query token.
+// Multi-token rows are many and their splits few, so a wave takes a row: the
+// lanes find the largest partial maximum together, then every lane adds the
+// weighted accumulators of its D / 64 channels over the splits.
 template <int D>
 __global__ __launch_bounds__(256) void multitoken_merge_kernel(MultiTokenArgs a) {
-  const int64_t slot = blockIdx.x;
+  constexpr int CPL = D / 64;  // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= (int64_t)a.batch * a.max_query_len * a.hq) return;
   const int h = (int)(slot % a.hq);
   const int64_t rest = slot / a.hq;
   const int i = (int)(rest % a.max_query_len);
@@ -576,7 +590,34 @@ __global__ __launch_bounds__(256) void multitoken_merge_kernel(MultiTokenArgs a)
   const int nblk = (lim + 15) >> 4;
   const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
   const int64_t row = (int64_t)(q0 + i) * a.hq + h;
-  merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.nsplit, a.out_bf16}, row, ns);
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml + row * a.nsplit * 2);
+  const float *pa = a.part_acc + row * a.nsplit * D + CPL * lane;
+  float mx = kNegInf;
+  for (int sp = lane; sp < ns; sp += 64) mx = __builtin_fmaxf(mx, ml[sp].x);
+  mx = __builtin_fmaxf(mx, xor1(mx));
+  mx = __builtin_fmaxf(mx, xor2(mx));
+  mx = __builtin_fmaxf(mx, xor4(mx));
+  mx = __builtin_fmaxf(mx, xor8(mx));
+  mx = __builtin_fmaxf(mx, xor16(mx));
+  mx = __builtin_fmaxf(mx, xor32(mx));
+  float den = 0.f, num[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) num[c] = 0.f;
+#pragma unroll 4
+  for (int sp = 0; sp < ns; ++sp) {
+    const float2 m_l = ml[sp];  // the same address on every lane
+    const float f = m_l.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_l.x - mx);
+    den += f * m_l.y;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) num[c] += f * pa[(int64_t)sp * D + c];
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t oi = row * D + CPL * lane + c;
+    if (a.out_bf16) reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(num[c] * inv);
+    else reinterpret_cast<float *>(a.out)[oi] = num[c] * inv;
+  }
 }
 
 template <int D>
@@ -593,7 +634,7 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t rows = (int64_t)a.batch * a.max_query_len * a.hq;
-  hipLaunchKernelGGL(multitoken_merge_kernel<D>, dim3((unsigned)rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(multitoken_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -305,8 +305,10 @@ tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_he
   const int64_t rows = (int64_t)max_query_len * g;
   const int rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
   const int64_t row_tiles = (rows + rows_per_wg - 1) / rows_per_wg;
+  // prefill-sized tiles (MFMA-heavy per block) walk whole contexts; smaller
+  // ones split long contexts at 512 blocks so uneven lengths balance
   const tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
-                                                     max_context_len);
+                                                     max_context_len, rows_per_wg >= 256 ? 4096 : 512);
   if ((int64_t)batch * hkv * row_tiles * sp.nsplit >= (int64_t(1) << 31) ||
       (int64_t)batch * max_query_len * num_q_heads >= (int64_t(1) << 31))
     return fail(TQ_ERR_INVALID_ARG, "launch grid too large");

@@ -123,7 +123,7 @@ struct SplitPlan {
 SplitPlan plan_split(int batch, int hkv, int max_context_len);
 // Multi-token attention: `units` work-groups per split (sequences x kv-heads x
 // row tiles); splits only when the units alone leave compute units idle, at
-// most 512 blocks per work-group.
-SplitPlan plan_split_multitoken(int64_t units, int max_context_len);
+// most max_split_blocks blocks per work-group.
+SplitPlan plan_split_multitoken(int64_t units, int max_context_len, int max_split_blocks);
 
 }  // namespace tq

@@ -188,15 +188,15 @@ SplitPlan plan_split(int batch, int hkv, int max_context_len) {
   return p;
 }
 
-SplitPlan plan_split_multitoken(int64_t units, int max_context_len) {
+SplitPlan plan_split_multitoken(int64_t units, int max_context_len, int max_split_blocks) {
   const int64_t max_nblk = std::max<int64_t>(1, ((int64_t)max_context_len + 15) / 16);
   units = std::max<int64_t>(1, units);
   const int64_t want = (256 + units - 1) / units;
   int64_t s = (max_nblk + want - 1) / want;
-  s = std::min<int64_t>(512, std::max<int64_t>(16, ((s + 7) / 8) * 8));
+  s = std::min<int64_t>(max_split_blocks, std::max<int64_t>(16, ((s + 7) / 8) * 8));
   if (const char *env = std::getenv("TQ_SPLIT_BLOCKS")) {
     const long v = std::strtol(env, nullptr, 10);
-    if (v >= 1 && v <= 512) s = v;
+    if (v >= 1 && v <= 4096) s = v;
   }
   SplitPlan p;
   p.split_blocks = (int)s;

@@ -135,3 +135,13 @@ def test_full_size_sampled(name):
         rows += [(int(i), int(h)) for i in toks for h in rng.choice(cfg.num_q_heads, size=3, replace=False)]
     say(f"case: multi-token full size {name}: sampled sequences {seqs}, {len(rows)} rows")
     _run(case, m, rows=rows, seqs=seqs)
+
+
+def test_long_split_walks_more_than_64_blocks_per_wave():
+    # 1024-block splits: each wave walks up to ~94 blocks, past the 64 block
+    # ids one wave-wide load holds
+    os.environ["TQ_SPLIT_BLOCKS"] = "1024"
+    cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(9000, 12000),
+                                 seed=212)
+    say("case: multi-token with 1024-block splits (block ids fetched in chunks of 64 per wave)")
+    _run(Case(cfg), 40)
