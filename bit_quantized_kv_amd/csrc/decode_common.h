@@ -212,13 +212,17 @@ __device__ __forceinline__ void write_zero_rows(const DecodeArgs &a, int b, int 
   }
 }
 
-// Combine the split partials of one output row (one work-group of 256 threads).
-// Thread (cq, sl) takes channels 4*cq .. 4*cq+3 of splits sl, sl + SL, ...,
-// in chunks of 8 splits whose loads (maxima, sums, accumulators) are all
-// issued before any is used; the first chunk's loads go out before the
-// largest partial maximum M is found (every wave on its own: lane-strided
-// loads and a wave reduction, no barrier).  The weights are 2^(m_s - M); the
-// SL slices are added in LDS.
+// Combine the split partials of one output row (one work-group of 256 threads)
+// in one pass over them.  Thread (cq, sl) takes channels 4*cq .. 4*cq+3 of
+// splits sl, sl + SL, ..., in chunks of 8 splits whose loads (maxima, sums,
+// accumulators) are all issued before any is used, and keeps a running
+// maximum m with its sum and accumulators scaled to 2^-m (an online softmax
+// over partials); the SL slices are rescaled to the largest maximum when they
+// are added in LDS.  The first chunk may be loaded before the row's count of
+// partials is known (it waits on a context length): it reads slots below
+// nload, which are inside the row's workspace whether or not they hold one of
+// its partials, and the ones at or past ns are dropped by selection (their
+// contents may be anything, NaN included).
 struct MergeView {
   const float *part_ml;   // [rows][nsplit][2]: (max, sum) in log2 units
   const float *part_acc;  // [rows][nsplit][d]
@@ -238,77 +242,91 @@ struct SlotsTwoRuns {
   __device__ __forceinline__ int operator()(int k) const { return k < n0 ? k : lo1 + (k - n0); }
 };
 
-// ns: partials that hold this row's tokens (0: the row attends to nothing and
-// is written as zeros); slot(k) is the slot of the k-th.
-template <int D, typename Slots = SlotsDirect>
-__device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int ns, Slots slot = Slots()) {
+// nload >= 1: chunk 0 reads slots slot(k), k < nload, before the row's count
+// of partials ns = ns_fn() is asked for (slot(k) for k < nload must lie in
+// the row's workspace); ns = 0 writes a zero row.
+template <int D, typename NsFn, typename Slots>
+__device__ __forceinline__ void merge_row_impl(const MergeView &v, int64_t row, int nload, NsFn ns_fn,
+                                               Slots slot) {
   constexpr int CQ = D / 4;          // channel quads
   constexpr int SL = 256 / CQ;       // split lanes
   constexpr int CH = 8;              // splits per thread per chunk
-  __shared__ float s_l[SL][CQ];
+  __shared__ float s_m[SL][CQ], s_l[SL][CQ];
   __shared__ float4 s_acc[SL][CQ];
-  const int tid = threadIdx.x, lane = tid & 63, cq = tid % CQ, sl = tid / CQ;
-  if (ns == 0) {  // no tokens: a zero row (no partial exists to read)
-    for (int c = tid; c < D; c += 256) {
-      if (v.out_bf16) reinterpret_cast<uint16_t *>(v.out)[row * D + c] = 0;
-      else reinterpret_cast<float *>(v.out)[row * D + c] = 0.f;
-    }
-    return;
-  }
+  const int tid = threadIdx.x, cq = tid % CQ, sl = tid / CQ;
   const float2 *ml = reinterpret_cast<const float2 *>(v.part_ml + row * v.nsplit * 2);
   const float *pa = v.part_acc + row * v.nsplit * D;
-  // first chunk of this thread's partials, loaded before the maximum is known
   float2 c_ml[CH];
   float4 c_v[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const int sp = min(sl + j * SL, ns - 1);  // clamped: valid split of this row
+    const int sp = min(sl + j * SL, nload - 1);
     c_ml[j] = ml[slot(sp)];
     c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)slot(sp) * D + 4 * cq);
   }
-  float M = kNegInf;
-  for (int sp = lane; sp < ns; sp += 64) M = __builtin_fmaxf(M, ml[slot(sp)].x);
-  M = __builtin_fmaxf(M, xor1(M));
-  M = __builtin_fmaxf(M, xor2(M));
-  M = __builtin_fmaxf(M, xor4(M));
-  M = __builtin_fmaxf(M, xor8(M));
-  M = __builtin_fmaxf(M, xor16(M));
-  M = __builtin_fmaxf(M, xor32(M));
-  float den = 0.f;
+  // chunk 0 is processed unconditionally (no partial in it counts when ns = 0,
+  // which then writes zeros), so its loads stay ahead of the use of ns
+  const int ns = ns_fn();
+  float m = kNegInf, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = 0; base < ns; base += CH * SL) {
-    if (base) {
+  auto take = [&](int base) {
+    bool in[CH];
+    float cm = m;
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int sp = min(base + sl + j * SL, ns - 1);
-        c_ml[j] = ml[slot(sp)];
-        c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)slot(sp) * D + 4 * cq);
-      }
+    for (int j = 0; j < CH; ++j) {
+      in[j] = base + sl + j * SL < ns && c_ml[j].x != kNegInf;
+      if (in[j]) cm = __builtin_fmaxf(cm, c_ml[j].x);
+    }
+    if (cm != m) {  // the running maximum rises (from -inf on the first partial)
+      const float r = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - cm);
+      den *= r;
+      num.x *= r;
+      num.y *= r;
+      num.z *= r;
+      num.w *= r;
+      m = cm;
     }
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const bool in = base + sl + j * SL < ns;
-      const float f = (!in || c_ml[j].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(c_ml[j].x - M);
-      den += f * c_ml[j].y;
-      num.x += f * c_v[j].x;
-      num.y += f * c_v[j].y;
-      num.z += f * c_v[j].z;
-      num.w += f * c_v[j].w;
+      if (in[j]) {
+        const float f = __builtin_amdgcn_exp2f(c_ml[j].x - m);
+        den = __builtin_fmaf(f, c_ml[j].y, den);
+        num.x = __builtin_fmaf(f, c_v[j].x, num.x);
+        num.y = __builtin_fmaf(f, c_v[j].y, num.y);
+        num.z = __builtin_fmaf(f, c_v[j].z, num.z);
+        num.w = __builtin_fmaf(f, c_v[j].w, num.w);
+      }
     }
+  };
+  take(0);
+  for (int base = CH * SL; base < ns; base += CH * SL) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int sp = min(base + sl + j * SL, ns - 1);
+      c_ml[j] = ml[slot(sp)];
+      c_v[j] = *reinterpret_cast<const float4 *>(pa + (int64_t)slot(sp) * D + 4 * cq);
+    }
+    take(base);
   }
+  s_m[sl][cq] = m;
   s_l[sl][cq] = den;
   s_acc[sl][cq] = num;
   __syncthreads();
   if (sl == 0) {
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) M = __builtin_fmaxf(M, s_m[i][cq]);
     float L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
-      L += s_l[i][cq];
-      o.x += s_acc[i][cq].x;
-      o.y += s_acc[i][cq].y;
-      o.z += s_acc[i][cq].z;
-      o.w += s_acc[i][cq].w;
+      const float mi = s_m[i][cq];
+      const float w = mi == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+      L = __builtin_fmaf(w, s_l[i][cq], L);
+      o.x = __builtin_fmaf(w, s_acc[i][cq].x, o.x);
+      o.y = __builtin_fmaf(w, s_acc[i][cq].y, o.y);
+      o.z = __builtin_fmaf(w, s_acc[i][cq].z, o.z);
+      o.w = __builtin_fmaf(w, s_acc[i][cq].w, o.w);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
@@ -319,6 +337,20 @@ __device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int n
       else reinterpret_cast<float *>(v.out)[oi] = ov[c];
     }
   }
+}
+
+// ns: partials that hold this row's tokens (0: the row attends to nothing and
+// is written as zeros); slot(k) is the slot of the k-th.
+template <int D, typename Slots = SlotsDirect>
+__device__ __forceinline__ void merge_row(const MergeView &v, int64_t row, int ns, Slots slot = Slots()) {
+  if (ns == 0) {  // no partial exists to read
+    for (int c = threadIdx.x; c < D; c += 256) {
+      if (v.out_bf16) reinterpret_cast<uint16_t *>(v.out)[row * D + c] = 0;
+      else reinterpret_cast<float *>(v.out)[row * D + c] = 0.f;
+    }
+    return;
+  }
+  merge_row_impl<D>(v, row, ns, [ns]() { return ns; }, slot);
 }
 
 }  // namespace tq

@@ -315,15 +315,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   finish_workgroup<D, GQ, NW, CASCADE>(a, st, b, qh0, sp, s_m, s_l, s_acc);
 }
 
-// One work-group per (sequence, query head): combine the split partials.
+// One work-group per (sequence, query head) (grid x, y): combine the split
+// partials.  Every slot below nsplit is in the row's workspace, so the first
+// partials are loaded while the context length is still on its way.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  const int64_t row = blockIdx.x;
-  const int b = (int)(row / a.hq);
-  const int T = a.ctx[b];
-  const int nblk = (T + 15) >> 4;
-  const int ns = (nblk + a.split_blocks - 1) / a.split_blocks;
-  merge_row<D>(MergeView{a.part_ml, a.part_acc, a.out, a.nsplit, a.out_bf16}, row, ns);
+  const int b = blockIdx.x;
+  const int64_t row = (int64_t)b * a.hq + blockIdx.y;
+  merge_row_impl<D>(MergeView{a.part_ml, a.part_acc, a.out, a.nsplit, a.out_bf16}, row, a.nsplit,
+                    [&]() {
+                      const int nblk = (a.ctx[b] + 15) >> 4;
+                      return (nblk + a.split_blocks - 1) / a.split_blocks;
+                    },
+                    SlotsDirect());
 }
 
 // Cascade: one work-group per (sequence, query head) combines the row's own
@@ -375,7 +379,7 @@ hipError_t launch_cascade_merge(int d, const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.batch * a.hq)), block(256);
+  const dim3 grid((unsigned)a.batch, (unsigned)a.hq), block(256);
   if (d == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, s, a);
   return hipGetLastError();
