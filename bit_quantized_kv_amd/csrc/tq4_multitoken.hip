@@ -28,6 +28,9 @@ namespace tq {
 namespace {
 
 constexpr int kMtWaves = 8;
+// block ids of one split staged in LDS: split_blocks <= kMtMaxIds
+constexpr int kMtMaxIds = 4096;
+constexpr int kDirMaxIds = 1024;
 // A running maximum that starts finite, so that a column whose tokens are all
 // masked so far gets p = 2^(-inf - m) = 0 rather than 2^(-inf + inf).
 constexpr float kMtFloor = -1.0e30f;
@@ -284,6 +287,7 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   // block-group merge overlay them
   __shared__ __attribute__((aligned(16))) MtPair<D> s_stage[2][NW / 2];
   __shared__ float s_fm[NW][TR][16], s_fl[NW][TR][16];
+  __shared__ int32_t s_ids[kMtMaxIds];  // the split's block ids
   static_assert(sizeof(s_stage) >= (size_t)NRG * TR * 32 * D * sizeof(_Float16), "query staging overlay");
   static_assert(NBG == 1 || sizeof(s_stage) >= (size_t)NW * TR * NT * 64 * sizeof(float4v), "merge overlay");
 
@@ -358,27 +362,32 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   };
 
   // ---- block ids and the first loads ---------------------------------------------
+  // lane k < 4 holds the id of this wave's block k (the first loads); the
+  // split's ids (nb <= kMtMaxIds) go to LDS for the ring's refills, so that no
+  // load is issued on a path of its own inside the loop (the compiler would
+  // then wait for every load in flight before each refill)
   const int32_t *btab = a.block_table + (int64_t)tab_seq * a.max_blocks;
-  const int my_id_raw = btab[min(blk0 + wv + lane * NW, a.max_blocks - 1)];
+  const int my_id_raw = btab[min(blk0 + wv + (lane & 3) * NW, a.max_blocks - 1)];
   const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
+  int ids[kMtMaxIds / (NW * 64)];
+#pragma unroll
+  for (int i = 0; i < kMtMaxIds / (NW * 64); ++i) ids[i] = btab[min(blk0 + tid + i * NW * 64, a.max_blocks - 1)];
   __asm__ volatile("" ::: "memory");
   const uint8_t *base = a.pool + (int64_t)kvh * REC;
   const int64_t stride = (int64_t)a.hkv * REC;
   const int mine = nb > wv ? (nb - wv + NW - 1) / NW : 0;
-  // the ids of this wave's blocks 64 c .. 64 c + 63 (lane j: block 64 c + j);
-  // a split longer than 64 blocks per wave fetches the next 64 when the
-  // prefetch index reaches them (once per 64 stages: the wait is negligible)
-  int my_id = settled(my_id_raw), id_chunk = 0;
+  const int my_id = settled(my_id_raw);
   // block k of this wave (k >= mine: its last block again, an L2 hit; a wave
   // with no block of this split refills from block 0's record, never used)
+  auto first_rec = [&](int k) {
+    const int kk = k < mine ? k : mine - 1;
+    if (kk < 0) return base;
+    return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk) * stride;
+  };
   auto rec_of = [&](int k) {
     const int kk = k < mine ? k : mine - 1;
     if (kk < 0) return base;
-    if ((kk >> 6) != id_chunk) {
-      id_chunk = kk >> 6;
-      my_id = settled(btab[min(blk0 + wv + (64 * id_chunk + lane) * NW, a.max_blocks - 1)]);
-    }
-    return base + (int64_t)__builtin_amdgcn_readlane(my_id, kk & 63) * stride;
+    return base + (int64_t)__builtin_amdgcn_readfirstlane(s_ids[wv + kk * NW]) * stride;
   };
   const int seq_nblk = (T + 15) >> 4;
   const int tail_blk = (T & 15) ? seq_nblk - 1 : seq_nblk;
@@ -390,17 +399,20 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   }
   MtBlk<D> b0, b1, b2, b3;
   if (mine > 0) {
-    mt_load_blk<D>(b0, rec_of(0), lane);
+    mt_load_blk<D>(b0, first_rec(0), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(b1, rec_of(1), lane);
+    mt_load_blk<D>(b1, first_rec(1), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(b2, rec_of(2), lane);
+    mt_load_blk<D>(b2, first_rec(2), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(b3, rec_of(3), lane);
+    mt_load_blk<D>(b3, first_rec(3), lane);
   }
 
   // ---- the row group's 16 TR rotated, scaled query rows: fp16 high and low ------
   if (tid < 256) s_lut[tid] = lut_w;
+#pragma unroll
+  for (int i = 0; i < kMtMaxIds / (NW * 64); ++i)
+    if (tid + i * NW * 64 < nb) s_ids[tid + i * NW * 64] = ids[i];
   _Float16(*s_q)[TR][2][16][D] = reinterpret_cast<_Float16(*)[TR][2][16][D]>(&s_stage[0][0]);
   if (bg == 0) {
 #pragma unroll
@@ -467,12 +479,15 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
       mt_consume_pair<D, TR>(cur[j >> 1], j + 1 < cnt, bq_hi, bq_lo, st, lane, tok0, lim, tok0 + 32 > lmin_w);
     }
   };
+  // the four stages of an iteration run unconditionally (a stage past the
+  // last has no block and no pair: one barrier), so every path through the
+  // loop issues the same loads and the waits stay partial
 #pragma unroll 1
   for (int k = 0; k < nstage; k += 4) {
     stage(b0, k);
-    if (k + 1 < nstage) stage(b1, k + 1);
-    if (k + 2 < nstage) stage(b2, k + 2);
-    if (k + 3 < nstage) stage(b3, k + 3);
+    stage(b1, k + 1);
+    stage(b2, k + 2);
+    stage(b3, k + 3);
   }
 
   // ---- merge the block groups of each row group ---------------------------------
@@ -567,6 +582,373 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   }
 }
 
+// Direct kernel for up to 32 rows per (sequence, kv-head) (verification of a
+// few proposed tokens): every row of the sequence's kv-head sees every block,
+// so staging the blocks through LDS (above) would share each dequantized block
+// among only two waves.  Here a work-group of 4 waves takes one split of the
+// key blocks, and every wave runs all RT 16-row tiles against its own pairs of
+// blocks (pair p = blocks 2p, 2p + 1 of the split, p = wave + 4k), as the
+// decode kernel does for one query token: no barrier in the main loop, keys
+// through the byte-pair table in LDS straight into the QK A operand, values
+// dequantized in registers straight into the PV A operand (the pair's 32
+// tokens: operand index 8r + j is token 4r + j of the first block for j < 4 and
+// of the second otherwise, the QK accumulators' order).  Two pairs of loads
+// stay in flight per wave, and the query operands stay in registers (two
+// waves per SIMD: two work-groups per CU).  The 4 waves' softmax states are
+// merged in LDS at the end (two halving rounds).
+constexpr int kDirWaves = 4;
+
+template <int D, int RT>
+__global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void tq4_mt_direct_kernel(
+    MultiTokenArgs a) {
+  constexpr int G = D / 32, KS = D / 32, NT = D / 16;
+  constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
+  constexpr int NW = kDirWaves;
+
+  __shared__ uint32_t s_lut[256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_vm[NW][2][64];
+  // the query staging area, then the wave-merge area
+  constexpr size_t kQBytes = (size_t)RT * 2 * 16 * D * sizeof(_Float16);
+  constexpr size_t kMBytes = (size_t)(NW / 2) * RT * NT * 64 * sizeof(float4v);
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kQBytes > kMBytes ? kQBytes : kMBytes];
+  __shared__ float s_wm[NW / 2][RT][16], s_wl[NW / 2][RT][16];
+  __shared__ int32_t s_ids[kDirMaxIds];  // the split's block ids
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const MtTask task = mt_task(a);
+  const int b = task.b, kvh = task.kvh, sp = task.sp;
+  const int q0 = a.q_start[b];
+  const int M = a.q_start[b + 1] - q0;
+  const int T = a.ctx[b];
+  const int R = M * a.g;
+  if (R <= 0) return;
+  // the last row sees all T keys, the first T - M + 1
+  const int nblk = (T + 15) >> 4;
+  const int blk0 = sp * a.split_blocks;
+  if (blk0 >= nblk) return;
+  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  const int npair = (blk1 - blk0 + 1) >> 1;
+  const int lmin = T - M + 1;
+
+  const int n = lane & 15, r = lane >> 4;
+  int myrow[RT], lim[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    myrow[t] = 16 * t + n;
+    lim[t] = myrow[t] < R ? T - M + myrow[t] / a.g + 1 : 0;
+  }
+  auto q_row = [&](int row) -> int64_t {
+    return (int64_t)(q0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
+  };
+
+  // ---- block ids and the first loads ---------------------------------------------
+  // lane j < 4 holds the id of block j & 1 of this wave's pair j / 2 (the first
+  // loads); the split's ids (at most kDirMaxIds) go to LDS for the refills
+  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
+  const int my_id_raw = btab[min(blk0 + 2 * (wv + ((lane & 3) >> 1) * NW) + (lane & 1), a.max_blocks - 1)];
+  const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
+  int ids[kDirMaxIds / (NW * 64)];
+#pragma unroll
+  for (int i = 0; i < kDirMaxIds / (NW * 64); ++i) ids[i] = btab[min(blk0 + tid + i * NW * 64, a.max_blocks - 1)];
+  __asm__ volatile("" ::: "memory");
+  const uint8_t *base = a.pool + (int64_t)kvh * REC;
+  const int64_t stride = (int64_t)a.hkv * REC;
+  const int mine = npair > wv ? (npair - wv + NW - 1) / NW : 0;
+  const int my_id = settled(my_id_raw);
+  // block h of this wave's pair k (k >= mine: its last pair again, an L2 hit;
+  // the missing second block of a lone last pair: the first again; a wave
+  // without pairs refills from block 0's record, never used)
+  auto first_rec = [&](int k, int h) {
+    const int kk = k < mine ? k : mine - 1;
+    if (kk < 0) return base;
+    const int hh = blk0 + 2 * (wv + kk * NW) + h < blk1 ? h : 0;
+    return base + (int64_t)__builtin_amdgcn_readlane(my_id, 2 * kk + hh) * stride;
+  };
+  auto rec_of = [&](int k, int h) {
+    const int kk = k < mine ? k : mine - 1;
+    if (kk < 0) return base;
+    const int hh = blk0 + 2 * (wv + kk * NW) + h < blk1 ? h : 0;
+    return base + (int64_t)__builtin_amdgcn_readfirstlane(s_ids[2 * (wv + kk * NW) + hh]) * stride;
+  };
+  const int tail_blk = (T & 15) ? nblk - 1 : nblk;
+  uint32_t tail_keep;
+  {
+    const int rr = 4 * (lane >> 4), w = lane & 3;
+    const int ta = (T & 15) - (rr + 2 * (w & 1)), tb = ta - 1;
+    tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
+  }
+  MtBlk<D> a0, b0, a1, b1;
+  if (mine > 0) {
+    mt_load_blk<D>(a0, first_rec(0, 0), lane);
+    mt_load_blk<D>(b0, first_rec(0, 1), lane);
+    __asm__ volatile("" ::: "memory");
+    mt_load_blk<D>(a1, first_rec(1, 0), lane);
+    mt_load_blk<D>(b1, first_rec(1, 1), lane);
+  }
+
+  // ---- the RT 16-row tiles of rotated, scaled query rows: fp16 high and low -----
+  if (tid < 256) s_lut[tid] = lut_w;
+#pragma unroll
+  for (int i = 0; i < kDirMaxIds / (NW * 64); ++i)
+    if (tid + i * NW * 64 < blk1 - blk0) s_ids[tid + i * NW * 64] = ids[i];
+  _Float16(*s_q)[2][16][D] = reinterpret_cast<_Float16(*)[2][16][D]>(s_buf);
+  if (wv < RT) {
+    uint32_t qw[16];  // all 16 query loads in flight before the first rotation
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qw[j] = load_query_word<D>(a.q + q_row(min(16 * wv + j, R - 1)) * D, lane);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float x0 = 0.f, x1 = 0.f;
+      if (16 * wv + j < R) rotate_row<D>(qw[j], lane, x0, x1);
+#pragma unroll
+      for (int e = 0; e < (D == 128 ? 2 : 1); ++e) {
+        const float xs = (e ? x1 : x0) * a.qscale;
+        const _Float16 hi = (_Float16)xs;
+        const _Float16 lo = (_Float16)(xs - (float)hi);
+        const int c = rotated_channel<D>(lane, e);
+        s_q[wv][0][j][c] = hi;
+        s_q[wv][1][j][c] = lo;
+      }
+    }
+  }
+  __syncthreads();
+  // the query operands (B of the QK product) stay in registers
+  half8v bq[RT][2][KS];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        bq[t][hl][s] = *reinterpret_cast<const half8v *>(&s_q[t][hl][n][r * (D / 4) + 8 * s]);
+
+  WaveState<NT> st[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    st[t].m = kMtFloor;
+    st[t].l = 0.f;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) st[t].acc[c] = (float4v){0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint32_t *vm_a = s_vm[wv][0], *vm_b = s_vm[wv][1];
+  const int vm_i = (lane >> 4) * (4 * G) + (lane & (4 * G - 1));
+  auto pair = [&](const MtBlk<D> &ba, const MtBlk<D> &bb, int k) {
+    const int blk = blk0 + 2 * (wv + k * NW);
+    const bool has_b = blk + 1 < blk1;
+    const int tok0 = 16 * blk;
+    // the value (scale, min) tiles go through LDS (rows of the partial last
+    // block past the context get zero scale and minimum)
+    uint32_t vma = ba.vmw, vmb = bb.vmw;
+    if (blk == tail_blk) {
+      __asm__ volatile("");
+      vma &= tail_keep;
+    }
+    if (blk + 1 == tail_blk) {
+      __asm__ volatile("");
+      vmb &= tail_keep;
+    }
+    vm_a[vm_i] = vma;
+    vm_b[vm_i] = vmb;
+    // ---- logits of both blocks for every tile ----
+    float4v qa[RT], qb[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) qa[t] = qb[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t wa = mt_word(ba.kq, s), wb = mt_word(bb.kq, s);
+      uint4 ea, eb;
+      ea.x = s_lut[wa & 0xFF];
+      ea.y = s_lut[(wa >> 8) & 0xFF];
+      ea.z = s_lut[(wa >> 16) & 0xFF];
+      ea.w = s_lut[wa >> 24];
+      eb.x = s_lut[wb & 0xFF];
+      eb.y = s_lut[(wb >> 8) & 0xFF];
+      eb.z = s_lut[(wb >> 16) & 0xFF];
+      eb.w = s_lut[wb >> 24];
+      const half8v ka = __builtin_bit_cast(half8v, ea), kb = __builtin_bit_cast(half8v, eb);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const half8v qh = bq[t][0][s];
+        qa[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh, qa[t], 0, 0, 0);
+        qb[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qh, qb[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const half8v ql = bq[t][1][s];
+        qa[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql, qa[t], 0, 0, 0);
+        qb[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, ql, qb[t], 0, 0, 0);
+      }
+    }
+    const half2v a01 = as_h2(ba.ks.x), a23 = as_h2(ba.ks.y), b01 = as_h2(bb.ks.x), b23 = as_h2(bb.ks.y);
+    const bool masked = tok0 + 32 > lmin;
+    half8v ph[RT], pl[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      float x[8];
+      x[0] = __builtin_fmaf(qa[t][0], (float)a01[0], 0.0f);
+      x[1] = __builtin_fmaf(qa[t][1], (float)a01[1], 0.0f);
+      x[2] = __builtin_fmaf(qa[t][2], (float)a23[0], 0.0f);
+      x[3] = __builtin_fmaf(qa[t][3], (float)a23[1], 0.0f);
+      x[4] = __builtin_fmaf(qb[t][0], (float)b01[0], 0.0f);
+      x[5] = __builtin_fmaf(qb[t][1], (float)b01[1], 0.0f);
+      x[6] = __builtin_fmaf(qb[t][2], (float)b23[0], 0.0f);
+      x[7] = __builtin_fmaf(qb[t][3], (float)b23[1], 0.0f);
+      if (!has_b) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int i = 4; i < 8; ++i) x[i] = kNegInf;
+      }
+      if (masked) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (tok0 + (i >> 2) * 16 + 4 * r + (i & 3) >= lim[t]) x[i] = kNegInf;
+      }
+      float p[8];
+      mt_softmax8<NT>(x, st[t], p);
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
+        const half2v l = __builtin_bit_cast(
+            half2v, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(-1.0f, (float)h[0], p[i]),
+                                               __builtin_fmaf(-1.0f, (float)h[1], p[i + 1])));
+        ph[t][i] = h[0];
+        ph[t][i + 1] = h[1];
+        pl[t][i] = l[0];
+        pl[t][i + 1] = l[1];
+      }
+    }
+    // ---- values: code * scale + min in fp16, both blocks into one operand ----
+    const uint4 *vra = reinterpret_cast<const uint4 *>(vm_a) + (lane >> 4) * G;
+    const uint4 *vrb = reinterpret_cast<const uint4 *>(vm_b) + (lane >> 4) * G;
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      const uint4 ma = vra[gp], mb = vrb[gp];
+      const uint32_t wa = mt_word(ba.vq, gp), wb = mt_word(bb.vq, gp);
+      const uint32_t la = wa & 0x0F0F0F0Fu, ha = (wa >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lb = wb & 0x0F0F0F0Fu, hb = (wb >> 4) & 0x0F0F0F0Fu;
+      const half2v ea01 = __builtin_elementwise_fma(mt_codes_f16<false>(la), as_h2(ma.x), as_h2(ma.z));
+      const half2v ea23 = __builtin_elementwise_fma(mt_codes_f16<true>(la), as_h2(ma.y), as_h2(ma.w));
+      const half2v oa01 = __builtin_elementwise_fma(mt_codes_f16<false>(ha), as_h2(ma.x), as_h2(ma.z));
+      const half2v oa23 = __builtin_elementwise_fma(mt_codes_f16<true>(ha), as_h2(ma.y), as_h2(ma.w));
+      const half2v eb01 = __builtin_elementwise_fma(mt_codes_f16<false>(lb), as_h2(mb.x), as_h2(mb.z));
+      const half2v eb23 = __builtin_elementwise_fma(mt_codes_f16<true>(lb), as_h2(mb.y), as_h2(mb.w));
+      const half2v ob01 = __builtin_elementwise_fma(mt_codes_f16<false>(hb), as_h2(mb.x), as_h2(mb.z));
+      const half2v ob23 = __builtin_elementwise_fma(mt_codes_f16<true>(hb), as_h2(mb.y), as_h2(mb.w));
+      const half8v ve = __builtin_bit_cast(half8v, make_uint4(as_u(ea01), as_u(ea23), as_u(eb01), as_u(eb23)));
+      const half8v vo = __builtin_bit_cast(half8v, make_uint4(as_u(oa01), as_u(oa23), as_u(ob01), as_u(ob23)));
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, ph[t], st[t].acc[2 * gp], 0, 0, 0);
+        st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, ph[t], st[t].acc[2 * gp + 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, pl[t], st[t].acc[2 * gp], 0, 0, 0);
+        st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, pl[t], st[t].acc[2 * gp + 1], 0, 0, 0);
+      }
+    }
+  };
+  // process ring slot (pair k, if it is one of this wave's), then refill it
+  auto run = [&](MtBlk<D> &ba, MtBlk<D> &bb, int k) {
+    if (k < mine) pair(ba, bb, k);
+    mt_load_blk<D>(ba, rec_of(k + 2, 0), lane);
+    mt_load_blk<D>(bb, rec_of(k + 2, 1), lane);
+  };
+#pragma unroll 1
+  for (int k = 0; k < mine; k += 2) {
+    run(a0, b0, k);
+    run(a1, b1, k + 1);
+  }
+
+  // ---- merge the waves' states: halving rounds through LDS -----------------------
+  float l[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    l[t] = st[t].l;
+    l[t] += xor16(l[t]);
+    l[t] += xor32(l[t]);
+  }
+  float4v(*s_fa)[RT][NT][64] = reinterpret_cast<float4v(*)[RT][NT][64]>(s_buf);
+#pragma unroll 1
+  for (int h = NW / 2; h >= 1; h >>= 1) {
+    __syncthreads();  // the area is free (query staging read, or the last round's reads done)
+    if (wv >= h && wv < 2 * h) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) s_fa[wv - h][t][c][lane] = st[t].acc[c];
+        if (r == 0) {
+          s_wm[wv - h][t][n] = st[t].m;
+          s_wl[wv - h][t][n] = l[t];
+        }
+      }
+    }
+    __syncthreads();
+    if (wv < h) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const float m2 = s_wm[wv][t][n];
+        const float mx = __builtin_fmaxf(st[t].m, m2);
+        const float f1 = __builtin_amdgcn_exp2f(st[t].m - mx), f2 = __builtin_amdgcn_exp2f(m2 - mx);
+        l[t] = l[t] * f1 + s_wl[wv][t][n] * f2;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) st[t].acc[c] = st[t].acc[c] * f1 + s_fa[wv][t][c][lane] * f2;
+        st[t].m = mx;
+      }
+    }
+  }
+  if (wv != 0) return;
+
+  // ---- wave 0 writes the rows: output, or the split partial ---------------------------
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    if (myrow[t] >= R) continue;
+    const int64_t orow = q_row(myrow[t]);
+    if (a.nsplit == 1) {
+      const float inv = l[t] > 0.f ? 1.f / l[t] : 0.f;
+#pragma unroll
+      for (int gp = 0; gp < G; ++gp) {
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = st[t].acc[2 * gp][i] * inv;
+          o[2 * i + 1] = st[t].acc[2 * gp + 1][i] * inv;
+        }
+        const int64_t oi = orow * D + 32 * gp + 8 * r;
+        if (a.out_bf16) {
+          uint4 w;
+          w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+          w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+          w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+          w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + oi) = w;
+        } else {
+          float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + oi);
+          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+      }
+    } else {
+      const int64_t pi = orow * a.part_stride + sp;
+#pragma unroll
+      for (int gp = 0; gp < G; ++gp) {
+        float4 *dst = reinterpret_cast<float4 *>(a.part_acc + pi * D + 32 * gp + 8 * r);
+        dst[0] = make_float4(st[t].acc[2 * gp][0], st[t].acc[2 * gp + 1][0], st[t].acc[2 * gp][1],
+                             st[t].acc[2 * gp + 1][1]);
+        dst[1] = make_float4(st[t].acc[2 * gp][2], st[t].acc[2 * gp + 1][2], st[t].acc[2 * gp][3],
+                             st[t].acc[2 * gp + 1][3]);
+      }
+      if (r == 0) {
+        a.part_ml[pi * 2] = st[t].m;
+        a.part_ml[pi * 2 + 1] = l[t];
+      }
+    }
+  }
+}
+
 // One wave per (sequence, query token, query head) slot, four per work-group:
 // combine the split partials of the row, if the slot holds a query token.
 // Multi-token rows are many and their splits few, so a wave takes a row: the
@@ -625,7 +1007,8 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, 1, false>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2>), grid, dim3(kDirWaves * 64), 0, s, a); break;
     case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, false>), grid, block, 0, s, a); break;
     case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, false>), grid, block, 0, s, a); break;
     case 256: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 2, false>), grid, block, 0, s, a); break;

@@ -299,16 +299,25 @@ tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_he
   if (num_tokens > (int64_t)batch * max_query_len)
     return fail(TQ_ERR_INVALID_ARG, "num_tokens must be <= batch * max_query_len");
   const int64_t g = num_q_heads / hkv;
-  // rows of one (sequence, kv-head): up to 32 in one work-group of 2 row
-  // groups x 4 block groups, up to 64 in 4 x 2, up to 128 in 8 x 1, more in
-  // tiles of 256 (8 x 1, two 16-row tiles per wave)
+  // rows of one (sequence, kv-head): up to 16 or 32 in the direct kernel
+  // (every wave runs all rows against its own block pairs), up to 64 in a
+  // staged work-group of 4 row groups x 2 block groups, up to 128 in 8 x 1,
+  // more in tiles of 256 (8 x 1, two 16-row tiles per wave)
   const int64_t rows = (int64_t)max_query_len * g;
-  const int rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
+  const int rows_per_wg = rows <= 16 ? 16 : rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
   const int64_t row_tiles = (rows + rows_per_wg - 1) / rows_per_wg;
   // prefill-sized tiles (MFMA-heavy per block) walk whole contexts; smaller
   // ones split long contexts at 512 blocks so uneven lengths balance
-  const tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
-                                                     max_context_len, rows_per_wg >= 256 ? 4096 : 512);
+  const int max_split = rows_per_wg >= 256 ? 4096 : 512;
+  tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
+                                               max_context_len, max_split);
+  // a work-group stages its split's block ids in LDS: at most 4096 (staged
+  // kernel) or 1024 (direct kernel)
+  const int max_ids = rows_per_wg <= 32 ? 1024 : 4096;
+  if (sp.split_blocks > max_ids) {
+    sp.split_blocks = max_ids;
+    sp.nsplit = (int)std::max<int64_t>(1, (((int64_t)max_context_len + 15) / 16 + max_ids - 1) / max_ids);
+  }
   if ((int64_t)batch * hkv * row_tiles * sp.nsplit >= (int64_t(1) << 31) ||
       (int64_t)batch * max_query_len * num_q_heads >= (int64_t(1) << 31))
     return fail(TQ_ERR_INVALID_ARG, "launch grid too large");
@@ -415,6 +424,8 @@ tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads
     return fail(TQ_ERR_INVALID_ARG, "max_depth must be in [1, num_groups]");
   if ((int64_t)16 * max_group_blocks > max_context_len)
     return fail(TQ_ERR_INVALID_ARG, "16 * max_group_blocks must be <= max_context_len");
+  if (max_group_blocks > 4096)
+    return fail(TQ_ERR_UNSUPPORTED, "a group's shared range is at most 4096 blocks (cut longer ones into chained groups)");
   p->own = tq::plan_split(batch, hkv, max_context_len);
   const int64_t rows = (int64_t)std::max(1, max_group_size) * g;
   p->rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;

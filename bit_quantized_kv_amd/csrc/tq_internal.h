@@ -70,7 +70,7 @@ struct MultiTokenArgs {
   float qscale;                  // softmax_scale * log2(e) * fp32(1/sqrt(d))
   int32_t max_blocks, batch, hq, hkv, g;
   int32_t max_query_len;         // bound on q_start[b+1] - q_start[b]
-  int32_t rows_per_wg;           // 32, 64, 128 or 256 query rows per work-group
+  int32_t rows_per_wg;           // 16 or 32 (direct kernel), 64, 128 or 256 query rows per work-group
   int32_t row_tiles;             // row tiles per (sequence, kv-head)
   int32_t split_blocks, nsplit;
   int32_t out_bf16;

@@ -231,7 +231,9 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
  *   group_blocks       int32 [num_groups][2]: lo, hi (hi - lo <= max_group_blocks)
  *   group_depth        int32 [num_groups]: the group's depth (< max_depth)
  *   host: num_groups >= 0; when > 0, max_group_size in [1, batch] and
- *   max_depth in [1, num_groups]; 16 * max_group_blocks <= max_context_len.
+ *   max_depth in [1, num_groups]; 16 * max_group_blocks <= max_context_len;
+ *   max_group_blocks <= 4096 (TQ_ERR_UNSUPPORTED beyond: cut longer shared
+ *   ranges into chained groups).
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8.  workspace: device buffer
  * of at least tq_cascade_workspace_bytes (always needed).  MX-FP4 caches
  * return TQ_ERR_UNSUPPORTED.  Asynchronous: the shared-block pass runs on a

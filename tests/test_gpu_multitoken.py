@@ -145,3 +145,45 @@ def test_long_split_walks_more_than_64_blocks_per_wave():
                                  seed=212)
     say("case: multi-token with 1024-block splits (block ids fetched in chunks of 64 per wave)")
     _run(Case(cfg), 40)
+
+
+@pytest.mark.parametrize("d,g,hkv,seed,mmax,split", [
+    (128, 4, 2, 213, 8, None), (128, 8, 1, 214, 2, 3), (128, 1, 3, 215, 16, None), (128, 2, 2, 216, 16, 5),
+    (128, 4, 1, 217, 4, 1), (64, 4, 2, 218, 8, 7), (64, 8, 1, 219, 4, None), (64, 2, 2, 220, 8, 2),
+])
+def test_direct_kernel_small_row_counts(d, g, hkv, seed, mmax, split):
+    """At most 32 rows per (sequence, kv-head): the direct kernel (16- or
+    32-row tiles), ragged query counts (zero included), odd split sizes that
+    end splits inside a block pair, and lone last pairs."""
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=5, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                 ctx_range=(1, 700), seed=seed)
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, mmax + 1, size=5)
+    m[rng.integers(0, 5)] = mmax
+    assert mmax * g <= 32
+    say(f"case: multi-token direct d={d} g={g} hkv={hkv} seed={seed} m={m.tolist()} split={split}")
+    _run(Case(cfg), m)
+
+
+def test_direct_kernel_whole_short_contexts_bf16_and_long_splits():
+    """Direct kernel: query tokens that are the whole (short) context, so the
+    first rows see one key; bf16 output equal to the rounded fp32 output; and
+    1024-block splits, where a wave walks more than the 32 block pairs one
+    wave-wide id load holds."""
+    cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(1, 8),
+                                 seed=221)
+    say("case: multi-token direct, whole short contexts")
+    _run(Case(cfg), 10 ** 6)
+    cfg = workloads.small_config(batch=3, num_q_heads=16, num_kv_heads=4, head_dim=128, ctx_range=(900, 2000),
+                                 seed=222)
+    say("case: multi-token direct, bf16 output")
+    case = Case(cfg)
+    _run(case, 8)
+    _bf16_of(case, 8, None)
+    os.environ["TQ_SPLIT_BLOCKS"] = "1024"
+    cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(9000, 12000),
+                                 seed=223)
+    say("case: multi-token direct, 1024-block splits (block ids fetched in chunks of 32 pairs per wave)")
+    _run(Case(cfg), 8)
