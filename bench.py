@@ -181,6 +181,12 @@ class Bench:
         self.caches[i % self.pool_copies].decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s], c.scale,
                                                  out=self.out)
 
+    def append(self, i, s):
+        """The single-token append of decode step s (one token per sequence)
+        into pool copy i."""
+        ka, va, sa = self.appends[s]
+        self.caches[i % self.pool_copies].quantize_append(ka, va, sa)
+
     def step(self, i):
         """One pass of the whole path: quantize-append batch i into pool copy
         i, then (append one token per sequence and) decode over pool copy i-2."""
@@ -636,6 +642,8 @@ def main():
     q_ms = timed(torch, stream, args.steps, lambda j: bench.quantize(base + j))
     nd = args.steps * c.decode_steps
     d_ms = timed(torch, stream, nd, lambda j: bench.decode(j, j % c.decode_steps))
+    # the single-token appends of the decode steps (one token per sequence), alone
+    a_ms = (timed(torch, stream, nd, lambda j: bench.append(j, j % c.decode_steps)) if bench.appends else None)
 
     kv_logical = sum(bench.decode_bytes(s)[0] for s in range(c.decode_steps)) / c.decode_steps
     kv_unique = sum(bench.decode_bytes(s, unique=True)[0] for s in range(c.decode_steps)) / c.decode_steps
@@ -684,6 +692,9 @@ def main():
         "roofline_other": roof("decode" if dominant == "quantize" else "quantize"),
         "kernel_source_hash": kernel_source_hash(),
     }
+    if a_ms is not None:
+        res["append_1tok_us"] = round(a_ms * 1e3, 2)
+        res["append_1tok_GBps"] = round(bench.append_bytes() / (a_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res))
