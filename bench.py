@@ -277,7 +277,8 @@ def traffic_from_profiles(cfg_name, kernel):
             cands = [(int(k.split("|")[1]), e) for k, e in ents.items() if "quantize_kernel" in k]
             return round(hbm(max(cands, key=lambda x: x[0])[1])) if cands else None
         if kernel == "multitoken":
-            parts = [e for k, e in ents.items() if "multitoken" in k]
+            # the attention launch: the direct or staged kernel and its merge
+            parts = [e for k, e in ents.items() if "multitoken" in k or "mt_direct" in k]
         else:
             # the decode launch: decode kernel and merge, and for cascade decode
             # the shared-block pass too

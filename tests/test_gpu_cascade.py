@@ -87,3 +87,16 @@ def test_full_agentic_sampled():
     seqs = [0, 6, 9, 15, 16, 31]
     say(f"case: cascade agentic: {len(groups)} nested groups of shared blocks; sampled sequences {seqs}")
     _run(case, groups, seqs=seqs)
+
+
+def test_shared_range_longer_than_the_block_id_table_is_refused():
+    """A group's shared range is at most 4096 blocks (a work-group stages its
+    range's block ids in LDS); the host refuses longer ones before any launch,
+    and accepts exactly 4096."""
+    from bit_quantized_kv_amd import Cache
+    from bit_quantized_kv_amd.binding import TqError, tq_cascade_workspace_bytes
+    cache = Cache(0, 128, 2, 16)
+    say("case: cascade workspace query with 4096 and 4097 shared blocks")
+    assert tq_cascade_workspace_bytes(cache.handle, 2, 8, 16 * 4097, 1, 2, 4096, 1) > 0
+    with pytest.raises(TqError):
+        tq_cascade_workspace_bytes(cache.handle, 2, 8, 16 * 4097, 1, 2, 4097, 1)
