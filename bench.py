@@ -59,12 +59,18 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the native sources with comments and whitespace taken out, so
+    that stored counters stay valid across edits of comments only."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_kv_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

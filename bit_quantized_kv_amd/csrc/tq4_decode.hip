@@ -6,7 +6,7 @@
 // values are dequantized in registers.
 //
 // Work-group = (sequence b, kv-head, split) with NW waves.  Each wave takes
-// every NW-th block of the split, two blocks of loads in flight, and keeps an
+// every NW-th block of the split, four blocks of loads in flight, and keeps an
 // online-softmax state; the waves are merged in LDS at the end.  Per 16-token
 // block a wave does:
 //   * one 128-bit load per lane of the key codes (the record places each lane's

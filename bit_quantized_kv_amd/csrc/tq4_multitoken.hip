@@ -3,25 +3,29 @@
 // The query tokens are the last M_b of sequence b's context of T_b tokens and
 // see the keys causally: query token i sees positions t < T_b - M_b + i + 1.
 //
-// Rows are (query token, query head) pairs of one kv-head, token-major.  A
-// work-group of 8 waves takes 128 rows (16 per wave, one MFMA column each) of
-// one (sequence, kv-head) and one split of the key blocks.  The key blocks are
-// dequantized once per work-group and shared through LDS:
-//   * stage k: wave w loads block 8k + w of the split (a ring of four blocks
-//     of 128-bit loads in flight per wave), dequantizes it into the
-//     work-group's LDS stage buffer (keys: the fp16 table entries, in the QK
-//     MFMA's A-operand order; values: code * scale + min in fp16, in the PV
-//     MFMA's A-operand order; key scales), and after one barrier every wave
-//     runs its 16 rows against the 8 blocks of the stage.  Two stage buffers
-//     alternate, so one barrier per stage suffices;
-//   * per block and wave: logits = K_hat (16 tokens x D) times the rotated
-//     query rows (D x 16 rows) with v_mfma_f32_16x16x32_f16, the query split
-//     into fp16 high and low parts (two MFMAs into one accumulator); the key
-//     scale; the causal mask; online softmax in log2 units with lazy rescale;
-//     out^T (channels x rows) += V_hat^T P with v_mfma_f32_16x16x16f16, P
-//     again as fp16 high and low parts.
-// With one split a wave writes its rows; otherwise split partials (max, sum,
-// acc) go to the workspace and a merge kernel combines them per row.
+// Rows are (query token, query head) pairs of one kv-head, token-major.  Two
+// kernels, chosen by the number of rows of a (sequence, kv-head):
+//   * up to 32 (verification of a few tokens): the direct kernel below, where
+//     every wave runs all rows against its own block pairs, dequantizing keys
+//     and values in registers as the decode kernel does;
+//   * more (chunked prefill), and the shared-block pass of cascade decode: the
+//     staged kernel.  A work-group of 8 waves takes 32 to 256 rows of one
+//     (sequence, kv-head) and one split of the key blocks, which are
+//     dequantized once per work-group and shared through LDS.  Stage k: wave w
+//     loads block 8k + w of the split (a ring of four blocks of 128-bit loads
+//     in flight per wave), dequantizes it into the work-group's stage buffer
+//     (keys: the fp16 table entries in the QK A-operand order; values: code *
+//     scale + min in fp16 in the PV A-operand order; key scales), and after
+//     one barrier every wave runs its rows against its pairs of blocks of the
+//     stage.  Two stage buffers alternate, so one barrier per stage suffices.
+// Per pair of blocks and 16-row tile: logits = K_hat (16 tokens x D) times the
+// rotated query rows (D x 16 rows) on v_mfma_f32_16x16x32_f16, the query split
+// into fp16 high and low parts (two MFMAs into one accumulator); the key
+// scale; the causal mask; online softmax in log2 units with lazy rescale;
+// out^T (channels x rows) += V_hat^T P over the pair's 32 tokens on
+// v_mfma_f32_16x16x32_f16, P again as fp16 high and low parts.
+// With one split the rows are written directly; otherwise split partials
+// (max, sum, acc) go to the workspace and a merge kernel combines them per row.
 #include "decode_common.h"
 
 namespace tq {
