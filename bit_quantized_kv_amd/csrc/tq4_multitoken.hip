@@ -23,7 +23,7 @@
 // into fp16 high and low parts (two MFMAs into one accumulator); the key
 // scale; the causal mask; online softmax in log2 units with lazy rescale;
 // out^T (channels x rows) += V_hat^T P over the pair's 32 tokens on
-// v_mfma_f32_16x16x32_f16, P again as fp16 high and low parts.
+// v_mfma_f32_16x16x32_f16, P rounded once to fp16.
 // With one split the rows are written directly; otherwise split partials
 // (max, sum, acc) go to the workspace and a merge kernel combines them per row.
 #include "decode_common.h"
@@ -157,6 +157,16 @@ __device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtPair<D> &slot, 
   }
 }
 
+// The probabilities of a pair of blocks as the PV B operand: each rounded once
+// to fp16, to nearest even (v_cvt_pk_f16_f32).  The relative error is at most
+// 2^-11 and unbiased, the same bound as the fp16 rounding of the dequantized
+// values; the running sum of the softmax stays in fp32.
+__device__ __forceinline__ half8v mt_p_f16(const float (&p)[8]) {
+  typedef float float8v __attribute__((ext_vector_type(8)));
+  const float8v f = {p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
+  return __builtin_convertvector(f, half8v);
+}
+
 // Online softmax over a pair of blocks (8 logits per lane: tokens 4r..4r+3 of
 // each block, column n = lane % 16), with the lazy rescale of softmax_block.
 template <int NT>
@@ -219,7 +229,7 @@ __device__ __forceinline__ void mt_consume_pair(const MtPair<D> &sp, bool has_b,
   }
   const uint2 ka_s = sp.ks[0][r], kb_s = sp.ks[1][r];
   const half2v a01 = as_h2(ka_s.x), a23 = as_h2(ka_s.y), b01 = as_h2(kb_s.x), b23 = as_h2(kb_s.y);
-  half8v ph[TR], pl[TR];
+  half8v ph[TR];
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
     float x[8];
@@ -244,26 +254,13 @@ __device__ __forceinline__ void mt_consume_pair(const MtPair<D> &sp, bool has_b,
     }
     float p[8];
     mt_softmax8<NT>(x, st[t], p);
-    // P = high + low fp16 parts; the residual p - high in one v_fma_mix each
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
-      const half2v l = __builtin_bit_cast(
-          half2v, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(-1.0f, (float)h[0], p[i]),
-                                             __builtin_fmaf(-1.0f, (float)h[1], p[i + 1])));
-      ph[t][i] = h[0];
-      ph[t][i + 1] = h[1];
-      pl[t][i] = l[0];
-      pl[t][i + 1] = l[1];
-    }
+    ph[t] = mt_p_f16(p);
   }
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
     const half8v v8 = __builtin_bit_cast(half8v, sp.v[c][lane]);
 #pragma unroll
     for (int t = 0; t < TR; ++t) st[t].acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, ph[t], st[t].acc[c], 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < TR; ++t) st[t].acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, pl[t], st[t].acc[c], 0, 0, 0);
   }
 }
 
@@ -787,7 +784,7 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
     }
     const half2v a01 = as_h2(ba.ks.x), a23 = as_h2(ba.ks.y), b01 = as_h2(bb.ks.x), b23 = as_h2(bb.ks.y);
     const bool masked = tok0 + 32 > lmin;
-    half8v ph[RT], pl[RT];
+    half8v ph[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       float x[8];
@@ -812,17 +809,7 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
       }
       float p[8];
       mt_softmax8<NT>(x, st[t], p);
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
-        const half2v l = __builtin_bit_cast(
-            half2v, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(-1.0f, (float)h[0], p[i]),
-                                               __builtin_fmaf(-1.0f, (float)h[1], p[i + 1])));
-        ph[t][i] = h[0];
-        ph[t][i + 1] = h[1];
-        pl[t][i] = l[0];
-        pl[t][i + 1] = l[1];
-      }
+      ph[t] = mt_p_f16(p);
     }
     // ---- values: code * scale + min in fp16, both blocks into one operand ----
     const uint4 *vra = reinterpret_cast<const uint4 *>(vm_a) + (lane >> 4) * G;
@@ -847,11 +834,6 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
       for (int t = 0; t < RT; ++t) {
         st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, ph[t], st[t].acc[2 * gp], 0, 0, 0);
         st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, ph[t], st[t].acc[2 * gp + 1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, pl[t], st[t].acc[2 * gp], 0, 0, 0);
-        st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, pl[t], st[t].acc[2 * gp + 1], 0, 0, 0);
       }
     }
   };

@@ -110,6 +110,10 @@ def test_bf16_output_and_split_invariance():
 
 
 def test_one_query_token_matches_decode():
+    """One query token per sequence through the multi-token path equals the
+    decode path up to their one numerical difference: the multi-token kernels
+    round the probabilities once to fp16 (at most 2^-11 relative, unbiased),
+    the decode kernel carries them as fp16 high + low parts."""
     cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(50, 900),
                                  seed=210)
     case = Case(cfg)
@@ -118,7 +122,7 @@ def test_one_query_token_matches_decode():
     ctx = case.w.total_lens.astype(np.int32)
     dec = case.cache.decode(to_dev_bf16(qbits), case.table_dev, to_dev_i32(ctx), int(ctx.max()), cfg.scale)
     torch.cuda.synchronize()
-    assert row_rel_err(out, dec.cpu().numpy()) <= 1e-5
+    assert row_rel_err(out, dec.cpu().numpy()) <= 1e-3
 
 
 @pytest.mark.parametrize("name", ["verify", "prefill"])
