@@ -2,9 +2,8 @@
 import math
 
 import numpy as np
-import pytest
 
-from oracle import attention, layout, lloyd_max, paged, tq4, wht
+from oracle import attention, lloyd_max, paged, tq4, wht
 import workloads
 
 

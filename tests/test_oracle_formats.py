@@ -1,8 +1,5 @@
 """Pins for oracle.fpformats: torch's own conversions, exhaustive tables, ties."""
-import math
-
 import numpy as np
-import pytest
 import torch
 
 from oracle import fpformats as fp
