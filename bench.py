@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
     p.add_argument("--cascade-group-blocks", type=int, default=48,
                    help="cascade: shared ranges are cut into groups of at most this many blocks")
+    p.add_argument("--cascade-group-members", type=int, default=0,
+                   help="cascade: groups are cut into groups of at most this many sequences "
+                        "(default: 32 rows' worth, the direct kernel's tile)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for counter calibration)")
@@ -87,7 +90,7 @@ def copy_calibration():
 
 
 class Bench:
-    def __init__(self, cfg, copies, cascade=False, group_blocks=48):
+    def __init__(self, cfg, copies, cascade=False, group_blocks=48, group_members=None):
         import torch
 
         import workloads
@@ -139,7 +142,9 @@ class Bench:
         self.cascade = None
         if cascade:
             from bit_quantized_kv_amd import CascadeGroups
-            self.cascade = CascadeGroups(c.batch, w.shared_block_groups(w.context_lens_at(0)), max_blocks=group_blocks)
+            g = c.num_q_heads // c.num_kv_heads
+            self.cascade = CascadeGroups(c.batch, w.shared_block_groups(w.context_lens_at(0)), max_blocks=group_blocks,
+                                         max_members=group_members if group_members else max(1, 32 // g))
             for cache in self.caches:
                 cache.cascade_decode(self.q[0], self.table, self.ctx[0], self.max_ctx[0], c.scale, self.cascade,
                                      out=self.out)
@@ -634,7 +639,8 @@ def main():
         cfg = dataclasses.replace(workloads.CONFIGS["llama8b"], name="tq4v2", fmt=2)
     else:
         cfg = workloads.CONFIGS[cfg_name]
-    bench = Bench(cfg, args.copies, cascade=cascade, group_blocks=args.cascade_group_blocks)
+    bench = Bench(cfg, args.copies, cascade=cascade, group_blocks=args.cascade_group_blocks,
+                  group_members=args.cascade_group_members)
     c = bench.cfg
     stream = bench.stream
     for i in range(args.warmup + bench.pool_copies):

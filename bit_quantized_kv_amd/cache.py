@@ -100,15 +100,22 @@ class CascadeGroups:
     block tables agree on blocks lo .. hi - 1; the groups of a sequence must
     cover its first blocks contiguously from 0.  A range longer than
     ``max_blocks`` is cut into chained groups of that many blocks (a group is
-    one unit of parallel work).  Marshalling only: depths, per-sequence block
-    counts and the bounds follow from the list."""
+    one unit of parallel work), and a group of more than ``max_members``
+    sequences (if given) into groups of at most that many over the same range:
+    at most 32 rows (members times query heads per kv-head) per group take the
+    library's direct kernel, which runs every row of a group on each wave.
+    Marshalling only: depths, per-sequence block counts and the bounds follow
+    from the list."""
 
-    def __init__(self, batch, groups, max_blocks=48, device="cuda"):
+    def __init__(self, batch, groups, max_blocks=48, max_members=None, device="cuda"):
         i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=device)
         cut = []
         for members, lo, hi in groups:
-            for s in range(lo, hi, max_blocks):
-                cut.append((members, s, min(hi, s + max_blocks)))
+            members = list(members)
+            step = max_members or max(1, len(members))
+            for m0 in range(0, len(members), step):
+                for s in range(lo, hi, max_blocks):
+                    cut.append((members[m0:m0 + step], s, min(hi, s + max_blocks)))
         groups = cut
         pb = [0] * batch
         depth = [0] * batch

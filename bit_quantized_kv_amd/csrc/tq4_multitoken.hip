@@ -599,7 +599,11 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
 // merged in LDS at the end (two halving rounds).
 constexpr int kDirWaves = 4;
 
-template <int D, int RT>
+// PREFIX (the shared-block pass of cascade decode, groups of at most 32
+// rows): the rows are the (member sequence, query head) pairs of one group,
+// every row sees all the group's blocks, and the results are always partials
+// (at slot slot0 + the group's depth).
+template <int D, int RT, bool PREFIX>
 __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void tq4_mt_direct_kernel(
     MultiTokenArgs a) {
   constexpr int G = D / 32, KS = D / 32, NT = D / 16;
@@ -619,34 +623,63 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const MtTask task = mt_task(a);
   const int b = task.b, kvh = task.kvh, sp = task.sp;
-  const int q0 = a.q_start[b];
-  const int M = a.q_start[b + 1] - q0;
-  const int T = a.ctx[b];
+  // causal: b is a sequence, its query tokens q0 .. q0 + M - 1, and the last
+  // row sees all T keys, the first T - M + 1; prefix: b is a group, q0 its
+  // first member's index into group_seqs, M its size, and every row sees the
+  // group's blocks blk_lo .. T / 16 - 1
+  int q0, M, T, tab_seq, blk_lo = 0, slot = sp;
+  if constexpr (PREFIX) {
+    q0 = a.group_start[b];
+    M = a.group_start[b + 1] - q0;
+    if (M <= 0) return;
+    tab_seq = a.group_seqs[q0];
+    blk_lo = a.group_blocks[2 * b];
+    T = 16 * a.group_blocks[2 * b + 1];
+    slot = a.slot0 + a.group_depth[b];
+  } else {
+    q0 = a.q_start[b];
+    M = a.q_start[b + 1] - q0;
+    T = a.ctx[b];
+    tab_seq = b;
+  }
   const int R = M * a.g;
   if (R <= 0) return;
-  // the last row sees all T keys, the first T - M + 1
+  auto q_row = [&](int row) -> int64_t {
+    const int who = row / a.g, j = row % a.g;
+    const int64_t tok = PREFIX ? (int64_t)a.group_seqs[q0 + who] : (int64_t)(q0 + who);
+    return tok * a.hq + kvh * a.g + j;
+  };
   const int nblk = (T + 15) >> 4;
-  const int blk0 = sp * a.split_blocks;
-  if (blk0 >= nblk) return;
+  const int blk0 = blk_lo + sp * a.split_blocks;
+  if (blk0 >= nblk) {
+    if constexpr (PREFIX) {
+      // an empty group range: its rows get empty partials (max -inf, sum 0),
+      // which the merge weighs 0
+      for (int i = tid; i < R * (D + 2); i += NW * 64) {
+        const int64_t pi = q_row(i / (D + 2)) * a.part_stride + slot;
+        const int c = i % (D + 2);
+        if (c < D) a.part_acc[pi * D + c] = 0.f;
+        else a.part_ml[pi * 2 + (c - D)] = c == D ? kNegInf : 0.f;
+      }
+    }
+    return;
+  }
   const int blk1 = min(nblk, blk0 + a.split_blocks);
   const int npair = (blk1 - blk0 + 1) >> 1;
-  const int lmin = T - M + 1;
+  const int lmin = PREFIX ? T : T - M + 1;
 
   const int n = lane & 15, r = lane >> 4;
   int myrow[RT], lim[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     myrow[t] = 16 * t + n;
-    lim[t] = myrow[t] < R ? T - M + myrow[t] / a.g + 1 : 0;
+    lim[t] = myrow[t] < R ? (PREFIX ? T : T - M + myrow[t] / a.g + 1) : 0;
   }
-  auto q_row = [&](int row) -> int64_t {
-    return (int64_t)(q0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
-  };
 
   // ---- block ids and the first loads ---------------------------------------------
   // lane j < 4 holds the id of block j & 1 of this wave's pair j / 2 (the first
   // loads); the split's ids (at most kDirMaxIds) go to LDS for the refills
-  const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks;
+  const int32_t *btab = a.block_table + (int64_t)tab_seq * a.max_blocks;
   const int my_id_raw = btab[min(blk0 + 2 * (wv + ((lane & 3) >> 1) * NW) + (lane & 1), a.max_blocks - 1)];
   const uint32_t lut_w = tid < 256 ? a.tables->lut2[tid] : 0u;
   int ids[kDirMaxIds / (NW * 64)];
@@ -893,7 +926,7 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
   for (int t = 0; t < RT; ++t) {
     if (myrow[t] >= R) continue;
     const int64_t orow = q_row(myrow[t]);
-    if (a.nsplit == 1) {
+    if (!PREFIX && a.nsplit == 1) {
       const float inv = l[t] > 0.f ? 1.f / l[t] : 0.f;
 #pragma unroll
       for (int gp = 0; gp < G; ++gp) {
@@ -918,7 +951,7 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
         }
       }
     } else {
-      const int64_t pi = orow * a.part_stride + sp;
+      const int64_t pi = orow * a.part_stride + slot;
 #pragma unroll
       for (int gp = 0; gp < G; ++gp) {
         float4 *dst = reinterpret_cast<float4 *>(a.part_acc + pi * D + 32 * gp + 8 * r);
@@ -993,8 +1026,8 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1>), grid, dim3(kDirWaves * 64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1, false>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2, false>), grid, dim3(kDirWaves * 64), 0, s, a); break;
     case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, false>), grid, block, 0, s, a); break;
     case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, false>), grid, block, 0, s, a); break;
     case 256: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 2, false>), grid, block, 0, s, a); break;
@@ -1012,7 +1045,8 @@ hipError_t launch_prefix(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 32: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 2, 1, true>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1, true>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2, true>), grid, dim3(kDirWaves * 64), 0, s, a); break;
     case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, true>), grid, block, 0, s, a); break;
     case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, true>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;

@@ -427,8 +427,12 @@ tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads
   if (max_group_blocks > 4096)
     return fail(TQ_ERR_UNSUPPORTED, "a group's shared range is at most 4096 blocks (cut longer ones into chained groups)");
   p->own = tq::plan_split(batch, hkv, max_context_len);
+  // groups of at most 32 rows take the direct kernel (every wave runs all rows
+  // against its own blocks; the group's block ids, at most 1024, in LDS),
+  // larger ones the staged kernel
   const int64_t rows = (int64_t)std::max(1, max_group_size) * g;
-  p->rows_per_wg = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+  const bool direct = rows <= 32 && max_group_blocks <= 1024;
+  p->rows_per_wg = direct ? (rows <= 16 ? 16 : 32) : rows <= 64 ? 64 : 128;
   p->row_tiles = (int)((rows + p->rows_per_wg - 1) / p->rows_per_wg);
   // one split per group: a group is the unit of parallel work (callers cut
   // long shared ranges into chained groups)

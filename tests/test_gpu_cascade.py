@@ -24,7 +24,7 @@ def _split_env():
         os.environ["TQ_SPLIT_BLOCKS"] = saved
 
 
-def _run(case, groups, seqs=None, ctx=None, rows=None):
+def _run(case, groups, seqs=None, ctx=None, rows=None, max_members=None):
     c, w = case.cfg, case.w
     ranges = case.write_ranges()
     case.quantize(ranges)
@@ -38,7 +38,7 @@ def _run(case, groups, seqs=None, ctx=None, rows=None):
     q = to_dev_bf16(w.query_bits(0))
     from bit_quantized_kv_amd import CascadeGroups
     out = case.cache.cascade_decode(q, case.table_dev, to_dev_i32(ctx), int(ctx.max()), c.scale,
-                                    CascadeGroups(c.batch, groups))
+                                    CascadeGroups(c.batch, groups, max_members=max_members))
     plain = case.cache.decode(q, case.table_dev, to_dev_i32(ctx), int(ctx.max()), c.scale)
     torch.cuda.synchronize()
     out, plain = out.cpu().numpy(), plain.cpu().numpy()
@@ -80,13 +80,29 @@ def test_context_ending_at_the_prefix_and_no_groups():
     _run(Case(cfg), [])
 
 
-def test_full_agentic_sampled():
+@pytest.mark.parametrize("max_members", [None, 3])
+def test_large_group_staged_and_cut(max_members):
+    """A group of 6 sequences at g = 8 (48 rows: the staged kernel), and the
+    same group cut into groups of at most 3 members (24 rows: the direct
+    kernel), with a nested group below it."""
+    cfg = workloads.small_config(batch=7, num_q_heads=8, num_kv_heads=1, head_dim=128, ctx_range=(200, 500),
+                                 shared_seqs=6, shared_tokens=160, seed=307)
+    say(f"case: cascade, a 6-sequence group over 10 shared blocks, max_members={max_members}")
+    _run(Case(cfg), [([0, 1, 2, 3, 4, 5], 0, 6), ([1, 3, 5], 6, 10)], max_members=max_members)
+
+
+@pytest.mark.parametrize("max_members", [None, 8])
+def test_full_agentic_sampled(max_members):
+    """The agentic workload's nested groups as they are (16 sharers: 64 rows,
+    the staged kernel) and cut into 8-sequence groups (32 rows, the direct
+    kernel)."""
     cfg = workloads.CONFIGS["agentic"]
     case = Case(cfg)
     groups = case.w.shared_block_groups()
     seqs = [0, 6, 9, 15, 16, 31]
-    say(f"case: cascade agentic: {len(groups)} nested groups of shared blocks; sampled sequences {seqs}")
-    _run(case, groups, seqs=seqs)
+    say(f"case: cascade agentic: {len(groups)} nested groups of shared blocks, max_members={max_members}; "
+        f"sampled sequences {seqs}")
+    _run(case, groups, seqs=seqs, max_members=max_members)
 
 
 def test_shared_range_longer_than_the_block_id_table_is_refused():
