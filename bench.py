@@ -299,6 +299,23 @@ def traffic_from_profiles(cfg_name, kernel):
         return None
 
 
+def mfma_busy_from_profiles(cfg_name, kernel_prefix):
+    """SQ_VALU_MFMA_BUSY_CYCLES per SIMD-cycle of the kernel whose name starts
+    with ``kernel_prefix``, from the committed counter run; None unless it was
+    taken on the current kernel sources."""
+    path = os.path.join(PROFILES, "mfma_busy.json")
+    try:
+        d = json.load(open(path))
+        if d.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        for k, e in d["workloads"].get(cfg_name, {}).items():
+            if k.startswith(kernel_prefix):
+                return e["mfma_busy"]
+    except Exception:
+        return None
+    return None
+
+
 _SPIN_CYCLES_PER_MS = None
 
 
@@ -563,6 +580,9 @@ def bench_multitoken(args):
         "attention_us": round(a_ms * 1e3, 2),
         "append_us": round(q_ms * 1e3, 2),
         "effective_kv_GBps": round(kv / (a_ms * 1e-3) / 1e9, 1),
+        # the attention kernel's matrix-unit use (committed counters)
+        "attention_mfma_busy": (mfma_busy_from_profiles(args.config, "tq::tq4_mt_direct_kernel")
+                                or mfma_busy_from_profiles(args.config, "tq::tq4_multitoken_kernel")),
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -705,6 +725,9 @@ def main():
         "roofline_other": roof("decode" if dominant == "quantize" else "quantize"),
         "kernel_source_hash": kernel_source_hash(),
     }
+    if c.fmt == 1:
+        # the FP4 decode's matrix-unit use (committed counters)
+        res["decode_mfma_busy"] = mfma_busy_from_profiles(args.config, "tq::mxfp4_decode_kernel")
     if a_ms is not None:
         res["append_1tok_us"] = round(a_ms * 1e3, 2)
         res["append_1tok_GBps"] = round(bench.append_bytes() / (a_ms * 1e-3) / 1e9, 1)
