@@ -191,7 +191,7 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
  * on the device).  num_q_heads a multiple of num_kv_heads (any ratio).
  * Host-checked: max_query_len <= max_context_len, num_tokens <= batch *
  * max_query_len.  workspace: device buffer of at least
- * tq_multitoken_workspace_bytes (NULL allowed when that is 0).  MX-FP4 caches
+ * tq_multitoken_workspace_bytes (NULL allowed when that is 0).  MX-FP4 and TQ4/2 caches
  * return TQ_ERR_UNSUPPORTED.  Asynchronous. */
 tq_status tq_multitoken_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
                                         int64_t num_tokens, int32_t max_query_len, int32_t max_context_len,
@@ -235,7 +235,7 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
  *   max_group_blocks <= 4096 (TQ_ERR_UNSUPPORTED beyond: cut longer shared
  *   ranges into chained groups).
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8.  workspace: device buffer
- * of at least tq_cascade_workspace_bytes (always needed).  MX-FP4 caches
+ * of at least tq_cascade_workspace_bytes (always needed).  MX-FP4 and TQ4/2 caches
  * return TQ_ERR_UNSUPPORTED.  Asynchronous: the shared-block pass runs on a
  * second stream of the handle (created on first use, default priority),
  * forked from `stream` and joined back to it by events before the merge, so
