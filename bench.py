@@ -352,6 +352,13 @@ def timed(torch, stream, launches, enqueue):
     return a.elapsed_time(b) / launches
 
 
+def timed_median(torch, stream, launches, enqueue, regions=3):
+    """Median over ``regions`` timed regions of ``launches`` launches each
+    (the per-kernel figures; the whole-step figure is one region of exactly
+    the requested steps)."""
+    return sorted(timed(torch, stream, launches, enqueue) for _ in range(regions))[regions // 2]
+
+
 FP64_VALU_PEAK_TFLOPS = 78.6
 
 
@@ -543,8 +550,8 @@ def bench_multitoken(args):
     torch.cuda.synchronize()
     base = args.warmup + mb.copies
     step_ms = timed(torch, mb.stream, args.steps, lambda j: mb.step(base + j))
-    a_ms = timed(torch, mb.stream, args.steps, lambda j: mb.attention(base + j))
-    q_ms = timed(torch, mb.stream, args.steps, lambda j: mb.append(base + j))
+    a_ms = timed_median(torch, mb.stream, args.steps, lambda j: mb.attention(base + j))
+    q_ms = timed_median(torch, mb.stream, args.steps, lambda j: mb.append(base + j))
     byts, flops, kv = mb.work()
     t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
     t_mfma = flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
@@ -672,11 +679,11 @@ def main():
     step_ms = timed(torch, stream, args.steps, lambda j: bench.step(base + j))
     # 2. each kernel alone, back to back over the rotating copies (the decode
     #    launch includes its split merge)
-    q_ms = timed(torch, stream, args.steps, lambda j: bench.quantize(base + j))
+    q_ms = timed_median(torch, stream, args.steps, lambda j: bench.quantize(base + j))
     nd = args.steps * c.decode_steps
-    d_ms = timed(torch, stream, nd, lambda j: bench.decode(j, j % c.decode_steps))
+    d_ms = timed_median(torch, stream, nd, lambda j: bench.decode(j, j % c.decode_steps))
     # the single-token appends of the decode steps (one token per sequence), alone
-    a_ms = (timed(torch, stream, nd, lambda j: bench.append(j, j % c.decode_steps)) if bench.appends else None)
+    a_ms = (timed_median(torch, stream, nd, lambda j: bench.append(j, j % c.decode_steps)) if bench.appends else None)
 
     kv_logical = sum(bench.decode_bytes(s)[0] for s in range(c.decode_steps)) / c.decode_steps
     kv_unique = sum(bench.decode_bytes(s, unique=True)[0] for s in range(c.decode_steps)) / c.decode_steps
