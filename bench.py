@@ -644,7 +644,7 @@ def torch_int16():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(the decode shards by sequence or kv-head with no exchange).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
