@@ -154,6 +154,7 @@ def test_long_split_walks_more_than_64_blocks_per_wave():
 @pytest.mark.parametrize("d,g,hkv,seed,mmax,split", [
     (128, 4, 2, 213, 8, None), (128, 8, 1, 214, 2, 3), (128, 1, 3, 215, 16, None), (128, 2, 2, 216, 16, 5),
     (128, 4, 1, 217, 4, 1), (64, 4, 2, 218, 8, 7), (64, 8, 1, 219, 4, None), (64, 2, 2, 220, 8, 2),
+    (128, 1, 2, 224, 32, None), (64, 1, 1, 225, 32, 3),
 ])
 def test_direct_kernel_small_row_counts(d, g, hkv, seed, mmax, split):
     """At most 32 rows per (sequence, kv-head): the direct kernel (16- or

@@ -182,3 +182,13 @@ def test_full_longprefix_sampled_steps():
         err = row_rel_err(np.array([gpu_outs[step][b, h] for b, h in rows]), np.array([ref[b, h] for b, h in rows]))
         say(f"  step {step}: max rel err {err:.2e}")
         assert err <= TOL
+
+
+def test_longest_split_per_wave():
+    """512-block splits: a wave of the decode kernel walks 64 blocks, the most
+    one wave-wide block-id load holds; contexts of 9000 to 12000 tokens."""
+    os.environ["TQ_SPLIT_BLOCKS"] = "512"
+    cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(9000, 12000),
+                                 seed=116)
+    say("case: decode with 512-block splits (64 blocks per wave)")
+    _check_case(Case(cfg))
