@@ -157,7 +157,10 @@ tq_status tq_decode_workspace_bytes(const tq_cache *cache, int32_t batch, int32_
  * with q~ the rotated query (TQ4: H_D q; MX-FP4: its e4m3 code values) and
  * k_hat, v_hat the dequantized cache rows of kv-head h / g.  The keys are
  * compared in the rotated domain, which leaves q . k unchanged ([TQ-AMD]
- * section 4).  Split-K over the context with a log-sum-exp merge.
+ * section 4).  Split-K over the context with a log-sum-exp merge; the split
+ * size follows from the sizes (the environment variable TQ_SPLIT_BLOCKS, 1 to
+ * 512 blocks, overrides it for tests; multi-token attention reads it too, 1 to
+ * 4096, capped at what the chosen kernel stages).
  * q: device bf16 [batch][num_q_heads][head_dim]; out: device fp32 or bf16
  * (out_dtype) of the same shape; block_table: device int32
  * [batch][max_blocks]; context_lens: device int32 [batch], each in
