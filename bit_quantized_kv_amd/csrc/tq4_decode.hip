@@ -367,7 +367,8 @@ hipError_t launch_tq4_decode(int d, int vbits, const DecodeArgs &a, hipStream_t 
   return d == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }
 
-hipError_t launch_tq4_cascade_decode(int d, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_tq4_cascade_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s) {
+  if (vbits == 2) return d == 128 ? launch_d<128, true, 2>(a, s) : launch_d<64, true, 2>(a, s);
   return d == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
 }
 

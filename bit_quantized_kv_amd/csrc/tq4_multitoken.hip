@@ -1,5 +1,6 @@
-// TQ4/4 attention of several query tokens per sequence over the 4-bit paged
-// cache: chunked prefill of new tokens, or the verification of proposed tokens.
+// TQ4/4 (and TQ4/2) attention of several query tokens per sequence over the
+// 4-bit-key paged cache: chunked prefill of new tokens, or the verification of
+// proposed tokens.
 // The query tokens are the last M_b of sequence b's context of T_b tokens and
 // see the keys causally: query token i sees positions t < T_b - M_b + i + 1.
 //
@@ -54,28 +55,68 @@ __device__ __forceinline__ uint32_t mt_word(const uint4 &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 __device__ __forceinline__ uint32_t mt_word(const uint2 &v, int i) { return i == 0 ? v.x : v.y; }
+__device__ __forceinline__ uint32_t mt_word(uint32_t v, int) { return v; }
+
+// Value-code words per lane: 4-bit values, one per 32-channel group; 2-bit
+// values (TQ4/2), one per group pair.
+template <int D, int VB>
+struct MtVTile {
+  typedef typename MtTile<D>::T T;
+};
+template <>
+struct MtVTile<128, 2> {
+  typedef uint2 T;
+};
+template <>
+struct MtVTile<64, 2> {
+  typedef uint32_t T;
+};
+
+// Record bytes of one (block, kv-head).
+template <int D, int VB>
+constexpr int mt_rec_bytes() {
+  return 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * (D / 32);
+}
+
+// The value codes of channel group gp as bytes 0000cccc: `lo` the even
+// channels, `hi` the odd ones (bytes = tokens 4r + 0..3).  2-bit: the group
+// pair's word holds group 2w in bits 0-3 of each byte and 2w + 1 in bits 4-7,
+// the even channel in the lower two bits.
+template <int VB, typename VT>
+__device__ __forceinline__ void mt_value_codes(const VT &vq, int gp, uint32_t &lo, uint32_t &hi) {
+  if constexpr (VB == 4) {
+    const uint32_t w = mt_word(vq, gp);
+    lo = w & 0x0F0F0F0Fu;
+    hi = (w >> 4) & 0x0F0F0F0Fu;
+  } else {
+    const uint32_t w = mt_word(vq, gp >> 1) >> (4 * (gp & 1));
+    lo = w & 0x03030303u;
+    hi = (w >> 2) & 0x03030303u;
+  }
+}
 
 template <bool HI_WORD>
 __device__ __forceinline__ half2v mt_codes_f16(uint32_t bytes) {
   return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
 }
 
-template <int D>
+template <int D, int VB>
 struct MtBlk {
   typename MtTile<D>::T kq;
   uint2 ks;
-  typename MtTile<D>::T vq;
+  typename MtVTile<D, VB>::T vq;
   uint32_t vmw;
 };
 
-template <int D>
-__device__ __forceinline__ void mt_load_blk(MtBlk<D> &o, const uint8_t *rec, int lane) {
+template <int D, int VB>
+__device__ __forceinline__ void mt_load_blk(MtBlk<D, VB> &o, const uint8_t *rec, int lane) {
   constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + P16;
+  constexpr int VW = VB == 4 ? G : G / 2;  // value-code words per lane
+  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + 64 * 4 * VW;
   const int r = lane >> 4, c = lane & 15;
   o.kq = *reinterpret_cast<const typename MtTile<D>::T *>(rec + lane * Q);
   o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
-  o.vq = *reinterpret_cast<const typename MtTile<D>::T *>(rec + OFF_VC + lane * (4 * G));
+  o.vq = *reinterpret_cast<const typename MtVTile<D, VB>::T *>(rec + OFF_VC + lane * (4 * VW));
   o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
 }
 
@@ -111,8 +152,8 @@ __device__ __forceinline__ MtTask mt_task(const MultiTokenArgs &a) {
 // pair; `lone`: the block is the last of the stage and unpaired, so the other
 // half's values are cleared (their probabilities are 0, and 0 * NaN would
 // not be).
-template <int D>
-__device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtPair<D> &slot, int half, bool lone,
+template <int D, int VB>
+__device__ __forceinline__ void mt_produce(const MtBlk<D, VB> &bk, MtPair<D> &slot, int half, bool lone,
                                            const uint32_t *s_lut, uint32_t *vm_slot, int lane, bool tail,
                                            uint32_t vm_keep) {
   constexpr int G = D / 32, KS = D / 32;
@@ -136,9 +177,9 @@ __device__ __forceinline__ void mt_produce(const MtBlk<D> &bk, MtPair<D> &slot, 
   const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
 #pragma unroll
   for (int gp = 0; gp < G; ++gp) {
-    const uint32_t w = mt_word(bk.vq, gp);
     const uint4 vm = vm_row[gp];
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    uint32_t lo, hi;
+    mt_value_codes<VB>(bk.vq, gp, lo, hi);
     const half2v sc01 = as_h2(vm.x), sc23 = as_h2(vm.y);
     const half2v mn01 = as_h2(vm.z), mn23 = as_h2(vm.w);
     const half2v e01 = __builtin_elementwise_fma(mt_codes_f16<false>(lo), sc01, mn01);
@@ -274,10 +315,10 @@ __device__ __forceinline__ void mt_consume_pair(const MtPair<D> &sp, bool has_b,
 // the (member sequence, query head) pairs of one group of sequences that share
 // their leading blocks; every row sees all the shared tokens, which are read
 // once for the whole group; the results are always partials.
-template <int D, int NRG, int TR, bool PREFIX>
+template <int D, int NRG, int TR, bool PREFIX, int VB>
 __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiTokenArgs a) {
   constexpr int G = D / 32, KS = D / 32, NT = D / 16;
-  constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
+  constexpr int REC = mt_rec_bytes<D, VB>();
   constexpr int NW = kMtWaves;
   constexpr int NBG = NW / NRG;
   constexpr int RW = 16 * TR * NRG;  // rows per work-group
@@ -398,15 +439,15 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     const int ta = (T & 15) - (rr + 2 * (w & 1)), tb = ta - 1;
     tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
   }
-  MtBlk<D> b0, b1, b2, b3;
+  MtBlk<D, VB> b0, b1, b2, b3;
   if (mine > 0) {
-    mt_load_blk<D>(b0, first_rec(0), lane);
+    mt_load_blk<D, VB>(b0, first_rec(0), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(b1, first_rec(1), lane);
+    mt_load_blk<D, VB>(b1, first_rec(1), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(b2, first_rec(2), lane);
+    mt_load_blk<D, VB>(b2, first_rec(2), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(b3, first_rec(3), lane);
+    mt_load_blk<D, VB>(b3, first_rec(3), lane);
   }
 
   // ---- the row group's 16 TR rotated, scaled query rows: fp16 high and low ------
@@ -462,16 +503,16 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
 
   uint32_t *vm_slot = s_vm[wv];
   const int nstage = (nb + NW - 1) / NW;
-  auto stage = [&](MtBlk<D> &buf, int k) {
+  auto stage = [&](MtBlk<D, VB> &buf, int k) {
     MtPair<D>(&cur)[NW / 2] = s_stage[k & 1];
     const int first = blk0 + k * NW;
     const int cnt = min(NW, blk1 - first);
     if (k < mine) {
       const int blk = first + wv;
-      mt_produce<D>(buf, cur[wv >> 1], wv & 1, (wv & 1) == 0 && wv + 1 == cnt, s_lut, vm_slot, lane,
+      mt_produce<D, VB>(buf, cur[wv >> 1], wv & 1, (wv & 1) == 0 && wv + 1 == cnt, s_lut, vm_slot, lane,
                     blk == tail_blk, tail_keep);
     }
-    mt_load_blk<D>(buf, rec_of(k + 4), lane);
+    mt_load_blk<D, VB>(buf, rec_of(k + 4), lane);
     __syncthreads();
 #pragma unroll 1
     for (int j = 2 * bg; j < cnt; j += 2 * NBG) {
@@ -603,11 +644,11 @@ constexpr int kDirWaves = 4;
 // rows): the rows are the (member sequence, query head) pairs of one group,
 // every row sees all the group's blocks, and the results are always partials
 // (at slot slot0 + the group's depth).
-template <int D, int RT, bool PREFIX>
+template <int D, int RT, bool PREFIX, int VB>
 __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void tq4_mt_direct_kernel(
     MultiTokenArgs a) {
   constexpr int G = D / 32, KS = D / 32, NT = D / 16;
-  constexpr int REC = 16 * (D / 2) + 32 + 16 * (D / 2) + 64 * G;
+  constexpr int REC = mt_rec_bytes<D, VB>();
   constexpr int NW = kDirWaves;
 
   __shared__ uint32_t s_lut[256];
@@ -712,13 +753,13 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const int ta = (T & 15) - (rr + 2 * (w & 1)), tb = ta - 1;
     tail_keep = (ta > 0 ? 0x0000FFFFu : 0u) | (tb > 0 ? 0xFFFF0000u : 0u);
   }
-  MtBlk<D> a0, b0, a1, b1;
+  MtBlk<D, VB> a0, b0, a1, b1;
   if (mine > 0) {
-    mt_load_blk<D>(a0, first_rec(0, 0), lane);
-    mt_load_blk<D>(b0, first_rec(0, 1), lane);
+    mt_load_blk<D, VB>(a0, first_rec(0, 0), lane);
+    mt_load_blk<D, VB>(b0, first_rec(0, 1), lane);
     __asm__ volatile("" ::: "memory");
-    mt_load_blk<D>(a1, first_rec(1, 0), lane);
-    mt_load_blk<D>(b1, first_rec(1, 1), lane);
+    mt_load_blk<D, VB>(a1, first_rec(1, 0), lane);
+    mt_load_blk<D, VB>(b1, first_rec(1, 1), lane);
   }
 
   // ---- the RT 16-row tiles of rotated, scaled query rows: fp16 high and low -----
@@ -768,7 +809,7 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
   uint32_t *vm_a = s_vm[wv][0], *vm_b = s_vm[wv][1];
   const int vm_i = (lane >> 4) * (4 * G) + (lane & (4 * G - 1));
-  auto pair = [&](const MtBlk<D> &ba, const MtBlk<D> &bb, int k) {
+  auto pair = [&](const MtBlk<D, VB> &ba, const MtBlk<D, VB> &bb, int k) {
     const int blk = blk0 + 2 * (wv + k * NW);
     const bool has_b = blk + 1 < blk1;
     const int tok0 = 16 * blk;
@@ -850,9 +891,9 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int gp = 0; gp < G; ++gp) {
       const uint4 ma = vra[gp], mb = vrb[gp];
-      const uint32_t wa = mt_word(ba.vq, gp), wb = mt_word(bb.vq, gp);
-      const uint32_t la = wa & 0x0F0F0F0Fu, ha = (wa >> 4) & 0x0F0F0F0Fu;
-      const uint32_t lb = wb & 0x0F0F0F0Fu, hb = (wb >> 4) & 0x0F0F0F0Fu;
+      uint32_t la, ha, lb, hb;
+      mt_value_codes<VB>(ba.vq, gp, la, ha);
+      mt_value_codes<VB>(bb.vq, gp, lb, hb);
       const half2v ea01 = __builtin_elementwise_fma(mt_codes_f16<false>(la), as_h2(ma.x), as_h2(ma.z));
       const half2v ea23 = __builtin_elementwise_fma(mt_codes_f16<true>(la), as_h2(ma.y), as_h2(ma.w));
       const half2v oa01 = __builtin_elementwise_fma(mt_codes_f16<false>(ha), as_h2(ma.x), as_h2(ma.z));
@@ -871,10 +912,10 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
     }
   };
   // process ring slot (pair k, if it is one of this wave's), then refill it
-  auto run = [&](MtBlk<D> &ba, MtBlk<D> &bb, int k) {
+  auto run = [&](MtBlk<D, VB> &ba, MtBlk<D, VB> &bb, int k) {
     if (k < mine) pair(ba, bb, k);
-    mt_load_blk<D>(ba, rec_of(k + 2, 0), lane);
-    mt_load_blk<D>(bb, rec_of(k + 2, 1), lane);
+    mt_load_blk<D, VB>(ba, rec_of(k + 2, 0), lane);
+    mt_load_blk<D, VB>(bb, rec_of(k + 2, 1), lane);
   };
 #pragma unroll 1
   for (int k = 0; k < mine; k += 2) {
@@ -1021,16 +1062,16 @@ __global__ __launch_bounds__(256) void multitoken_merge_kernel(MultiTokenArgs a)
   }
 }
 
-template <int D>
+template <int D, int VB>
 hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1, false>), grid, dim3(kDirWaves * 64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2, false>), grid, dim3(kDirWaves * 64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, false>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, false>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 2, false>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1, false, VB>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2, false, VB>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, false, VB>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, false, VB>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 2, false, VB>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -1040,15 +1081,15 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int VB>
 hipError_t launch_prefix(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
   const dim3 grid((unsigned)wgs), block(kMtWaves * 64);
   switch (a.rows_per_wg) {
-    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1, true>), grid, dim3(kDirWaves * 64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2, true>), grid, dim3(kDirWaves * 64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, true>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, true>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 1, true, VB>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tq4_mt_direct_kernel<D, 2, true, VB>), grid, dim3(kDirWaves * 64), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 4, 1, true, VB>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((tq4_multitoken_kernel<D, 8, 1, true, VB>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1056,12 +1097,14 @@ hipError_t launch_prefix(const MultiTokenArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_tq4_multitoken(int d, const MultiTokenArgs &a, hipStream_t s) {
-  return d == 128 ? launch_mt<128>(a, s) : launch_mt<64>(a, s);
+hipError_t launch_tq4_multitoken(int d, int vbits, const MultiTokenArgs &a, hipStream_t s) {
+  if (vbits == 2) return d == 128 ? launch_mt<128, 2>(a, s) : launch_mt<64, 2>(a, s);
+  return d == 128 ? launch_mt<128, 4>(a, s) : launch_mt<64, 4>(a, s);
 }
 
-hipError_t launch_prefix_attention(int d, const MultiTokenArgs &a, hipStream_t s) {
-  return d == 128 ? launch_prefix<128>(a, s) : launch_prefix<64>(a, s);
+hipError_t launch_prefix_attention(int d, int vbits, const MultiTokenArgs &a, hipStream_t s) {
+  if (vbits == 2) return d == 128 ? launch_prefix<128, 2>(a, s) : launch_prefix<64, 2>(a, s);
+  return d == 128 ? launch_prefix<128, 4>(a, s) : launch_prefix<64, 4>(a, s);
 }
 
 }  // namespace tq

@@ -287,8 +287,8 @@ struct MtPlan {
 tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads, int64_t num_tokens,
                           int32_t max_query_len, int32_t max_context_len, MtPlan *p) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
-  if (cache->desc.format != TQ_FORMAT_TQ4)
-    return fail(TQ_ERR_UNSUPPORTED, "multi-token attention is built for the TQ4/4 format");
+  if (cache->desc.format == TQ_FORMAT_MXFP4)
+    return fail(TQ_ERR_UNSUPPORTED, "multi-token attention is built for the TQ4/4 and TQ4/2 formats");
   const int hkv = cache->desc.num_kv_heads;
   if (batch < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0)
     return fail(TQ_ERR_INVALID_ARG, "batch, num_tokens, max_query_len and max_context_len must be >= 0");
@@ -390,7 +390,7 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
   a.part_stride = p.split.nsplit;
   a.slot0 = 0;
   a.out_bf16 = out_dtype == TQ_OUT_BF16;
-  hipError_t e = tq::launch_tq4_multitoken(d, a, static_cast<hipStream_t>(stream));
+  hipError_t e = tq::launch_tq4_multitoken(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "multi-token attention launch");
   return TQ_OK;
 }
@@ -407,8 +407,8 @@ tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads
                        int32_t num_groups, int32_t max_group_size, int32_t max_group_blocks, int32_t max_depth,
                        CascadePlan *p) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
-  if (cache->desc.format != TQ_FORMAT_TQ4)
-    return fail(TQ_ERR_UNSUPPORTED, "cascade decode is built for the TQ4/4 format");
+  if (cache->desc.format == TQ_FORMAT_MXFP4)
+    return fail(TQ_ERR_UNSUPPORTED, "cascade decode is built for the TQ4/4 and TQ4/2 formats");
   const int hkv = cache->desc.num_kv_heads;
   if (batch < 0 || max_context_len < 0 || num_groups < 0 || max_group_blocks < 0 || max_depth < 0)
     return fail(TQ_ERR_INVALID_ARG,
@@ -531,7 +531,7 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
     e = hipEventRecord(cache->fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(cache->aux, cache->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "cascade fork");
-    e = tq::launch_prefix_attention(d, m, cache->aux);
+    e = tq::launch_prefix_attention(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, m, cache->aux);
     if (e != hipSuccess) return hip_fail(e, "shared-block attention launch");
     e = hipEventRecord(cache->join, cache->aux);
     if (e != hipSuccess) return hip_fail(e, "cascade join record");
@@ -558,7 +558,7 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
   a.first_blk = seq_prefix_blocks;
   a.depth = seq_depth;
   a.part_stride = p.part_stride;
-  e = tq::launch_tq4_cascade_decode(d, a, s);
+  e = tq::launch_tq4_cascade_decode(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, s);
   if (e != hipSuccess) return hip_fail(e, "cascade decode launch");
   if (num_groups > 0) {
     e = hipStreamWaitEvent(s, cache->join, 0);

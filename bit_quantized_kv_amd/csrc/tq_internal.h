@@ -94,9 +94,9 @@ hipError_t launch_tq4_decode(int d, int vbits, const DecodeArgs &a, hipStream_t 
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
-hipError_t launch_tq4_multitoken(int d, const MultiTokenArgs &a, hipStream_t s);
-hipError_t launch_prefix_attention(int d, const MultiTokenArgs &a, hipStream_t s);
-hipError_t launch_tq4_cascade_decode(int d, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_tq4_multitoken(int d, int vbits, const MultiTokenArgs &a, hipStream_t s);
+hipError_t launch_prefix_attention(int d, int vbits, const MultiTokenArgs &a, hipStream_t s);
+hipError_t launch_tq4_cascade_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_cascade_merge(int d, const DecodeArgs &a, hipStream_t s);
 size_t calibrate_workspace_bytes(int64_t layers, int64_t rows, int d);
 hipError_t launch_calibrate(int d, int layers, int64_t rows, const uint16_t *k, const uint16_t init_f16[16],

@@ -1,6 +1,6 @@
 /*
- * tq.h - 4-bit paged KV cache (TQ4/4 and MX-FP4) and decode attention that
- * reads the compressed cache, for AMD Instinct MI355X (gfx950).
+ * tq.h - 4-bit paged KV cache (TQ4/4, TQ4/2 and MX-FP4) and decode attention
+ * that reads the compressed cache, for AMD Instinct MI355X (gfx950).
  *
  * C ABI.  Plain pointers and sizes only; every device pointer is a HIP device
  * address, every `stream` argument is a hipStream_t (NULL = the legacy default
@@ -194,8 +194,8 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
  * on the device).  num_q_heads a multiple of num_kv_heads (any ratio).
  * Host-checked: max_query_len <= max_context_len, num_tokens <= batch *
  * max_query_len.  workspace: device buffer of at least
- * tq_multitoken_workspace_bytes (NULL allowed when that is 0).  MX-FP4 and TQ4/2 caches
- * return TQ_ERR_UNSUPPORTED.  Asynchronous. */
+ * tq_multitoken_workspace_bytes (NULL allowed when that is 0).  TQ4/4 and
+ * TQ4/2 caches; MX-FP4 caches return TQ_ERR_UNSUPPORTED.  Asynchronous. */
 tq_status tq_multitoken_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
                                         int64_t num_tokens, int32_t max_query_len, int32_t max_context_len,
                                         size_t *bytes);
@@ -238,12 +238,12 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
  *   max_group_blocks <= 4096 (TQ_ERR_UNSUPPORTED beyond: cut longer shared
  *   ranges into chained groups).
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8.  workspace: device buffer
- * of at least tq_cascade_workspace_bytes (always needed).  MX-FP4 and TQ4/2 caches
- * return TQ_ERR_UNSUPPORTED.  Asynchronous: the shared-block pass runs on a
- * second stream of the handle (created on first use, default priority),
- * forked from `stream` and joined back to it by events before the merge, so
- * the call is ordered on `stream` like the others; calls on one handle from
- * several streams at once are not supported. */
+ * of at least tq_cascade_workspace_bytes (always needed).  TQ4/4 and TQ4/2
+ * caches; MX-FP4 caches return TQ_ERR_UNSUPPORTED.  Asynchronous: the
+ * shared-block pass runs on a second stream of the handle (created on first
+ * use, default priority), forked from `stream` and joined back to it by events
+ * before the merge, so the call is ordered on `stream` like the others; calls
+ * on one handle from several streams at once are not supported. */
 tq_status tq_cascade_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
                                      int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
                                      int32_t max_group_blocks, int32_t max_depth, size_t *bytes);

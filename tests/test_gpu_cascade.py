@@ -68,6 +68,18 @@ def test_small_groups(d, g, hkv, seed, split):
     _run(Case(cfg), [([0, 1, 2], 0, 4), ([0, 2], 4, 10), ([4], 0, 3)])
 
 
+@pytest.mark.parametrize("d,g,hkv,seed,split", [(128, 4, 2, 311, None), (64, 8, 1, 312, 4)])
+def test_two_bit_values(d, g, hkv, seed, split):
+    """TQ4/2 caches with nested groups: at g = 4 every group takes the direct
+    kernel; at g = 8 the 6-sequence group's 48 rows take the staged one."""
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=7, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, ctx_range=(200, 600),
+                                 shared_seqs=6, shared_tokens=160, seed=seed, fmt=2)
+    say(f"case: cascade TQ4/2 d={d} g={g} hkv={hkv} seed={seed} split={split}")
+    _run(Case(cfg), [([0, 1, 2, 3, 4, 5], 0, 4), ([0, 2, 4], 4, 10), ([6], 0, 3)])
+
+
 def test_context_ending_at_the_prefix_and_no_groups():
     cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(200, 400),
                                  shared_seqs=2, shared_tokens=192, seed=306)

@@ -1,5 +1,5 @@
-"""GPU parity of multi-token attention over the TQ4/4 cache (chunked prefill,
-verification) against the CPU oracle, through the C ABI: max over rows of
+"""GPU parity of multi-token attention over the TQ4/4 and TQ4/2 caches (chunked
+prefill, verification) against the CPU oracle, through the C ABI: max over rows of
 ||o - o_ref||_inf / ||o_ref||_inf within 2e-3, rows computed by the oracle's
 exact fp64 causal attention over the same (byte-identical) cache."""
 import os
@@ -70,6 +70,24 @@ def test_small_ragged(d, g, hkv, seed, mmax, split):
     m = rng.integers(1, mmax + 1, size=5)
     say(f"case: multi-token small ragged d={d} g={g} hkv={hkv} seed={seed} m={m.tolist()} split={split}")
     _run(Case(cfg), m)
+
+
+@pytest.mark.parametrize("d,g,hkv,seed,m,split", [
+    (128, 4, 2, 221, [3, 8, 1, 5, 8], None),       # at most 32 rows: the direct kernel, two row tiles
+    (128, 8, 1, 222, [2, 1, 2, 0, 2], None),       # at most 16 rows: the direct kernel, one row tile
+    (128, 8, 1, 223, [8, 3, 5, 7, 1], 8),          # 64 rows: the staged kernel, 8-block splits
+    (128, 4, 2, 224, [30, 12, 1, 25, 9], None),    # 120 rows: the staged kernel, 128-row tiles
+    (64, 8, 1, 225, [32, 5, 17, 1, 26], 16),       # 256 rows at D = 64
+    (64, 2, 2, 226, [16, 4, 9, 1, 12], None),      # 32 rows at D = 64: the direct kernel
+])
+def test_two_bit_values(d, g, hkv, seed, m, split):
+    """TQ4/2 caches (2-bit values) through both kernels and every row tiling."""
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=5, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                 ctx_range=(60, 700), seed=seed, fmt=2)
+    say(f"case: multi-token TQ4/2 d={d} g={g} hkv={hkv} seed={seed} m={m} split={split}")
+    _run(Case(cfg), np.array(m))
 
 
 def test_prefill_from_the_first_token_and_empty_sequences():

@@ -97,3 +97,20 @@ def test_fp4_edge_lengths():
 def test_full_fp4_sampled():
     say("case: fp4 (B=128, 64/8, D=128, T=16384), sampled sequences")
     _check(Case(workloads.CONFIGS["fp4"]), seqs=[0, 77, 127], rows=[(b, h) for b in (0, 77, 127) for h in range(64)])
+
+
+def test_multi_token_and_cascade_refuse_mxfp4():
+    """Multi-token and cascade attention are built for the TQ4 formats; an
+    MX-FP4 cache is refused (status TQ_ERR_UNSUPPORTED) before any launch."""
+    from bit_quantized_kv_amd import Cache, TqError
+    from bit_quantized_kv_amd.binding import tq_cascade_workspace_bytes
+    cache = Cache(1, 128, 2, 4)
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    say("case: multi-token and cascade calls on an MX-FP4 cache")
+    with pytest.raises(TqError) as e:
+        cache.multitoken(q, i32([0, 1]), 1, i32([[0]]), i32([16]), 16, 0.1)
+    assert e.value.status == 2
+    with pytest.raises(TqError) as e:
+        tq_cascade_workspace_bytes(cache.handle, 1, 8, 16, 1, 1, 1, 1)
+    assert e.value.status == 2

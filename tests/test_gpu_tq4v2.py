@@ -60,16 +60,6 @@ def test_unaligned_skipped_and_single_token_slots():
     assert np.array_equal(gpu, op.pool)
 
 
-def test_other_paths_refuse_tq4v2():
-    from bit_quantized_kv_amd import Cache, TqError
-    cache = Cache(V2, 128, 2, 4)
-    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
-    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
-    with pytest.raises(TqError) as e:
-        cache.multitoken(q, i32([0, 1]), 1, i32([[0]]), i32([16]), 16, 0.1)
-    assert e.value.status == 2
-
-
 def test_full_llama8b_shape():
     cfg = dataclasses.replace(workloads.CONFIGS["llama8b"], name="llama8b-tq4v2", fmt=V2)
     say("case: TQ4/2 on the llama8b layer shape (B=1, 32/8, D=128, T=32768), all rows")
