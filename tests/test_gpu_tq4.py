@@ -118,6 +118,53 @@ def test_unaligned_skipped_and_single_token_slots():
     assert np.array_equal(gpu, op.pool)
 
 
+def test_pool_beyond_4_gib():
+    """A 4.7 GB pool (10^6 blocks x 2 kv-heads x 2336 B): records past byte
+    2^32 are written and read through 64-bit offsets.  One sequence lives on
+    the pool's first blocks, one on its last; their records, decode and
+    multi-token attention match the oracle, which holds the same blocks in a
+    compact pool (block b * 19 + j for the GPU's block j of sequence b)."""
+    from bit_quantized_kv_amd import Cache
+    from gpu_common import to_dev_bf16, to_dev_i32
+    from oracle import attention, paged
+    nblk, hkv, d, g, T = 1_000_000, 2, 128, 4, 300
+    nb = (T + 15) // 16
+    cfg = workloads.small_config(batch=2, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, ctx_range=(T, T),
+                                 seed=131)
+    w = workloads.make(cfg)
+    rng = np.random.default_rng(131)
+    ids = np.stack([rng.permutation(nb), nblk - 1 - rng.permutation(nb)]).astype(np.int32)
+    compact = np.arange(2 * nb, dtype=np.int32).reshape(2, nb)
+    t = np.arange(T)
+    kb = np.concatenate([w.sequence_kv(b)[0][:T] for b in range(2)])
+    vb = np.concatenate([w.sequence_kv(b)[1][:T] for b in range(2)])
+    slots = np.concatenate([ids[b][t // 16] * 16 + t % 16 for b in range(2)]).astype(np.int32)
+    oslots = np.concatenate([compact[b][t // 16] * 16 + t % 16 for b in range(2)]).astype(np.int32)
+    cache = Cache(0, d, hkv, nblk)
+    assert cache.pool.numel() > 2 ** 32
+    say(f"case: pool of {cache.pool.numel() / 1e9:.2f} GB, blocks {ids[1].min()}..{ids[1].max()} at its end")
+    cache.quantize_append(to_dev_bf16(kb), to_dev_bf16(vb), to_dev_i32(slots))
+    sel = torch.from_numpy(ids.ravel().astype(np.int64)).cuda()
+    gpu = cache.pool.view(nblk, hkv, -1)[sel].cpu().numpy()
+    op = paged.PagedPool(0, 2 * nb, hkv, d)
+    op.append(workloads.bf16_bits_to_f32(kb), workloads.bf16_bits_to_f32(vb), oslots)
+    assert np.array_equal(gpu, op.pool), "records past 4 GiB differ from the oracle's"
+    ctx = np.array([T, T], np.int32)
+    qbits = w.query_bits(0)
+    out = cache.decode(to_dev_bf16(qbits), to_dev_i32(ids), to_dev_i32(ctx), T, cfg.scale).cpu().numpy()
+    ref = attention.decode(op, workloads.bf16_bits_to_f32(qbits), compact, ctx, cfg.scale)
+    err = row_rel_err(out.reshape(-1, d), ref.reshape(-1, d))
+    say(f"  decode: max rel err {err:.2e}")
+    assert err <= TOL
+    mq, q_start = w.multi_queries(8)
+    mt = cache.multitoken(to_dev_bf16(mq), to_dev_i32(q_start), 8, to_dev_i32(ids), to_dev_i32(ctx), T,
+                          cfg.scale).float().cpu().numpy()
+    mref = attention.multi_token(op, workloads.bf16_bits_to_f32(mq), q_start, compact, ctx, cfg.scale)
+    err = row_rel_err(mt.reshape(-1, d), mref.reshape(-1, d))
+    say(f"  multi-token: max rel err {err:.2e}")
+    assert err <= TOL
+
+
 def test_custom_key_table():
     table = list(np.linspace(-2.5, 2.5, 16))
     cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(50, 400), seed=112)
