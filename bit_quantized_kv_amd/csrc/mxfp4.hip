@@ -114,7 +114,8 @@ __device__ __forceinline__ void mx_quantize_row(const QuantizeArgs &a, const Row
   }
 }
 
-__global__ __launch_bounds__(kQuantThreads) void mxfp4_quantize_kernel(QuantizeArgs a) {
+template <bool BAL>
+__global__ __launch_bounds__(BAL ? kQuantThreadsBal : kQuantThreads) void mxfp4_quantize_kernel(QuantizeArgs a) {
   using L = QLanes<kD>;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kQuantThreads) void mxfp4_quantize_kernel(QuantizeA
   // keys leave the butterflies with the sign (-1)^popcount(li); folding it into
   // the 1/sqrt(D) factor is exact
   const float ksign = a.rsqrt_d * wht16_sign(li);
-  quantize_loop<kD>(a, wv, tw, li, [] {},
+  quantize_loop<kD, BAL>(a, wv, tw, li, [] {},
                     [&](const RowLoad<kD> &row, int h) { mx_quantize_row(a, row, h, lane, li, tq, ksign); });
 }
 
@@ -339,9 +340,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s) {
   if (a.num_tokens <= 0) return hipSuccess;
-  const int64_t tasks = quantize_tasks(kD, a.num_tokens, a.hkv);
-  const int grid = quantize_grid((const void *)mxfp4_quantize_kernel, kQuantThreads, tasks);
-  hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3(grid), dim3(kQuantThreads), 0, s, a);
+  const QuantGeometry g = quantize_geometry((const void *)mxfp4_quantize_kernel<false>,
+                                            (const void *)mxfp4_quantize_kernel<true>, kD, a.num_tokens, a.hkv);
+  if (g.balanced) hipLaunchKernelGGL(mxfp4_quantize_kernel<true>, dim3(g.grid), dim3(g.threads), 0, s, a);
+  else hipLaunchKernelGGL(mxfp4_quantize_kernel<false>, dim3(g.grid), dim3(g.threads), 0, s, a);
   return hipGetLastError();
 }
 

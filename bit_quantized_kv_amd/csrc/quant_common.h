@@ -198,18 +198,20 @@ __device__ __forceinline__ uint32_t vword(const RowLoad<D> &r, int i) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
 
-// The persistent loop of the quantize kernels.  A work-group task is (chunk of
-// 4 * TPW tokens, kv-head): wave wv codes tokens chunk * 4 * TPW + wv * TPW +
-// tw, so one work-group writes whole 16-token records.  The grid strides
-// through the tasks, tracked as (chunk, head) pairs so the loop needs no 64-bit
-// division.  Two row buffers: every step loads the next task into one (clamped
-// to a valid task, so the loads are unconditional) while coding the other.
-// `stage` runs once, after the first loads are issued (table staging);
-// `code(row, h)` codes one row.
-constexpr int kQuantThreads = 256;  // four waves per work-group
+constexpr int kQuantThreads = 256;       // static loop: four waves per work-group
+constexpr int kQuantThreadsBal = 1024;   // balanced loop: one work-group per compute unit
 
+// The static persistent loop (launches with few tasks per wave).  A
+// work-group task is (chunk of 4 * TPW tokens, kv-head): wave wv codes tokens
+// chunk * 4 * TPW + wv * TPW + tw, so one work-group writes whole 16-token
+// records.  The grid strides through the tasks, tracked as (chunk, head) pairs
+// so the loop needs no 64-bit division.  Two row buffers: every step loads the
+// next task into one (clamped to a valid task, so the loads are unconditional)
+// while coding the other.  `stage` runs once, after the first loads are issued
+// (table staging); `code(row, h)` codes one row.
 template <int D, class Stage, class Code>
-__device__ __forceinline__ void quantize_loop(const QuantizeArgs &a, int wv, int tw, int li, Stage stage, Code code) {
+__device__ __forceinline__ void quantize_loop_static(const QuantizeArgs &a, int wv, int tw, int li, Stage stage,
+                                                     Code code) {
   constexpr int TPW = QLanes<D>::TPW, WG_TOK = 4 * TPW;
   const int64_t chunks = (a.num_tokens + WG_TOK - 1) / WG_TOK;
   const int hkv = a.hkv;
@@ -245,15 +247,94 @@ __device__ __forceinline__ void quantize_loop(const QuantizeArgs &a, int wv, int
   }
 }
 
-// Work-group tasks of a quantize launch.
-inline int64_t quantize_tasks(int d, int64_t num_tokens, int hkv) {
-  const int wg_tok = d == 128 ? 4 * 8 : 4 * 16;
-  return ((num_tokens + wg_tok - 1) / wg_tok) * hkv;
+// The balanced persistent loop (launches with many tasks per wave).  A wave
+// task is (chunk of TPW tokens, kv-head), numbered chunk * Hkv + head: the
+// wave codes tokens chunk * TPW + tw of that head.  One work-group of 16 waves
+// per compute unit takes an equal contiguous range of the tasks; inside it,
+// wave w starts with task w of the range and every later task goes to the wave
+// that asks first (an LDS counter).  With four work-groups per unit and fixed
+// shares, the unit's arbiter favours the oldest: on long launches the first
+// ended at 0.6 of the run while the last ran its end on a partly idle unit;
+// here the waves of a unit end together.  Two row buffers, as above (past the
+// range, the range's first task is loaded again).
+template <int D, class Stage, class Code>
+__device__ __forceinline__ void quantize_loop_balanced(const QuantizeArgs &a, int wv, int tw, int li, Stage stage,
+                                                       Code code) {
+  constexpr int TPW = QLanes<D>::TPW;
+  __shared__ int s_next;
+  const uint32_t hkv = (uint32_t)a.hkv;
+  const int64_t tasks = (a.num_tokens + TPW - 1) / TPW * hkv;
+  // this work-group's range [lo, lo + count) and its first task as (chunk c0,
+  // head h0); 32-bit arithmetic whenever the task count allows it
+  int64_t c0;
+  int count, h0;
+  if (tasks <= 0x7FFFFFFF) {
+    const uint32_t t32 = (uint32_t)tasks, g = gridDim.x, b = blockIdx.x;
+    const uint32_t q = t32 / g, r = t32 % g;
+    const uint32_t lo = b * q + (b < r ? b : r);
+    count = (int)(q + (b < r ? 1u : 0u));
+    c0 = lo / hkv;
+    h0 = (int)(lo % hkv);
+  } else {
+    const int64_t g = gridDim.x, b = blockIdx.x, q = tasks / g, r = tasks % g;
+    const int64_t lo = b * q + (b < r ? b : r);
+    count = (int)(q + (b < r ? 1 : 0));
+    c0 = lo / hkv;
+    h0 = (int)(lo - c0 * hkv);
+  }
+  // task n of the range as (first token, head); n past the range: task 0
+  auto locate = [&](int n, int64_t &t0, int &h) {
+    const uint32_t m = (uint32_t)h0 + (uint32_t)(n < count ? n : 0);
+    t0 = (c0 + m / hkv) * TPW;
+    h = (int)(m % hkv);
+  };
+  auto grab = [&]() {
+    int x = 0;
+    if ((threadIdx.x & 63) == 0) x = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(x);
+  };
+  int n = wv, h;
+  int64_t t0;
+  locate(n, t0, h);
+  RowLoad<D> ra, rb;
+  load_row<D>(ra, a, t0, h, tw, li);
+  if (threadIdx.x == 0) s_next = (int)(blockDim.x >> 6);
+  stage();
+  __syncthreads();
+  while (n < count) {
+    int n2 = grab(), h2;
+    int64_t t2;
+    locate(n2, t2, h2);
+    load_row<D>(rb, a, t2, h2, tw, li);
+    code(ra, h);
+    if (n2 >= count) break;
+    n = grab();
+    locate(n, t0, h);
+    load_row<D>(ra, a, t0, h, tw, li);
+    code(rb, h2);
+  }
 }
 
-// Launch geometry of the persistent quantize kernels: enough work-groups to
-// fill every compute unit at the kernel's occupancy, each taking work-group
-// tasks with a stride of the grid size.
-int quantize_grid(const void *kernel, int threads, int64_t tasks);
+// The loop a launch runs: BAL selects the balanced one.
+template <int D, bool BAL, class Stage, class Code>
+__device__ __forceinline__ void quantize_loop(const QuantizeArgs &a, int wv, int tw, int li, Stage stage, Code code) {
+  if constexpr (BAL) quantize_loop_balanced<D>(a, wv, tw, li, stage, code);
+  else quantize_loop_static<D>(a, wv, tw, li, stage, code);
+}
+
+// Launch geometry of a quantize launch.  Static loop: work-group tasks of
+// 4 * TPW tokens and one kv-head, as many work-groups as fit at once (at most
+// one per task), 4 waves each.  Balanced loop, when there are at least 32
+// wave tasks (TPW tokens, one kv-head) per wave slot of the chip (16 per
+// compute unit): one work-group of 16 waves per compute unit.  Measured: the
+// balanced loop takes 8% off launches with 50 and more tasks per wave, is even
+// at 64 on a ragged batch, and costs 4% at 8, where the counter's round trips
+// outweigh the skew it removes.
+struct QuantGeometry {
+  bool balanced;
+  int grid, threads;
+};
+QuantGeometry quantize_geometry(const void *kernel_static, const void *kernel_balanced, int d, int64_t num_tokens,
+                                int hkv);
 
 }  // namespace tq

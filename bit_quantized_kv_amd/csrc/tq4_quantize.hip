@@ -20,6 +20,9 @@
 //   * persistent work-groups: each takes (32- or 64-token chunk, kv-head)
 //     tasks, so one work-group writes whole 16-token records, and every wave
 //     loads its next task before coding the current one.
+#include <cstdlib>
+#include <cstring>
+
 #include "quant_common.h"
 
 namespace tq {
@@ -197,8 +200,8 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
   }
 }
 
-template <int D, int VB>
-__global__ __launch_bounds__(kQuantThreads) void tq4_quantize_kernel(QuantizeArgs a) {
+template <int D, int VB, bool BAL>
+__global__ __launch_bounds__(BAL ? kQuantThreadsBal : kQuantThreads) void tq4_quantize_kernel(QuantizeArgs a) {
   using L = QLanes<D>;
   __shared__ float2 s_bins[kMaxBins];
   __shared__ float s_recip[1024];
@@ -208,10 +211,11 @@ __global__ __launch_bounds__(kQuantThreads) void tq4_quantize_kernel(QuantizeArg
   const int li = L::li(lane), tw = L::tw(lane), tq = tw & 3;
   const float bin_a = a.bins.a, bin_b = a.bins.b - 0.5f;  // v_cvt_pk_u8 rounds: floor via -0.5
   const float sigma = wht16_sign(li);
-  quantize_loop<D>(a, wv, tw, li,
+  quantize_loop<D, BAL>(a, wv, tw, li,
                    [&] {
-                     for (int i = threadIdx.x; i < kMaxBins; i += kQuantThreads) s_bins[i] = a.tables->bins[i];
-                     for (int i = threadIdx.x; i < 1024; i += kQuantThreads) s_recip[i] = a.tables->recip[i];
+                     constexpr int NT = BAL ? kQuantThreadsBal : kQuantThreads;
+                     for (int i = threadIdx.x; i < kMaxBins; i += NT) s_bins[i] = a.tables->bins[i];
+                     for (int i = threadIdx.x; i < 1024; i += NT) s_recip[i] = a.tables->recip[i];
                      __syncthreads();
                    },
                    [&](const RowLoad<D> &row, int h) {
@@ -221,34 +225,80 @@ __global__ __launch_bounds__(kQuantThreads) void tq4_quantize_kernel(QuantizeArg
 
 }  // namespace
 
-int quantize_grid(const void *kernel, int threads, int64_t tasks) {
-  static int cached_dev = -1, cached_cus = 0;
+namespace {
+
+// Work-groups of `kernel` (at `threads` per work-group) resident per compute
+// unit, and the compute units of the current device; remembered per host
+// thread, so a launch makes no runtime query after the first of its kind.
+struct QuantOccupancy {
+  int dev = -1, cus = 0;
+  const void *kernel[8] = {};
+  int per_cu[8] = {};
+};
+
+int resident_per_cu(QuantOccupancy &o, const void *kernel, int threads, int fallback) {
+  for (int i = 0; i < 8; ++i)
+    if (o.kernel[i] == kernel) return o.per_cu[i];
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || per <= 0)
+    per = fallback;
+  for (int i = 0; i < 8; ++i)
+    if (!o.kernel[i]) {
+      o.kernel[i] = kernel;
+      o.per_cu[i] = per;
+      break;
+    }
+  return per;
+}
+
+}  // namespace
+
+QuantGeometry quantize_geometry(const void *kernel_static, const void *kernel_balanced, int d, int64_t num_tokens,
+                                int hkv) {
+  thread_local QuantOccupancy occ;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (dev != cached_dev) {
+  if (dev != occ.dev) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached_cus = cus;
-    cached_dev = dev;
+    occ = QuantOccupancy{};
+    occ.dev = dev;
+    occ.cus = cus;
   }
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
-    per_cu = 2;
-  const int64_t cap = (int64_t)cached_cus * per_cu;
-  return (int)(tasks < cap ? tasks : cap);
+  const int tpw = d == 128 ? 8 : 16;
+  const int64_t wave_tasks = (num_tokens + tpw - 1) / tpw * hkv;
+  bool balanced = wave_tasks >= (int64_t)32 * (kQuantThreadsBal / 64) * occ.cus;
+  // override for tests: TQ_QUANT_LOOP=static or balanced
+  if (const char *env = std::getenv("TQ_QUANT_LOOP")) {
+    if (std::strcmp(env, "static") == 0) balanced = false;
+    if (std::strcmp(env, "balanced") == 0) balanced = true;
+  }
+  QuantGeometry g;
+  g.balanced = balanced;
+  if (balanced) {
+    g.threads = kQuantThreadsBal;
+    g.grid = occ.cus * resident_per_cu(occ, kernel_balanced, kQuantThreadsBal, 1);
+    return g;
+  }
+  const int64_t wg_tasks = (num_tokens + 4 * tpw - 1) / (4 * tpw) * hkv;
+  const int64_t cap = (int64_t)occ.cus * resident_per_cu(occ, kernel_static, kQuantThreads, 2);
+  g.threads = kQuantThreads;
+  g.grid = (int)(wg_tasks < cap ? wg_tasks : cap);
+  return g;
 }
 
 template <int D, int VB>
-void launch_q(const QuantizeArgs &a, int64_t tasks, hipStream_t s) {
-  const int grid = quantize_grid((const void *)tq4_quantize_kernel<D, VB>, kQuantThreads, tasks);
-  hipLaunchKernelGGL((tq4_quantize_kernel<D, VB>), dim3(grid), dim3(kQuantThreads), 0, s, a);
+void launch_q(const QuantizeArgs &a, hipStream_t s) {
+  const QuantGeometry g = quantize_geometry((const void *)tq4_quantize_kernel<D, VB, false>,
+                                            (const void *)tq4_quantize_kernel<D, VB, true>, D, a.num_tokens, a.hkv);
+  if (g.balanced) hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, true>), dim3(g.grid), dim3(g.threads), 0, s, a);
+  else hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, false>), dim3(g.grid), dim3(g.threads), 0, s, a);
 }
 
 hipError_t launch_tq4_quantize(int d, int vbits, const QuantizeArgs &a, hipStream_t s) {
   if (a.num_tokens <= 0) return hipSuccess;
-  const int64_t tasks = quantize_tasks(d, a.num_tokens, a.hkv);
-  if (d == 128) vbits == 4 ? launch_q<128, 4>(a, tasks, s) : launch_q<128, 2>(a, tasks, s);
-  else vbits == 4 ? launch_q<64, 4>(a, tasks, s) : launch_q<64, 2>(a, tasks, s);
+  if (d == 128) vbits == 4 ? launch_q<128, 4>(a, s) : launch_q<128, 2>(a, s);
+  else vbits == 4 ? launch_q<64, 4>(a, s) : launch_q<64, 2>(a, s);
   return hipGetLastError();
 }
 

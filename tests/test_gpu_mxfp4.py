@@ -56,6 +56,22 @@ def test_small_ragged_fp4(g, hkv, seed, split):
     _check(Case(cfg))
 
 
+@pytest.mark.parametrize("loop", ["static", "balanced"])
+def test_fp4_both_quantize_loops(loop):
+    """Both work distributions of the quantize kernel write the oracle's bytes."""
+    saved = os.environ.get("TQ_QUANT_LOOP")
+    os.environ["TQ_QUANT_LOOP"] = loop
+    try:
+        cfg = workloads.small_config(batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(1500, 3000),
+                                     seed=231, fmt=1)
+        say(f"case: fp4 quantize loop {loop}")
+        _check(Case(cfg))
+    finally:
+        os.environ.pop("TQ_QUANT_LOOP", None)
+        if saved is not None:
+            os.environ["TQ_QUANT_LOOP"] = saved
+
+
 def test_fp4_unaligned_skipped_single_token_slots():
     cfg = workloads.small_config(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, ctx_range=(160, 160),
                                  seed=205, fmt=1)

@@ -118,6 +118,30 @@ def test_unaligned_skipped_and_single_token_slots():
     assert np.array_equal(gpu, op.pool)
 
 
+@pytest.fixture
+def _loop_env():
+    saved = os.environ.pop("TQ_QUANT_LOOP", None)
+    yield
+    os.environ.pop("TQ_QUANT_LOOP", None)
+    if saved is not None:
+        os.environ["TQ_QUANT_LOOP"] = saved
+
+
+@pytest.mark.parametrize("loop", ["static", "balanced"])
+@pytest.mark.parametrize("fmt,d,hkv,seed", [(0, 128, 3, 141), (0, 64, 2, 142), (2, 128, 2, 143), (2, 64, 3, 144)])
+def test_both_quantize_loops(_loop_env, loop, fmt, d, hkv, seed):
+    """Both work distributions of the quantize kernel (fixed shares per
+    work-group, or per-compute-unit ranges handed out to waves by a counter)
+    write the oracle's bytes, for TQ4/4 and TQ4/2 at both head sizes."""
+    os.environ["TQ_QUANT_LOOP"] = loop
+    # about 15000 tokens: the balanced loop's 256 work-groups take 10 to 30
+    # tasks each, so waves ask the counter more than once
+    cfg = workloads.small_config(batch=6, num_q_heads=4 * hkv, num_kv_heads=hkv, head_dim=d, ctx_range=(1500, 3000),
+                                 seed=seed, fmt=fmt)
+    say(f"case: quantize loop {loop}, format {fmt}, d={d}, hkv={hkv}, seed={seed}")
+    _check_case(Case(cfg))
+
+
 def test_pool_beyond_4_gib():
     """A 4.7 GB pool (10^6 blocks x 2 kv-heads x 2336 B): records past byte
     2^32 are written and read through 64-bit offsets.  One sequence lives on
