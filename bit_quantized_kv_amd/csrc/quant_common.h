@@ -265,7 +265,9 @@ __device__ __forceinline__ void quantize_loop_balanced(const QuantizeArgs &a, in
   const uint32_t hkv = (uint32_t)a.hkv;
   const int64_t tasks = (a.num_tokens + TPW - 1) / TPW * hkv;
   // this work-group's range [lo, lo + count) and its first task as (chunk c0,
-  // head h0); 32-bit arithmetic whenever the task count allows it
+  // head h0); 32-bit arithmetic whenever the task count allows it.  count
+  // fits an int: a launch's K and V (512 B per token-head) lie in device
+  // memory, so it has well under 2^31 tasks per compute unit
   int64_t c0;
   int count, h0;
   if (tasks <= 0x7FFFFFFF) {
