@@ -342,8 +342,10 @@ hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s) {
   if (a.num_tokens <= 0) return hipSuccess;
   const QuantGeometry g = quantize_geometry((const void *)mxfp4_quantize_kernel<false>,
                                             (const void *)mxfp4_quantize_kernel<true>, kD, a.num_tokens, a.hkv);
-  if (g.balanced) hipLaunchKernelGGL(mxfp4_quantize_kernel<true>, dim3(g.grid), dim3(g.threads), 0, s, a);
-  else hipLaunchKernelGGL(mxfp4_quantize_kernel<false>, dim3(g.grid), dim3(g.threads), 0, s, a);
+  QuantizeArgs b = a;
+  b.grain = g.grain;
+  if (g.balanced) hipLaunchKernelGGL(mxfp4_quantize_kernel<true>, dim3(g.grid), dim3(g.threads), 0, s, b);
+  else hipLaunchKernelGGL(mxfp4_quantize_kernel<false>, dim3(g.grid), dim3(g.threads), 0, s, b);
   return hipGetLastError();
 }
 

@@ -251,8 +251,8 @@ __device__ __forceinline__ void quantize_loop_static(const QuantizeArgs &a, int 
 // task is (chunk of TPW tokens, kv-head), numbered chunk * Hkv + head: the
 // wave codes tokens chunk * TPW + tw of that head.  One work-group of 16 waves
 // per compute unit takes an equal contiguous range of the tasks; inside it,
-// wave w starts with task w of the range and every later task goes to the wave
-// that asks first (an LDS counter).  With four work-groups per unit and fixed
+// wave w starts with the range's first task (or pair of tasks) after w * grain,
+// and every later one goes to the wave that asks first (an LDS counter).  With four work-groups per unit and fixed
 // shares, the unit's arbiter favours the oldest: on long launches the first
 // ended at 0.6 of the run while the last ran its end on a partly idle unit;
 // here the waves of a unit end together.  Two row buffers, as above (past the
@@ -290,21 +290,26 @@ __device__ __forceinline__ void quantize_loop_balanced(const QuantizeArgs &a, in
     t0 = (c0 + m / hkv) * TPW;
     h = (int)(m % hkv);
   };
+  // grain 2: tasks go out in pairs (2k, 2k + 1), one round trip per two
+  // tasks; grain 1: one by one
+  const int grain = a.grain;
   auto grab = [&]() {
     int x = 0;
-    if ((threadIdx.x & 63) == 0) x = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((threadIdx.x & 63) == 0)
+      x = __hip_atomic_fetch_add(&s_next, grain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return __builtin_amdgcn_readfirstlane(x);
   };
-  int n = wv, h;
+  int n = grain * wv, h;
   int64_t t0;
   locate(n, t0, h);
   RowLoad<D> ra, rb;
   load_row<D>(ra, a, t0, h, tw, li);
-  if (threadIdx.x == 0) s_next = (int)(blockDim.x >> 6);
+  if (threadIdx.x == 0) s_next = grain * (int)(blockDim.x >> 6);
   stage();
   __syncthreads();
   while (n < count) {
-    int n2 = grab(), h2;
+    const int n2 = grain == 2 ? n + 1 : grab();  // the pair's second task, or the next one
+    int h2;
     int64_t t2;
     locate(n2, t2, h2);
     load_row<D>(rb, a, t2, h2, tw, li);
@@ -324,16 +329,19 @@ __device__ __forceinline__ void quantize_loop(const QuantizeArgs &a, int wv, int
   else quantize_loop_static<D>(a, wv, tw, li, stage, code);
 }
 
-// Launch geometry of a quantize launch.  Static loop: work-group tasks of
-// 4 * TPW tokens and one kv-head, as many work-groups as fit at once (at most
-// one per task), 4 waves each.  Balanced loop, when there are at least 32
-// wave tasks (TPW tokens, one kv-head) per wave slot of the chip (16 per
-// compute unit): one work-group of 16 waves per compute unit.  Measured: the
-// balanced loop takes 8% off launches with 50 and more tasks per wave, is even
-// at 64 on a ragged batch, and costs 4% at 8, where the counter's round trips
-// outweigh the skew it removes.
+// Launch geometry of a quantize launch, by wave tasks (TPW tokens, one
+// kv-head) per wave slot of the chip (16 per compute unit):
+// * under 8: the static loop: work-group tasks of 4 * TPW tokens and one
+//   kv-head, as many 4-wave work-groups as fit at once (at most one per task);
+// * 8 to 31: the balanced loop, one 16-wave work-group per compute unit,
+//   tasks handed out in pairs;
+// * 32 and more: the balanced loop, tasks handed out one by one.
+// Measured: single hand-outs take 8% off launches with 50 and more tasks per
+// wave and cost 4% at 8, where pairs (half the counter's round trips) take 2%
+// off instead; pairs cost 1.5% on the long launches (coarser balance).
 struct QuantGeometry {
   bool balanced;
+  int grain;  // balanced loop: tasks per hand-out
   int grid, threads;
 };
 QuantGeometry quantize_geometry(const void *kernel_static, const void *kernel_balanced, int d, int64_t num_tokens,

@@ -267,14 +267,19 @@ QuantGeometry quantize_geometry(const void *kernel_static, const void *kernel_ba
   }
   const int tpw = d == 128 ? 8 : 16;
   const int64_t wave_tasks = (num_tokens + tpw - 1) / tpw * hkv;
-  bool balanced = wave_tasks >= (int64_t)32 * (kQuantThreadsBal / 64) * occ.cus;
-  // override for tests: TQ_QUANT_LOOP=static or balanced
+  const int64_t slots = (int64_t)(kQuantThreadsBal / 64) * occ.cus;
+  bool balanced = wave_tasks >= 8 * slots;
+  int grain = wave_tasks >= 32 * slots ? 1 : 2;
+  // override for tests: TQ_QUANT_LOOP=static, balanced (one by one) or
+  // balanced-pairs
   if (const char *env = std::getenv("TQ_QUANT_LOOP")) {
     if (std::strcmp(env, "static") == 0) balanced = false;
-    if (std::strcmp(env, "balanced") == 0) balanced = true;
+    if (std::strcmp(env, "balanced") == 0) balanced = true, grain = 1;
+    if (std::strcmp(env, "balanced-pairs") == 0) balanced = true, grain = 2;
   }
   QuantGeometry g;
   g.balanced = balanced;
+  g.grain = grain;
   if (balanced) {
     g.threads = kQuantThreadsBal;
     g.grid = occ.cus * resident_per_cu(occ, kernel_balanced, kQuantThreadsBal, 1);
@@ -291,8 +296,10 @@ template <int D, int VB>
 void launch_q(const QuantizeArgs &a, hipStream_t s) {
   const QuantGeometry g = quantize_geometry((const void *)tq4_quantize_kernel<D, VB, false>,
                                             (const void *)tq4_quantize_kernel<D, VB, true>, D, a.num_tokens, a.hkv);
-  if (g.balanced) hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, true>), dim3(g.grid), dim3(g.threads), 0, s, a);
-  else hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, false>), dim3(g.grid), dim3(g.threads), 0, s, a);
+  QuantizeArgs b = a;
+  b.grain = g.grain;
+  if (g.balanced) hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, true>), dim3(g.grid), dim3(g.threads), 0, s, b);
+  else hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, false>), dim3(g.grid), dim3(g.threads), 0, s, b);
 }
 
 hipError_t launch_tq4_quantize(int d, int vbits, const QuantizeArgs &a, hipStream_t s) {

@@ -33,6 +33,7 @@ struct QuantizeArgs {
   const DeviceTables *tables;
   BinParams bins;
   float rsqrt_d;                 // fp32(1/sqrt(d))
+  int32_t grain;                 // balanced quantize loop: tasks per hand-out (1 or 2)
 };
 
 struct DecodeArgs {

@@ -145,8 +145,8 @@ tq_status tq_default_key_table(uint16_t out_f16[16]);
  * Slots must be < num_blocks * 16 and distinct within one call (trusted, not
  * checked on the device).  num_tokens = 0 is a no-op.  Asynchronous.  The
  * kernel's work distribution follows from the sizes (the environment variable
- * TQ_QUANT_LOOP, "static" or "balanced", overrides it for tests); the records
- * written do not depend on it. */
+ * TQ_QUANT_LOOP, "static", "balanced" or "balanced-pairs", overrides it for
+ * tests); the records written do not depend on it. */
 tq_status tq_quantize_append(tq_cache *cache, const void *k, const void *v, const int32_t *slot_mapping,
                              int64_t num_tokens, void *stream);
 

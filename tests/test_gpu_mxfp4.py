@@ -56,9 +56,9 @@ def test_small_ragged_fp4(g, hkv, seed, split):
     _check(Case(cfg))
 
 
-@pytest.mark.parametrize("loop", ["static", "balanced"])
+@pytest.mark.parametrize("loop", ["static", "balanced", "balanced-pairs"])
 def test_fp4_both_quantize_loops(loop):
-    """Both work distributions of the quantize kernel write the oracle's bytes."""
+    """Every work distribution of the quantize kernel writes the oracle's bytes."""
     saved = os.environ.get("TQ_QUANT_LOOP")
     os.environ["TQ_QUANT_LOOP"] = loop
     try:

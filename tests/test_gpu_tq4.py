@@ -127,12 +127,13 @@ def _loop_env():
         os.environ["TQ_QUANT_LOOP"] = saved
 
 
-@pytest.mark.parametrize("loop", ["static", "balanced"])
+@pytest.mark.parametrize("loop", ["static", "balanced", "balanced-pairs"])
 @pytest.mark.parametrize("fmt,d,hkv,seed", [(0, 128, 3, 141), (0, 64, 2, 142), (2, 128, 2, 143), (2, 64, 3, 144)])
 def test_both_quantize_loops(_loop_env, loop, fmt, d, hkv, seed):
-    """Both work distributions of the quantize kernel (fixed shares per
-    work-group, or per-compute-unit ranges handed out to waves by a counter)
-    write the oracle's bytes, for TQ4/4 and TQ4/2 at both head sizes."""
+    """Every work distribution of the quantize kernel (fixed shares per
+    work-group, or per-compute-unit ranges handed out to waves by a counter,
+    one task or a pair at a time) writes the oracle's bytes, for TQ4/4 and
+    TQ4/2 at both head sizes."""
     os.environ["TQ_QUANT_LOOP"] = loop
     # about 15000 tokens: the balanced loop's 256 work-groups take 10 to 30
     # tasks each, so waves ask the counter more than once
