@@ -53,8 +53,8 @@
  *     Vc2 8*P B    channel 2p + par, p = 16*gp + j, of token t: byte
  *                  ((r*16 + j)*(G/2) + gp/2)*4 + tt, bits 4*(gp%2) + 2*par
  *     Vm  64*G B   as TQ4/4
- *   Supported by tq_quantize_append and tq_decode_attention (multi-token and
- *   cascade attention return TQ_ERR_UNSUPPORTED).
+ *   Supported by every call: quantize-append, decode, multi-token and cascade
+ *   attention.
  *
  * MX-FP4 (format 1, D = 128).  Per (token, kv-head), groups of 32 channels:
  *   keys are rotated first, y = fp32(x * fp32(1/sqrt(D))), an exactly zero y
@@ -119,7 +119,10 @@ tq_status tq_record_bytes(const tq_cache_desc *desc, size_t *bytes);
 /* Bytes of the whole pool: num_blocks * num_kv_heads * record bytes. */
 tq_status tq_pool_bytes(const tq_cache_desc *desc, size_t *bytes);
 
-/* Create a cache handle.  `pool` is a caller-owned device buffer of at least
+/* Create a cache handle: a paged pool of 16-token blocks ([ST]: vLLM paged KV
+ * blocks of 16 tokens) holding the 4-bit records of the chosen format
+ * ([TQ-AMD] section 2 for TQ4/4; [UQ] "方法怎麼做，白話講" for MX-FP4), and the
+ * key table the coder uses.  `pool` is a caller-owned device buffer of at least
  * tq_pool_bytes bytes (its contents are kept), or NULL: then the library
  * allocates the pool and fills it with zeros.  The library always owns the
  * handle and a small device table buffer.  Synchronous.  Errors:
@@ -304,7 +307,8 @@ tq_status tq_calibrate_key_tables(const void *k, int32_t num_layers, int64_t row
  * r satisfies 100 * r < percent * num_layers.  percent 0 .. 100. */
 tq_status tq_select_layers(const double *mse, int32_t num_layers, int32_t percent, uint8_t *chosen);
 
-/* Free the handle (NULL-safe).  Synchronises the device first; frees the
+/* Free the handle made by tq_create_cache (the paged cache of [ST] and
+ * [TQ-AMD] section 2), NULL-safe.  Synchronises the device first; frees the
  * library-owned pool if the library allocated it. */
 void tq_free(tq_cache *cache);
 

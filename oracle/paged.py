@@ -12,7 +12,7 @@ describe sessions that reuse the same prefix blocks.  Readings (vLLM style):
   t % 16; several sequences may name the same block (shared prefixes);
 * a block row that was never written stays as the pool was initialised.
 
-Pinned by tests/test_oracle_paged.py (identity vs permuted block tables,
+Pinned by tests/test_oracle_attention.py (identity vs permuted block tables,
 shared blocks, skipped slots).
 """
 import numpy as np
