@@ -23,7 +23,7 @@ EXPORTS = (
     "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_free",
     "tq_status_string", "tq_last_error", "tq_calibrate_workspace_bytes", "tq_calibrate_key_tables",
     "tq_select_layers", "tq_multitoken_workspace_bytes", "tq_multitoken_attention", "tq_cascade_workspace_bytes",
-    "tq_cascade_decode_attention",
+    "tq_cascade_decode_attention", "tq_debug_dequantize",
 )
 
 
@@ -77,6 +77,7 @@ def _load():
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                          ctypes.c_size_t, P], ctypes.c_int),
+        "tq_debug_dequantize": ([P, P, ctypes.c_int32, P, P, P], ctypes.c_int),
         "tq_free": ([P], None),
         "tq_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
@@ -252,6 +253,13 @@ def tq_select_layers(mse, percent=10):
     out = (ctypes.c_uint8 * max(n, 1))()
     _check(LIB.tq_select_layers(arr, n, int(percent), out))
     return [bool(out[i]) for i in range(n)]
+
+
+def tq_debug_dequantize(cache, block_ids, k_out, v_out, stream=None):
+    """Test-only: block_ids device int32 [n]; k_out, v_out device float32
+    [n, num_kv_heads, 16, head_dim]."""
+    _check(LIB.tq_debug_dequantize(cache, _ptr(block_ids), int(block_ids.numel()), _ptr(k_out), _ptr(v_out),
+                                   _stream(stream)))
 
 
 def tq_free(cache):

@@ -43,6 +43,15 @@ class Cache:
                               stream)
         return out
 
+    def dequantize(self, block_ids, stream=None):
+        """Test-only: the dequantized records of ``block_ids`` (device int32
+        [n]) as (k_hat_rot, v_hat) float32 [n, Hkv, 16, D] device tensors."""
+        n = int(block_ids.numel())
+        k = torch.empty((n, self.num_kv_heads, 16, self.head_dim), dtype=torch.float32, device=self.pool.device)
+        v = torch.empty_like(k)
+        B.tq_debug_dequantize(self.handle, block_ids, k, v, stream)
+        return k, v
+
     def key_table_f16(self):
         return B.tq_cache_info(self.handle)[2]
 

@@ -144,8 +144,9 @@ __device__ __forceinline__ void softmax_block(const float (&x)[4], WaveState<G2>
 // Combine the NW waves of a work-group and write either the output (single
 // split) or a split partial.  s_m / s_l / s_acc are LDS scratch.  CASCADE:
 // always a partial, at slot sp of rows of a.part_stride slots.
-template <int D, int GQ, int NW, bool CASCADE = false>
-__device__ __forceinline__ void finish_workgroup(const DecodeArgs &a, WaveState<2 * D / 32> &st, int b, int qh0,
+// Tiles 0 .. 2D/32 - 1 of st are the output tiles (a state may carry more).
+template <int D, int GQ, int NW, bool CASCADE = false, int NA>
+__device__ __forceinline__ void finish_workgroup(const DecodeArgs &a, WaveState<NA> &st, int b, int qh0,
                                                  int sp, float (*s_m)[GQ], float (*s_l)[GQ],
                                                  float (*s_acc)[GQ][D]) {
   constexpr int G = D / 32;

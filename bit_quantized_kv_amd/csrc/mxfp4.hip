@@ -14,9 +14,12 @@
 // group, its own UE8M0 byte as the A scale) times q8 (FP8, B operand; lane
 // group gb carries channels 16gb..+15 and 64+16gb..+15) with
 // v_mfma_scale_f32_16x16x128_f8f6f4, one instruction per 16-token block.
-// Values are dequantized to fp16 exactly (v_cvt_scalef32_pk_f16_fp4 with the
-// scale 2^X) and PV runs on v_mfma_f32_16x16x16_f16 as in the TQ4/4 kernel.
+// Values are dequantized to bf16 exactly (v_cvt_scalef32_pk_bf16_fp4 with the
+// scale 2^X: an e2m1 element times 2^X has two significant bits, and bf16 has
+// the fp32 exponent range) and PV runs on v_mfma_f32_16x16x16_bf16 with P
+// split into bf16 high and low parts (16 significant bits).
 #include "decode_common.h"
+#include "dequant.h"
 #include "quant_common.h"
 
 namespace tq {
@@ -199,36 +202,32 @@ __device__ __forceinline__ void do_block4(const Blk4 &bk, const int8v &bq8, uint
   }
   float p[4];
   softmax_block<8>(x, st, p);
-  half4v bp;
+  // B operand: tokens in the order 0, 2, 1, 3 (the A operand's order below);
+  // bf16 high part on columns < g, bf16 low part (p - high, exact, then
+  // rounded to nearest) on columns g .. 2g-1
+  bf16x4v bp;
   {
-    const half2v h02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[0], p[2]));
-    const half2v h13 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p[1], p[3]));
-    const float r0 = __builtin_fmaf(-lo_mask, (float)h02[0], p[0]);
-    const float r2 = __builtin_fmaf(-lo_mask, (float)h02[1], p[2]);
-    const float r1 = __builtin_fmaf(-lo_mask, (float)h13[0], p[1]);
-    const float r3 = __builtin_fmaf(-lo_mask, (float)h13[1], p[3]);
-    const half2v a02 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r2));
-    const half2v a13 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r1, r3));
-    bp = (half4v){a02[0], a02[1], a13[0], a13[1]};
+    const uint32_t h02 = prob_hi_bf16(p[0], p[2]), h13 = prob_hi_bf16(p[1], p[3]);
+    const uint32_t a02 = prob_part_bf16(h02, p[0], p[2], lo_mask);
+    const uint32_t a13 = prob_part_bf16(h13, p[1], p[3], lo_mask);
+    bp = __builtin_bit_cast(bf16x4v, make_uint2(a02, a13));
   }
-  // ---- values: exact fp16 dequantization, then PV on fp16 MFMA --------------------
+  // ---- values: exact bf16 dequantization, then PV on bf16 MFMA --------------------
   const uint4 vs = reinterpret_cast<const uint4 *>(vs_slot)[lane >> 4];
 #pragma unroll
   for (int gp = 0; gp < kG; ++gp) {
     const uint32_t w = word4(bk.vq, gp);
     const uint32_t xs = word4(vs, gp);  // exponent bytes of tokens 4r + 0..3
-    const float f0 = as_f((xs & 0xFFu) << 23), f1 = as_f(((xs >> 8) & 0xFFu) << 23);
-    const float f2 = as_f(((xs >> 16) & 0xFFu) << 23), f3 = as_f((xs >> 24) << 23);
-    const uint32_t h0 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f0, 0));
-    const uint32_t h1 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f1, 1));
-    const uint32_t h2 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f2, 2));
-    const uint32_t h3 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f3, 3));
+    const uint32_t h0 = fp4_pair_bf16<0>(w, ue8m0_scale(xs & 0xFFu));
+    const uint32_t h1 = fp4_pair_bf16<1>(w, ue8m0_scale((xs >> 8) & 0xFFu));
+    const uint32_t h2 = fp4_pair_bf16<2>(w, ue8m0_scale((xs >> 16) & 0xFFu));
+    const uint32_t h3 = fp4_pair_bf16<3>(w, ue8m0_scale(xs >> 24));
     const uint32_t e02 = __builtin_amdgcn_perm(h2, h0, 0x05040100u), o02 = __builtin_amdgcn_perm(h2, h0, 0x07060302u);
     const uint32_t e13 = __builtin_amdgcn_perm(h3, h1, 0x05040100u), o13 = __builtin_amdgcn_perm(h3, h1, 0x07060302u);
-    const half4v ae = __builtin_bit_cast(half4v, make_uint2(e02, e13));
-    const half4v ao = __builtin_bit_cast(half4v, make_uint2(o02, o13));
-    st.acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x16f16(ae, bp, st.acc[2 * gp], 0, 0, 0);
-    st.acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ao, bp, st.acc[2 * gp + 1], 0, 0, 0);
+    const bf16x4v ae = __builtin_bit_cast(bf16x4v, make_uint2(e02, e13));
+    const bf16x4v ao = __builtin_bit_cast(bf16x4v, make_uint2(o02, o13));
+    st.acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, bp, st.acc[2 * gp], 0, 0, 0);
+    st.acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, bp, st.acc[2 * gp + 1], 0, 0, 0);
   }
 }
 

@@ -17,76 +17,19 @@
 //     v_mfma_f32_16x16x32_f16, then the per-token key scale;
 //   * online softmax in log2 units (the query carries log2(e)), rescaling the
 //     accumulators only when the running maximum moves by more than 2^8;
-//   * values dequantized to fp16 (code * scale + min, one rounding) and
-//     out^T (channels x columns) += V_hat^T P with v_mfma_f32_16x16x16_f16,
-//     P again split into fp16 high and low parts.
+//   * values: out^T (channels x columns) += V_hat^T P with P split into fp16
+//     high and low parts, V_hat = code * scale + min consumed exactly: code *
+//     scale as two exact fp16 parts on the 32-deep v_mfma_f32_16x16x32_f16
+//     (k = token and part), the minimum through one v_mfma_f32_16x16x16_f16
+//     of the group minima with P, added at the end.
 // Split partials (max, sum, acc) go to the workspace; decode_merge combines them.
 #include "decode_common.h"
+#include "dequant.h"
 
 namespace tq {
 namespace {
 
 constexpr int kWaves = 8;
-
-template <int D>
-struct KTile;
-template <>
-struct KTile<128> {
-  typedef uint4 T;
-};
-template <>
-struct KTile<64> {
-  typedef uint2 T;
-};
-
-__device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-__device__ __forceinline__ uint32_t word(const uint2 &v, int i) { return i == 0 ? v.x : v.y; }
-
-// Two 4-bit codes, each alone in a byte of `bytes` (word `hi_word`), as exact
-// fp16 values: 0000cccc is the OCP e4m3 encoding of c * 2^-9.
-template <bool HI_WORD>
-__device__ __forceinline__ half2v codes_f16(uint32_t bytes) {
-  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
-}
-
-// Value-code words per lane: 4-bit, one per 32-channel group; 2-bit (TQ4/2),
-// one per group pair.
-template <int D, int VB>
-struct VTile {
-  typedef typename KTile<D>::T T;
-};
-template <>
-struct VTile<128, 2> {
-  typedef uint2 T;
-};
-template <>
-struct VTile<64, 2> {
-  typedef uint32_t T;
-};
-__device__ __forceinline__ uint32_t word(uint32_t v, int) { return v; }
-
-template <int D, int VB>
-struct Blk {
-  typename KTile<D>::T kq;      // key codes: this lane's A-operand bytes
-  uint2 ks;                     // key scales of tokens 4r .. 4r+3
-  typename VTile<D, VB>::T vq;  // value codes: this lane's A-operand bytes
-  uint32_t vmw;                 // one dword of the value (scale, min) tile; lane
-                                // (r, c) holds dword c of row r's 16*G bytes
-};
-
-template <int D, int VB>
-__device__ __forceinline__ void load_blk(Blk<D, VB> &o, const uint8_t *rec, int lane) {
-  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
-  constexpr int VW = VB == 4 ? G : G / 2;  // value-code words per lane
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + 64 * 4 * VW;
-  const int r = lane >> 4, c = lane & 15;
-  o.kq = *reinterpret_cast<const typename KTile<D>::T *>(rec + lane * Q);
-  o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
-  o.vq = *reinterpret_cast<const typename VTile<D, VB>::T *>(rec + OFF_VC + lane * (4 * VW));
-  o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
-}
 
 // vm_slot: this wave's 16*D/8-byte LDS slot for the value (scale, min) tile.
 // vm_keep: per-lane mask clearing the (scale, min) halves of rows past the
@@ -95,10 +38,11 @@ __device__ __forceinline__ void load_blk(Blk<D, VB> &o, const uint8_t *rec, int 
 // earlier).
 // tail: the block is the partial last one of its sequence (rows past the
 // context are masked: -inf logits, zero value scale and minimum).
+// bq: this lane's B operand of the QK product in LDS (k-step s at bq[s]).
 template <int D, int GQ, int VB>
-__device__ __forceinline__ void do_block(const Blk<D, VB> &bk, const half8v (&bq)[D / 32], const uint32_t *s_lut,
-                                         uint32_t *vm_slot, WaveState<2 * D / 32> &st, float lo_mask, int lane,
-                                         int tok0, int T, bool tail, uint32_t vm_keep) {
+__device__ __forceinline__ void do_block(const Blk<D, VB> &bk, const half8v *bq, const uint32_t *s_lut,
+                                         uint32_t *vm_slot, WaveState<2 * D / 32 + 1> &st, float lo_mask, int lane,
+                                         int tok0, int T, bool tail, uint32_t vm_keep, uint32_t sc_lane) {
   constexpr int G = D / 32, KS = D / 32;
   // the value (scale, min) tile goes through LDS: lane (r, c) wrote dword c of
   // row r; every lane reads its row's 16*G bytes back (broadcast reads)
@@ -109,17 +53,22 @@ __device__ __forceinline__ void do_block(const Blk<D, VB> &bk, const half8v (&bq
     __asm__ volatile("");
     vmw &= vm_keep;
   }
+  // a value scale of 4096 or more in this block (lanes holding scale dwords):
+  // then every scale of the block is applied as sc * 2^-7 and P as P * 2^7
+  // (rare; code * sc < 65520 then holds for every scale, and the split stays
+  // exact for scales >= 2^-7)
+  const bool big = __builtin_amdgcn_ballot_w64(has_big_scale(vmw & sc_lane) != 0) != 0;
+  if (big) {
+    __asm__ volatile("");
+    const half2v f = (half2v){(_Float16)0x1p-7f, (_Float16)0x1p-7f};
+    if (sc_lane) vmw = as_u(as_h2(vmw) * f);
+  }
   vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = vmw;
   // ---- logits ---------------------------------------------------------------
   float4v qk = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const uint32_t w = word(bk.kq, s);
-    uint4 e;
-    e.x = s_lut[w & 0xFF];
-    e.y = s_lut[(w >> 8) & 0xFF];
-    e.z = s_lut[(w >> 16) & 0xFF];
-    e.w = s_lut[w >> 24];
+    const uint4 e = key_entries(s_lut, word(bk.kq, s));
     qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, e), bq[s], qk, 0, 0, 0);
   }
   const half2v s01 = as_h2(bk.ks.x), s23 = as_h2(bk.ks.y);
@@ -137,7 +86,7 @@ __device__ __forceinline__ void do_block(const Blk<D, VB> &bk, const half8v (&bq
       if (tok0 + i >= T) x[i] = kNegInf;
   }
   float p[4];
-  softmax_block<2 * G>(x, st, p);
+  softmax_block<2 * G + 1>(x, st, p);
   // B operand: tokens 4r + 0..3 in k order; high part on columns < g, low
   // part (p - high) on columns g .. 2g-1; other columns are never read
   half4v bp;
@@ -154,44 +103,46 @@ __device__ __forceinline__ void do_block(const Blk<D, VB> &bk, const half8v (&bq
   }
 
   // ---- values -----------------------------------------------------------------
-  // A nibble isolated in a byte, 0000cccc, is the OCP e4m3 encoding of
-  // c * 2^-9 (codes 0..7 subnormal, 8..15 with exponent field 1), so the fp8
-  // conversion with scale 2^9 turns two such bytes into two exact fp16 codes;
-  // one fma with the fp16 (scale, min) pair then dequantizes with one rounding.
+  // the minima: out^T gets sum_t mn(t, g) P(t, col) for every channel of group
+  // g; A rows c hold group c % G, so row 4r' + i of the result is group i % G
+  {
+    const uint2 mnw = *reinterpret_cast<const uint2 *>(vm_slot + (lane >> 4) * (4 * G) + 4 * (lane & (G - 1)) + 2);
+    st.acc[2 * G] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4v, mnw), bp, st.acc[2 * G], 0, 0, 0);
+  }
+  if (big) {
+    __asm__ volatile("");
+    bp = bp * (half4v){(_Float16)128.f, (_Float16)128.f, (_Float16)128.f, (_Float16)128.f};
+  }
+  // code * scale times P for every channel tile.  A operand of tile (group gp,
+  // parity): k = 8r + j holds token 4r + (j & 3) of the lane's channel, the
+  // high fp16 part of code * sc for j < 4 and the low part for j >= 4; the B
+  // operand repeats P for both halves, so one 32-deep MFMA adds (hi + lo) * P
+  // = code * sc * P exactly (up to the fp32 accumulation).
   const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
+  const half8v bp8 = (half8v){bp[0], bp[1], bp[2], bp[3], bp[0], bp[1], bp[2], bp[3]};
 #pragma unroll
   for (int gp = 0; gp < G; ++gp) {
-    const uint4 vm = vm_row[gp];
+    const uint2 scw = *reinterpret_cast<const uint2 *>(&vm_row[gp]);
     // bytes = tokens 4r + 0..3 of one channel pair; lo / hi = the even / odd
-    // channel's codes, each alone in its byte (2-bit: the group pair's word,
-    // group 2w in bits 0-3 of each byte, 2w + 1 in bits 4-7)
+    // channel's codes, each alone in its byte
     uint32_t lo, hi;
-    if constexpr (VB == 4) {
-      const uint32_t w = word(bk.vq, gp);
-      lo = w & 0x0F0F0F0Fu;
-      hi = (w >> 4) & 0x0F0F0F0Fu;
-    } else {
-      const uint32_t w = word(bk.vq, gp >> 1) >> (4 * (gp & 1));
-      lo = w & 0x03030303u;
-      hi = (w >> 2) & 0x03030303u;
-    }
-    const half2v sc01 = as_h2(vm.x), sc23 = as_h2(vm.y);
-    const half2v mn01 = as_h2(vm.z), mn23 = as_h2(vm.w);
-    const half2v e01 = __builtin_elementwise_fma(codes_f16<false>(lo), sc01, mn01);
-    const half2v e23 = __builtin_elementwise_fma(codes_f16<true>(lo), sc23, mn23);
-    const half2v o01 = __builtin_elementwise_fma(codes_f16<false>(hi), sc01, mn01);
-    const half2v o23 = __builtin_elementwise_fma(codes_f16<true>(hi), sc23, mn23);
-    const half4v ae = __builtin_bit_cast(half4v, make_uint2(as_u(e01), as_u(e23)));
-    const half4v ao = __builtin_bit_cast(half4v, make_uint2(as_u(o01), as_u(o23)));
-    st.acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x16f16(ae, bp, st.acc[2 * gp], 0, 0, 0);
-    st.acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ao, bp, st.acc[2 * gp + 1], 0, 0, 0);
+    value_code_bytes<VB>(VB == 4 ? word(bk.vq, gp) : word(bk.vq, gp >> 1), gp, lo, hi);
+    const half2v sc01 = as_h2(scw.x), sc23 = as_h2(scw.y);
+    const ScaledPair e01 = scaled_codes(codes_f16<false>(lo), sc01);
+    const ScaledPair e23 = scaled_codes(codes_f16<true>(lo), sc23);
+    const ScaledPair o01 = scaled_codes(codes_f16<false>(hi), sc01);
+    const ScaledPair o23 = scaled_codes(codes_f16<true>(hi), sc23);
+    const half8v ae = __builtin_bit_cast(half8v, make_uint4(as_u(e01.hi), as_u(e23.hi), as_u(e01.lo), as_u(e23.lo)));
+    const half8v ao = __builtin_bit_cast(half8v, make_uint4(as_u(o01.hi), as_u(o23.hi), as_u(o01.lo), as_u(o23.lo)));
+    st.acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bp8, st.acc[2 * gp], 0, 0, 0);
+    st.acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bp8, st.acc[2 * gp + 1], 0, 0, 0);
   }
 }
 
 template <int D, int GQ, bool CASCADE, int VB = 4>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void tq4_decode_kernel(
     DecodeArgs a) {
-  constexpr int G = D / 32, KS = D / 32;
+  constexpr int G = D / 32;
   constexpr int REC = 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * G;
   constexpr int NW = kWaves;
 
@@ -283,16 +234,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
   __syncthreads();
 
   const int r = lane >> 4, n = lane & 15;
-  half8v bq[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) bq[s] = *reinterpret_cast<const half8v *>(&s_bq[n][r * (D / 4) + 8 * s]);
+  // this lane's query operand (k-step s at bq[s]), read from LDS per block
+  const half8v *bq = reinterpret_cast<const half8v *>(&s_bq[n][r * (D / 4)]);
   const float lo_mask = (n >= GQ && n < 2 * GQ) ? 1.f : 0.f;
 
-  WaveState<2 * G> st;
+  // tiles 0 .. 2G-1: out^T per (group, parity); tile 2G: the minima's product
+  WaveState<2 * G + 1> st;
   st.m = kNegInf;
   st.l = 0.f;
 #pragma unroll
-  for (int t = 0; t < 2 * G; ++t) st.acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 2 * G + 1; ++t) st.acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+  // lanes whose dword of a group's 16-byte (scale, min) tile holds scales
+  const uint32_t sc_lane = (lane & 2) ? 0u : 0xFFFFFFFFu;
 
   // process buffer k (if it is one of this wave's blocks), then refill it
   uint32_t *vm_slot = s_vm[wv];
@@ -300,7 +253,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     if (k < mine) {
       const int blk = blk0 + wv + k * NW;
       do_block<D, GQ, VB>(buf, bq, s_lut, vm_slot, st, lo_mask, lane, blk * 16 + 4 * r, T, blk == tail_blk,
-                          tail_keep);
+                          tail_keep, sc_lane);
     }
     load_blk<D, VB>(buf, rec_of(k + 4), lane);
   };
@@ -312,6 +265,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     run(b3, k + 3);
   }
 
+  // the minima's contribution to every channel of their group
+#pragma unroll
+  for (int gp = 0; gp < G; ++gp) {
+    st.acc[2 * gp] += st.acc[2 * G][gp];
+    st.acc[2 * gp + 1] += st.acc[2 * G][gp];
+  }
   finish_workgroup<D, GQ, NW, CASCADE>(a, st, b, qh0, sp, s_m, s_l, s_acc);
 }
 

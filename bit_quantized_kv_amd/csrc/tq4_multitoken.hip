@@ -28,6 +28,7 @@
 // With one split the rows are written directly; otherwise split partials
 // (max, sum, acc) go to the workspace and a merge kernel combines them per row.
 #include "decode_common.h"
+#include "dequant.h"
 
 namespace tq {
 namespace {
@@ -78,28 +79,6 @@ constexpr int mt_rec_bytes() {
   return 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * (D / 32);
 }
 
-// The value codes of channel group gp as bytes 0000cccc: `lo` the even
-// channels, `hi` the odd ones (bytes = tokens 4r + 0..3).  2-bit: the group
-// pair's word holds group 2w in bits 0-3 of each byte and 2w + 1 in bits 4-7,
-// the even channel in the lower two bits.
-template <int VB, typename VT>
-__device__ __forceinline__ void mt_value_codes(const VT &vq, int gp, uint32_t &lo, uint32_t &hi) {
-  if constexpr (VB == 4) {
-    const uint32_t w = mt_word(vq, gp);
-    lo = w & 0x0F0F0F0Fu;
-    hi = (w >> 4) & 0x0F0F0F0Fu;
-  } else {
-    const uint32_t w = mt_word(vq, gp >> 1) >> (4 * (gp & 1));
-    lo = w & 0x03030303u;
-    hi = (w >> 2) & 0x03030303u;
-  }
-}
-
-template <bool HI_WORD>
-__device__ __forceinline__ half2v mt_codes_f16(uint32_t bytes) {
-  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
-}
-
 template <int D, int VB>
 struct MtBlk {
   typename MtTile<D>::T kq;
@@ -120,14 +99,20 @@ __device__ __forceinline__ void mt_load_blk(MtBlk<D, VB> &o, const uint8_t *rec,
   o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];
 }
 
-// LDS image of a pair of dequantized blocks (per lane: its MFMA A operands).
-// The PV operand of a lane holds its 4 values of the first block, then its 4
-// of the second, so one 16-byte read gives the 32-token operand.
+// LDS image of a pair of blocks (per lane: its MFMA A operands).  The PV
+// operand of a lane holds its 4 value codes of the first block, then its 4 of
+// the second (exact fp16 integers), so one 16-byte read gives the 32-token
+// operand; the consumers form code * scale from them and the blocks' (scale,
+// min) tiles.
 template <int D>
 struct MtPair {
   uint4 k[2][D / 32][64];  // QK A operand of block h, k-step s: 8 fp16 table entries
-  uint4 v[D / 16][64];     // PV A operand of tile t: 4 + 4 fp16 values
+  uint4 v[D / 16][64];     // PV A operand of tile t: 4 + 4 fp16 value codes
+  uint32_t vm[2][64];      // block h's (scale, min) tile as in the record (row r,
+                           // group gp: 4 scales then 4 minima, fp16), the scales
+                           // times 2^-7 when big[h]
   uint2 ks[2][4];          // fp16 key scales of tokens 4r .. 4r+3 of block h
+  uint32_t big[2];         // block h holds a value scale >= 4096
 };
 
 struct MtTask {
@@ -148,48 +133,45 @@ __device__ __forceinline__ MtTask mt_task(const MultiTokenArgs &a) {
   return t;
 }
 
-// Producer: dequantize this wave's loaded block into half `half` of its LDS
-// pair; `lone`: the block is the last of the stage and unpaired, so the other
-// half's values are cleared (their probabilities are 0, and 0 * NaN would
-// not be).
+// Producer: this wave's loaded block into half `half` of its LDS pair: key
+// table entries, value codes as exact fp16, the (scale, min) tile (the scales
+// pre-multiplied by 2^-7 when one of them is >= 4096, flagged in big[half]);
+// `lone`: the block is the last of the stage and unpaired, so the other
+// half's codes and (scale, min) tile are cleared (its probabilities are 0,
+// and 0 * NaN would not be).
 template <int D, int VB>
 __device__ __forceinline__ void mt_produce(const MtBlk<D, VB> &bk, MtPair<D> &slot, int half, bool lone,
-                                           const uint32_t *s_lut, uint32_t *vm_slot, int lane, bool tail,
-                                           uint32_t vm_keep) {
+                                           const uint32_t *s_lut, int lane, bool tail, uint32_t vm_keep,
+                                           uint32_t sc_lane) {
   constexpr int G = D / 32, KS = D / 32;
   uint32_t vmw = bk.vmw;
   if (tail) {
     __asm__ volatile("");
     vmw &= vm_keep;
   }
-  vm_slot[(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = vmw;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const uint32_t w = mt_word(bk.kq, s);
-    uint4 e;
-    e.x = s_lut[w & 0xFF];
-    e.y = s_lut[(w >> 8) & 0xFF];
-    e.z = s_lut[(w >> 16) & 0xFF];
-    e.w = s_lut[w >> 24];
-    slot.k[half][s][lane] = e;
+  const bool big = __builtin_amdgcn_ballot_w64(has_big_scale(vmw & sc_lane) != 0) != 0;
+  if (big) {
+    __asm__ volatile("");
+    if (sc_lane) vmw = as_u(as_h2(vmw) * (half2v){(_Float16)0x1p-7f, (_Float16)0x1p-7f});
   }
+  slot.vm[half][(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = vmw;
+  if (lane == 0) slot.big[half] = big ? 1u : 0u;
+  if (lone) {
+    __asm__ volatile("");
+    slot.vm[1][(lane >> 4) * (4 * G) + (lane & (4 * G - 1))] = 0u;
+    if (lane == 0) slot.big[1] = 0u;
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) slot.k[half][s][lane] = key_entries(s_lut, mt_word(bk.kq, s));
   if ((lane & 15) == 0) slot.ks[half][lane >> 4] = bk.ks;
-  const uint4 *vm_row = reinterpret_cast<const uint4 *>(vm_slot) + (lane >> 4) * G;
 #pragma unroll
   for (int gp = 0; gp < G; ++gp) {
-    const uint4 vm = vm_row[gp];
     uint32_t lo, hi;
-    mt_value_codes<VB>(bk.vq, gp, lo, hi);
-    const half2v sc01 = as_h2(vm.x), sc23 = as_h2(vm.y);
-    const half2v mn01 = as_h2(vm.z), mn23 = as_h2(vm.w);
-    const half2v e01 = __builtin_elementwise_fma(mt_codes_f16<false>(lo), sc01, mn01);
-    const half2v e23 = __builtin_elementwise_fma(mt_codes_f16<true>(lo), sc23, mn23);
-    const half2v o01 = __builtin_elementwise_fma(mt_codes_f16<false>(hi), sc01, mn01);
-    const half2v o23 = __builtin_elementwise_fma(mt_codes_f16<true>(hi), sc23, mn23);
+    value_code_bytes<VB>(VB == 4 ? mt_word(bk.vq, gp) : mt_word(bk.vq, gp >> 1), gp, lo, hi);
     uint2 *ve = reinterpret_cast<uint2 *>(&slot.v[2 * gp][lane]);
     uint2 *vo = reinterpret_cast<uint2 *>(&slot.v[2 * gp + 1][lane]);
-    ve[half] = make_uint2(as_u(e01), as_u(e23));
-    vo[half] = make_uint2(as_u(o01), as_u(o23));
+    ve[half] = make_uint2(as_u(codes_f16<false>(lo)), as_u(codes_f16<true>(lo)));
+    vo[half] = make_uint2(as_u(codes_f16<false>(hi)), as_u(codes_f16<true>(hi)));
     if (lone) {
       __asm__ volatile("");
       ve[1] = make_uint2(0u, 0u);
@@ -246,9 +228,9 @@ __device__ __forceinline__ void mt_softmax8(const float (&x)[8], WaveState<NT> &
 template <int D, int TR>
 __device__ __forceinline__ void mt_consume_pair(const MtPair<D> &sp, bool has_b,
                                                 const half8v (&bq_hi)[TR][D / 32],
-                                                const half8v (&bq_lo)[TR][D / 32], WaveState<D / 16> (&st)[TR],
+                                                const half8v (&bq_lo)[TR][D / 32], WaveState<D / 16 + 1> (&st)[TR],
                                                 int lane, int tok0, const int (&lim)[TR], bool masked) {
-  constexpr int KS = D / 32, NT = D / 16;
+  constexpr int G = D / 32, KS = D / 32, NT = D / 16;
   const int r = lane >> 4;
   float4v qa[TR], qb[TR];
 #pragma unroll
@@ -294,14 +276,42 @@ __device__ __forceinline__ void mt_consume_pair(const MtPair<D> &sp, bool has_b,
         if (tok0 + (i >> 2) * 16 + 4 * r + (i & 3) >= lim[t]) x[i] = kNegInf;
     }
     float p[8];
-    mt_softmax8<NT>(x, st[t], p);
+    mt_softmax8<NT + 1>(x, st[t], p);
     ph[t] = mt_p_f16(p);
   }
+  // the minima: tile NT gets sum_t mn(t, g) P(t, row) (A row c: group c % G)
+  {
+    const int mi = r * (4 * G) + 4 * (lane & (G - 1)) + 2;
+    const half8v amn = __builtin_bit_cast(half8v, make_uint4(sp.vm[0][mi], sp.vm[0][mi + 1], sp.vm[1][mi],
+                                                             sp.vm[1][mi + 1]));
 #pragma unroll
-  for (int c = 0; c < NT; ++c) {
-    const half8v v8 = __builtin_bit_cast(half8v, sp.v[c][lane]);
+    for (int t = 0; t < TR; ++t) st[t].acc[NT] = __builtin_amdgcn_mfma_f32_16x16x32_f16(amn, ph[t], st[t].acc[NT], 0, 0, 0);
+  }
+  const uint32_t big_a = __builtin_amdgcn_readfirstlane(sp.big[0]), big_b = __builtin_amdgcn_readfirstlane(sp.big[1]);
+  if (big_a | big_b) {
+    __asm__ volatile("");
+    const _Float16 fa = big_a ? (_Float16)128.f : (_Float16)1.f, fb = big_b ? (_Float16)128.f : (_Float16)1.f;
 #pragma unroll
-    for (int t = 0; t < TR; ++t) st[t].acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, ph[t], st[t].acc[c], 0, 0, 0);
+    for (int t = 0; t < TR; ++t) ph[t] = ph[t] * (half8v){fa, fa, fa, fa, fb, fb, fb, fb};
+  }
+  // code * scale as two exact fp16 parts (scales of this lane's 4 + 4 tokens
+  // of the group), one MFMA each
+#pragma unroll
+  for (int gp = 0; gp < G; ++gp) {
+    const int si = r * (4 * G) + 4 * gp;
+    const half8v sc = __builtin_bit_cast(half8v, make_uint4(sp.vm[0][si], sp.vm[0][si + 1], sp.vm[1][si],
+                                                            sp.vm[1][si + 1]));
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const half8v code = __builtin_bit_cast(half8v, sp.v[2 * gp + par][lane]);
+      const half8v hi = code * sc;
+      const half8v lo = __builtin_elementwise_fma(code, sc, -hi);
+#pragma unroll
+      for (int t = 0; t < TR; ++t) {
+        st[t].acc[2 * gp + par] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, ph[t], st[t].acc[2 * gp + par], 0, 0, 0);
+        st[t].acc[2 * gp + par] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, ph[t], st[t].acc[2 * gp + par], 0, 0, 0);
+      }
+    }
   }
 }
 
@@ -324,7 +334,6 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   constexpr int RW = 16 * TR * NRG;  // rows per work-group
 
   __shared__ uint32_t s_lut[256];
-  __shared__ __attribute__((aligned(16))) uint32_t s_vm[NW][64];
   // two stage buffers of NW block slots; the query staging area and the final
   // block-group merge overlay them
   __shared__ __attribute__((aligned(16))) MtPair<D> s_stage[2][NW / 2];
@@ -492,16 +501,18 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
   }
   __syncthreads();  // the staging area becomes stage buffer 0
 
-  WaveState<NT> st[TR];
+  // tiles 0 .. NT-1: out^T per (group, parity); tile NT: the minima's product
+  WaveState<NT + 1> st[TR];
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
     st[t].m = kMtFloor;
     st[t].l = 0.f;
 #pragma unroll
-    for (int c = 0; c < NT; ++c) st[t].acc[c] = (float4v){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NT + 1; ++c) st[t].acc[c] = (float4v){0.f, 0.f, 0.f, 0.f};
   }
+  // lanes whose dword of a group's 16-byte (scale, min) tile holds scales
+  const uint32_t sc_lane = (lane & 2) ? 0u : 0xFFFFFFFFu;
 
-  uint32_t *vm_slot = s_vm[wv];
   const int nstage = (nb + NW - 1) / NW;
   auto stage = [&](MtBlk<D, VB> &buf, int k) {
     MtPair<D>(&cur)[NW / 2] = s_stage[k & 1];
@@ -509,8 +520,8 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     const int cnt = min(NW, blk1 - first);
     if (k < mine) {
       const int blk = first + wv;
-      mt_produce<D, VB>(buf, cur[wv >> 1], wv & 1, (wv & 1) == 0 && wv + 1 == cnt, s_lut, vm_slot, lane,
-                    blk == tail_blk, tail_keep);
+      mt_produce<D, VB>(buf, cur[wv >> 1], wv & 1, (wv & 1) == 0 && wv + 1 == cnt, s_lut, lane, blk == tail_blk,
+                        tail_keep, sc_lane);
     }
     mt_load_blk<D, VB>(buf, rec_of(k + 4), lane);
     __syncthreads();
@@ -530,6 +541,16 @@ __global__ __launch_bounds__(kMtWaves * 64) void tq4_multitoken_kernel(MultiToke
     stage(b1, k + 1);
     stage(b2, k + 2);
     stage(b3, k + 3);
+  }
+
+  // the minima's contribution to every channel of their group
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      st[t].acc[2 * gp] += st[t].acc[NT][gp];
+      st[t].acc[2 * gp + 1] += st[t].acc[NT][gp];
+    }
   }
 
   // ---- merge the block groups of each row group ---------------------------------
@@ -798,14 +819,17 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
       for (int s = 0; s < KS; ++s)
         bq[t][hl][s] = *reinterpret_cast<const half8v *>(&s_q[t][hl][n][r * (D / 4) + 8 * s]);
 
-  WaveState<NT> st[RT];
+  // tiles 0 .. NT-1: out^T per (group, parity); tile NT: the minima's product
+  WaveState<NT + 1> st[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     st[t].m = kMtFloor;
     st[t].l = 0.f;
 #pragma unroll
-    for (int c = 0; c < NT; ++c) st[t].acc[c] = (float4v){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NT + 1; ++c) st[t].acc[c] = (float4v){0.f, 0.f, 0.f, 0.f};
   }
+  // lanes whose dword of a group's 16-byte (scale, min) tile holds scales
+  const uint32_t sc_lane = (lane & 2) ? 0u : 0xFFFFFFFFu;
 
   uint32_t *vm_a = s_vm[wv][0], *vm_b = s_vm[wv][1];
   const int vm_i = (lane >> 4) * (4 * G) + (lane & (4 * G - 1));
@@ -823,6 +847,16 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
     if (blk + 1 == tail_blk) {
       __asm__ volatile("");
       vmb &= tail_keep;
+    }
+    // a block holding a value scale >= 4096 gets every scale applied as
+    // sc * 2^-7 and its tokens' probabilities as P * 2^7 (rare)
+    const bool big_a = __builtin_amdgcn_ballot_w64(has_big_scale(vma & sc_lane) != 0) != 0;
+    const bool big_b = __builtin_amdgcn_ballot_w64(has_big_scale(vmb & sc_lane) != 0) != 0;
+    if (big_a || big_b) {
+      __asm__ volatile("");
+      const half2v f = (half2v){(_Float16)0x1p-7f, (_Float16)0x1p-7f};
+      if (big_a && sc_lane) vma = as_u(as_h2(vma) * f);
+      if (big_b && sc_lane) vmb = as_u(as_h2(vmb) * f);
     }
     vm_a[vm_i] = vma;
     vm_b[vm_i] = vmb;
@@ -882,32 +916,59 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
           if (tok0 + (i >> 2) * 16 + 4 * r + (i & 3) >= lim[t]) x[i] = kNegInf;
       }
       float p[8];
-      mt_softmax8<NT>(x, st[t], p);
+      mt_softmax8<NT + 1>(x, st[t], p);
       ph[t] = mt_p_f16(p);
     }
-    // ---- values: code * scale + min in fp16, both blocks into one operand ----
+    // ---- values ----
+    // the minima: the bias tile gets sum_t mn(t, g) P(t, row); A rows c hold
+    // group c % G of the pair's 32 tokens (operand index 8r + j: token 4r + j
+    // of the first block for j < 4, of the second otherwise), so row 4r' + i
+    // of the result is group i % G
+    {
+      const uint2 mna = *reinterpret_cast<const uint2 *>(vm_a + (lane >> 4) * (4 * G) + 4 * (lane & (G - 1)) + 2);
+      const uint2 mnb = *reinterpret_cast<const uint2 *>(vm_b + (lane >> 4) * (4 * G) + 4 * (lane & (G - 1)) + 2);
+      const half8v amn = __builtin_bit_cast(half8v, make_uint4(mna.x, mna.y, mnb.x, mnb.y));
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        st[t].acc[NT] = __builtin_amdgcn_mfma_f32_16x16x32_f16(amn, ph[t], st[t].acc[NT], 0, 0, 0);
+    }
+    if (big_a || big_b) {
+      __asm__ volatile("");
+      const _Float16 fa = big_a ? (_Float16)128.f : (_Float16)1.f, fb = big_b ? (_Float16)128.f : (_Float16)1.f;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) ph[t] = ph[t] * (half8v){fa, fa, fa, fa, fb, fb, fb, fb};
+    }
+    // code * scale as two exact fp16 parts per element, both blocks into one
+    // 32-token operand; the high and the low parts each take one MFMA
     const uint4 *vra = reinterpret_cast<const uint4 *>(vm_a) + (lane >> 4) * G;
     const uint4 *vrb = reinterpret_cast<const uint4 *>(vm_b) + (lane >> 4) * G;
 #pragma unroll
     for (int gp = 0; gp < G; ++gp) {
-      const uint4 ma = vra[gp], mb = vrb[gp];
+      const uint2 sa = *reinterpret_cast<const uint2 *>(&vra[gp]), sb = *reinterpret_cast<const uint2 *>(&vrb[gp]);
       uint32_t la, ha, lb, hb;
-      mt_value_codes<VB>(ba.vq, gp, la, ha);
-      mt_value_codes<VB>(bb.vq, gp, lb, hb);
-      const half2v ea01 = __builtin_elementwise_fma(mt_codes_f16<false>(la), as_h2(ma.x), as_h2(ma.z));
-      const half2v ea23 = __builtin_elementwise_fma(mt_codes_f16<true>(la), as_h2(ma.y), as_h2(ma.w));
-      const half2v oa01 = __builtin_elementwise_fma(mt_codes_f16<false>(ha), as_h2(ma.x), as_h2(ma.z));
-      const half2v oa23 = __builtin_elementwise_fma(mt_codes_f16<true>(ha), as_h2(ma.y), as_h2(ma.w));
-      const half2v eb01 = __builtin_elementwise_fma(mt_codes_f16<false>(lb), as_h2(mb.x), as_h2(mb.z));
-      const half2v eb23 = __builtin_elementwise_fma(mt_codes_f16<true>(lb), as_h2(mb.y), as_h2(mb.w));
-      const half2v ob01 = __builtin_elementwise_fma(mt_codes_f16<false>(hb), as_h2(mb.x), as_h2(mb.z));
-      const half2v ob23 = __builtin_elementwise_fma(mt_codes_f16<true>(hb), as_h2(mb.y), as_h2(mb.w));
-      const half8v ve = __builtin_bit_cast(half8v, make_uint4(as_u(ea01), as_u(ea23), as_u(eb01), as_u(eb23)));
-      const half8v vo = __builtin_bit_cast(half8v, make_uint4(as_u(oa01), as_u(oa23), as_u(ob01), as_u(ob23)));
+      value_code_bytes<VB>(VB == 4 ? mt_word(ba.vq, gp) : mt_word(ba.vq, gp >> 1), gp, la, ha);
+      value_code_bytes<VB>(VB == 4 ? mt_word(bb.vq, gp) : mt_word(bb.vq, gp >> 1), gp, lb, hb);
+      const ScaledPair ea01 = scaled_codes(codes_f16<false>(la), as_h2(sa.x));
+      const ScaledPair ea23 = scaled_codes(codes_f16<true>(la), as_h2(sa.y));
+      const ScaledPair oa01 = scaled_codes(codes_f16<false>(ha), as_h2(sa.x));
+      const ScaledPair oa23 = scaled_codes(codes_f16<true>(ha), as_h2(sa.y));
+      const ScaledPair eb01 = scaled_codes(codes_f16<false>(lb), as_h2(sb.x));
+      const ScaledPair eb23 = scaled_codes(codes_f16<true>(lb), as_h2(sb.y));
+      const ScaledPair ob01 = scaled_codes(codes_f16<false>(hb), as_h2(sb.x));
+      const ScaledPair ob23 = scaled_codes(codes_f16<true>(hb), as_h2(sb.y));
+      const half8v veh = __builtin_bit_cast(half8v, make_uint4(as_u(ea01.hi), as_u(ea23.hi), as_u(eb01.hi), as_u(eb23.hi)));
+      const half8v vel = __builtin_bit_cast(half8v, make_uint4(as_u(ea01.lo), as_u(ea23.lo), as_u(eb01.lo), as_u(eb23.lo)));
+      const half8v voh = __builtin_bit_cast(half8v, make_uint4(as_u(oa01.hi), as_u(oa23.hi), as_u(ob01.hi), as_u(ob23.hi)));
+      const half8v vol = __builtin_bit_cast(half8v, make_uint4(as_u(oa01.lo), as_u(oa23.lo), as_u(ob01.lo), as_u(ob23.lo)));
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, ph[t], st[t].acc[2 * gp], 0, 0, 0);
-        st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, ph[t], st[t].acc[2 * gp + 1], 0, 0, 0);
+        st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(veh, ph[t], st[t].acc[2 * gp], 0, 0, 0);
+        st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voh, ph[t], st[t].acc[2 * gp + 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        st[t].acc[2 * gp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vel, ph[t], st[t].acc[2 * gp], 0, 0, 0);
+        st[t].acc[2 * gp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vol, ph[t], st[t].acc[2 * gp + 1], 0, 0, 0);
       }
     }
   };
@@ -921,6 +982,16 @@ __global__ __launch_bounds__(kDirWaves * 64) __attribute__((amdgpu_waves_per_eu(
   for (int k = 0; k < mine; k += 2) {
     run(a0, b0, k);
     run(a1, b1, k + 1);
+  }
+
+  // the minima's contribution to every channel of their group
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      st[t].acc[2 * gp] += st[t].acc[NT][gp];
+      st[t].acc[2 * gp + 1] += st[t].acc[NT][gp];
+    }
   }
 
   // ---- merge the waves' states: halving rounds through LDS -----------------------

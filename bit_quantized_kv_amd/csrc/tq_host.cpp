@@ -630,6 +630,21 @@ tq_status tq_select_layers(const double *mse, int32_t num_layers, int32_t percen
   return TQ_OK;
 }
 
+tq_status tq_debug_dequantize(tq_cache *cache, const int32_t *block_ids, int32_t n, float *k_out, float *v_out,
+                              void *stream) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return TQ_OK;
+  if (!block_ids || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARG, "block_ids, k_out and v_out must be non-NULL");
+  if ((int64_t)n * cache->desc.num_kv_heads >= (int64_t(1) << 31))
+    return fail(TQ_ERR_INVALID_ARG, "n * num_kv_heads must be < 2^31");
+  hipError_t e = tq::launch_debug_dequant(cache->desc.format, cache->desc.head_dim, cache->pool,
+                                          cache->desc.num_blocks, cache->desc.num_kv_heads, block_ids, n,
+                                          cache->tables, k_out, v_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return TQ_OK;
+}
+
 void tq_free(tq_cache *cache) {
   if (!cache) return;
   (void)hipDeviceSynchronize();

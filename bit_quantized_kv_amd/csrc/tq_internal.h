@@ -99,6 +99,9 @@ hipError_t launch_tq4_multitoken(int d, int vbits, const MultiTokenArgs &a, hipS
 hipError_t launch_prefix_attention(int d, int vbits, const MultiTokenArgs &a, hipStream_t s);
 hipError_t launch_tq4_cascade_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_cascade_merge(int d, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_debug_dequant(int format, int d, const uint8_t *pool, int64_t num_blocks, int hkv,
+                                const int32_t *ids, int64_t n, const DeviceTables *tables, float *k_out,
+                                float *v_out, hipStream_t s);
 size_t calibrate_workspace_bytes(int64_t layers, int64_t rows, int d);
 hipError_t launch_calibrate(int d, int layers, int64_t rows, const uint16_t *k, const uint16_t init_f16[16],
                             int max_iters, float rsqrt_d, void *workspace, uint16_t *tables, double *levels,

@@ -307,6 +307,26 @@ tq_status tq_calibrate_key_tables(const void *k, int32_t num_layers, int64_t row
  * r satisfies 100 * r < percent * num_layers.  percent 0 .. 100. */
 tq_status tq_select_layers(const double *mse, int32_t num_layers, int32_t percent, uint8_t *chosen);
 
+/* ---------------------------------------------------------------------------
+ * Test-only: the dequantized records, as every attention call of this library
+ * consumes them ([TQ-AMD] section 2: k_hat = c[code] * s in the rotated domain,
+ * v_hat = code * sc + mn; [UQ] "方法怎麼做，白話講": k_hat, v_hat = e2m1 * 2^X).
+ * For each of the n block ids (device int32 [n]) and every kv-head h, writes
+ * token t's dequantized key and value rows:
+ *   k_out, v_out: device fp32 [n][num_kv_heads][16][head_dim], keys in the
+ *   rotated domain;
+ *   TQ4/4 and TQ4/2: k = fp32(c[code] * s), v = fp32(code * sc + mn) (exact
+ *   products, one rounding of the sum; the attention kernels carry code * sc
+ *   as two exact fp16 parts and add mn * p separately).  In a block holding a
+ *   value scale >= 4096 every scale of the block is applied as sc * 2^-7 (the
+ *   probabilities as p * 2^7); this stays exact for scales >= 2^-7;
+ *   MX-FP4: k = e2m1 * 2^X, v = e2m1 * 2^X (exact).
+ * The records are read as they are: rows past a sequence's context hold
+ * whatever the pool holds.  A block id outside [0, num_blocks) gives rows of
+ * zeros.  n = 0 is a no-op; n * num_kv_heads < 2^31.  Asynchronous. */
+tq_status tq_debug_dequantize(tq_cache *cache, const int32_t *block_ids, int32_t n, float *k_out, float *v_out,
+                              void *stream);
+
 /* Free the handle made by tq_create_cache (the paged cache of [ST] and
  * [TQ-AMD] section 2), NULL-safe.  Synchronises the device first; frees the
  * library-owned pool if the library allocated it. */

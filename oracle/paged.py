@@ -78,6 +78,25 @@ class PagedPool:
                 layout.mxfp4_write_rows(flat, base, row[sel], self.d, enc["kcode"][sel, h], enc["kexp"][sel, h],
                                         enc["vcode"][sel, h], enc["vexp"][sel, h])
 
+    def dequantize_blocks(self, ids):
+        """Every row of the records of blocks ``ids`` for every kv-head,
+        dequantized as the codecs define it, in fp32: (k_hat_rot, v_hat), each
+        [len(ids), Hkv, 16, D] ([TQ-AMD] section 2: k_hat = c[code] * s, v_hat
+        = fp32(code * sc + mn); [UQ] "方法怎麼做，白話講": e2m1 * 2^X).  Keys stay
+        in the rotated domain."""
+        ids = np.asarray(ids, dtype=np.int64)
+        recs = self.pool[ids].reshape(-1, self.rec_bytes)
+        shape = (len(ids), self.hkv, BLOCK, self.d)
+        if self.fmt in (FORMAT_TQ4, FORMAT_TQ4V2):
+            sec = (layout.tq4_read_block if self.fmt == FORMAT_TQ4 else layout.tq4v2_read_block)(recs, self.d)
+            k = tq4.key_dequant_rot(sec["kcode"], sec["kscale"], self.table)
+            v = tq4.value_dequant(sec["vcode"], sec["vscale"], sec["vmin"])
+        else:
+            sec = layout.mxfp4_read_block(recs, self.d)
+            k = mxfp4.mx_decode(sec["kcode"], sec["kexp"])
+            v = mxfp4.mx_decode(sec["vcode"], sec["vexp"])
+        return (np.asarray(k, dtype=np.float32).reshape(shape), np.asarray(v, dtype=np.float32).reshape(shape))
+
     def sequence_tokens(self, block_row, length, kv_head):
         """Dequantized tokens 0..length-1 of one sequence and kv-head, read
         through its block-table row.  Returns (k_hat_rot, v_hat) as fp64

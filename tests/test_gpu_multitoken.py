@@ -210,3 +210,19 @@ def test_direct_kernel_whole_short_contexts_bf16_and_long_splits():
                                  seed=223)
     say("case: multi-token direct, 1024-block splits (block ids fetched in chunks of 32 pairs per wave)")
     _run(Case(cfg), 8)
+
+
+@pytest.mark.parametrize("fmt,v_scale,m,seed", [
+    (0, 3.0e4, [3, 8, 1], 231),        # scales >= 4096: direct kernel (at most 32 rows)
+    (0, 3.0e4, [40, 12, 25], 232),     # and the staged kernel
+    (2, 3.0e4, [40, 12, 25], 233),
+    (0, 1.0e-6, [3, 8, 1], 234),       # fp16-subnormal scales and minima
+    (0, 1.0e-6, [40, 12, 25], 235),
+])
+def test_value_range_edges(fmt, v_scale, m, seed):
+    """Value groups beyond the fp16 range and tiny ones: the dequantized values
+    enter the products exactly in both kernels."""
+    cfg = workloads.small_config(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(60, 500),
+                                 seed=seed, fmt=fmt, v_scale=v_scale)
+    say(f"case: multi-token value range fmt={fmt} v_scale={v_scale:g} m={m} seed={seed}")
+    _run(Case(cfg), np.array(m))

@@ -48,6 +48,11 @@ class Config:
     identity_table: bool = False
     seed: int = 0
     softmax_scale: float = field(default=0.0)
+    # magnitude multipliers of the drawn K, V and q (1: the distributions
+    # above; other values give the range edge cases of the parity tests)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    q_scale: float = 1.0
 
     @property
     def scale(self):
@@ -120,6 +125,8 @@ class Workload:
         self.total_lens = self.prompt_lens + c.appended
         # 4. queries, one set per decode step
         qf = g.standard_normal(size=(c.decode_steps, c.batch, c.num_q_heads, d), dtype=np.float32)
+        if c.q_scale != 1.0:
+            qf *= np.float32(c.q_scale)
         self.q_bits = f32_to_bf16_bits(qf)
         # 5. block table and pool size
         self._build_table(g)
@@ -158,6 +165,10 @@ class Workload:
         k += self.bias[None]
         for h in range(c.num_kv_heads):
             k[:, h, self.outlier_idx[h]] *= np.float32(c.outlier_mult)
+        if c.k_scale != 1.0:
+            k *= np.float32(c.k_scale)
+        if c.v_scale != 1.0:
+            v *= np.float32(c.v_scale)
         return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
     def shared_prefix(self):
@@ -280,8 +291,10 @@ def calibration_keys(layers=32, tokens=20, num_kv_heads=8, head_dim=128, seed=10
 
 
 def small_config(name="small", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(1, 200),
-                 fmt=0, seed=7, shared_seqs=0, shared_tokens=0, outliers=2, bias_std=0.5, identity_table=False):
+                 fmt=0, seed=7, shared_seqs=0, shared_tokens=0, outliers=2, bias_std=0.5, identity_table=False,
+                 k_scale=1.0, v_scale=1.0, q_scale=1.0):
     """A small ragged configuration for parity tests (several tiles, a ragged tail)."""
     return Config(name, batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                   ctx_range=ctx_range, shared_seqs=shared_seqs, shared_tokens=shared_tokens, outliers=outliers,
-                  bias_std=bias_std, fmt=fmt, seed=seed, identity_table=identity_table)
+                  bias_std=bias_std, fmt=fmt, seed=seed, identity_table=identity_table, k_scale=k_scale,
+                  v_scale=v_scale, q_scale=q_scale)
