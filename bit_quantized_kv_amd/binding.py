@@ -23,7 +23,7 @@ EXPORTS = (
     "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention", "tq_free",
     "tq_status_string", "tq_last_error", "tq_calibrate_workspace_bytes", "tq_calibrate_key_tables",
     "tq_select_layers", "tq_multitoken_workspace_bytes", "tq_multitoken_attention", "tq_cascade_workspace_bytes",
-    "tq_cascade_decode_attention", "tq_debug_dequantize",
+    "tq_cascade_decode_attention", "tq_debug_dequantize", "tq_decode_attention_noalloc",
 )
 
 
@@ -78,6 +78,8 @@ def _load():
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                          ctypes.c_size_t, P], ctypes.c_int),
         "tq_debug_dequantize": ([P, P, ctypes.c_int32, P, P, P], ctypes.c_int),
+        "tq_decode_attention_noalloc": ([P, P, P, ctypes.c_int32, P, ctypes.c_int32, P, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P], ctypes.c_int),
         "tq_free": ([P], None),
         "tq_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
@@ -178,6 +180,16 @@ def tq_decode_attention(cache, q, out, block_table, context_lens, max_context_le
     _check(LIB.tq_decode_attention(cache, _ptr(q), _ptr(out), out_dtype, _ptr(block_table),
                                    int(block_table.shape[1]), _ptr(context_lens), b, hq, int(max_context_len),
                                    float(softmax_scale), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def tq_decode_attention_noalloc(cache, q, out, block_table, context_lens, max_context_len, softmax_scale,
+                                stream=None):
+    """tq_decode_attention without a workspace (the library's fixed scratch)."""
+    b, hq, _ = q.shape
+    out_dtype = TQ_OUT_BF16 if str(out.dtype) == "torch.bfloat16" else TQ_OUT_F32
+    _check(LIB.tq_decode_attention_noalloc(cache, _ptr(q), _ptr(out), out_dtype, _ptr(block_table),
+                                           int(block_table.shape[1]), _ptr(context_lens), b, hq,
+                                           int(max_context_len), float(softmax_scale), _stream(stream)))
 
 
 def tq_multitoken_workspace_bytes(cache, batch, num_q_heads, num_tokens, max_query_len, max_context_len):

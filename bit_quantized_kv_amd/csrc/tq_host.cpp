@@ -213,10 +213,39 @@ tq_status tq_decode_workspace_bytes(const tq_cache *cache, int32_t batch, int32_
   return TQ_OK;
 }
 
+namespace {
+
+// Decode attention with the workspace given (the caller's, or the fixed
+// scratch of the no-allocation entry point).
+tq_status decode_impl(tq_cache *cache, const void *q, void *out, int32_t out_dtype, const int32_t *block_table,
+                      int32_t max_blocks, const int32_t *context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t max_context_len, float softmax_scale, void *workspace, size_t workspace_bytes,
+                      void *stream, bool fixed_scratch);
+
+}  // namespace
+
 tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
                               const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
                               int32_t batch, int32_t num_q_heads, int32_t max_context_len, float softmax_scale,
                               void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(cache, q, out, out_dtype, block_table, max_blocks, context_lens, batch, num_q_heads,
+                     max_context_len, softmax_scale, workspace, workspace_bytes, stream, false);
+}
+
+tq_status tq_decode_attention_noalloc(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                                      const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                                      int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                      float softmax_scale, void *stream) {
+  return decode_impl(cache, q, out, out_dtype, block_table, max_blocks, context_lens, batch, num_q_heads,
+                     max_context_len, softmax_scale, nullptr, 0, stream, true);
+}
+
+namespace {
+
+tq_status decode_impl(tq_cache *cache, const void *q, void *out, int32_t out_dtype, const int32_t *block_table,
+                      int32_t max_blocks, const int32_t *context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t max_context_len, float softmax_scale, void *workspace, size_t workspace_bytes,
+                      void *stream, bool fixed_scratch) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
   if (batch < 0) return fail(TQ_ERR_INVALID_ARG, "batch must be >= 0");
   if (batch == 0) return TQ_OK;
@@ -237,6 +266,15 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
   const tq::SplitPlan p = tq::plan_split(batch, hkv, max_context_len);
   size_t need = 0;
   tq_decode_workspace_bytes(cache, batch, num_q_heads, max_context_len, &need);
+  if (fixed_scratch && need) {
+    if (need > tq::kNoallocScratchBytes)
+      return fail(TQ_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
+                                        " bytes of split partials, more than the fixed scratch of " +
+                                        std::to_string(tq::kNoallocScratchBytes) + " bytes");
+    hipError_t e = tq::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "fixed scratch lookup");
+    workspace_bytes = tq::kNoallocScratchBytes;
+  }
   if (need && (!workspace || workspace_bytes < need))
     return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_decode_workspace_bytes (" + std::to_string(need) + ")");
 
@@ -275,6 +313,8 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
   }
   return TQ_OK;
 }
+
+}  // namespace
 
 namespace {
 

@@ -89,6 +89,12 @@ struct MultiTokenArgs {
   int32_t part_stride, slot0;
 };
 
+// The fixed device scratch of tq_decode_attention_noalloc (noalloc.hip):
+// its size, and its address on the current device (looked up on the first
+// call per device).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // Launchers (defined next to their kernels).
 hipError_t launch_tq4_quantize(int d, int vbits, const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_tq4_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s);

@@ -181,6 +181,21 @@ tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t
                               int32_t batch, int32_t num_q_heads, int32_t max_context_len, float softmax_scale,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* tq_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and result without a workspace.  The
+ * split-K partials go to a fixed device scratch of the library, 32 MiB
+ * (33554432 bytes) per GPU, held from the first call on that GPU until the
+ * process ends; sizes whose tq_decode_workspace_bytes exceeds it return
+ * TQ_ERR_WORKSPACE.  Nothing is allocated and nothing needs clearing: every
+ * partial the merge reads is written by the same call first.  All calls on
+ * one GPU share its scratch, so calls that overlap on one GPU (several
+ * streams, several threads) race; serialise them.  Asynchronous. */
+tq_status tq_decode_attention_noalloc(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
+                                      const int32_t *block_table, int32_t max_blocks, const int32_t *context_lens,
+                                      int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                      float softmax_scale, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Multi-token attention over the compressed cache (TQ4/4): chunked prefill of
  * new tokens, or the verification of several proposed tokens.  The time to
