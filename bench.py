@@ -20,7 +20,7 @@ quantize rate; ``roofline`` the kernel that takes most of the step time
 against the 8 TB/s HBM peak; ``cpu_baseline`` the CPU oracle timed on this
 host on a bounded sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama8b]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config agentic]
 """
 import argparse
 import hashlib
@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="llama8b",
+    p.add_argument("--config", default="agentic",
                    choices=["llama8b", "agentic", "longprefix", "fp4", "tq4v2", "calib", "verify", "prefill",
                             "cascade"],
                    help="calib: the calibrated key-table fit of a 32-layer stack; verify / prefill: multi-token "
@@ -211,61 +211,141 @@ class Bench:
             self.decode(dc, s)
 
 
-def cpu_baseline(cfg, budget_s=10.0):
-    """The CPU oracle, as it stands, on a bounded sample of the workload:
-    (sequence, kv-head) units in order, each quantized and then decoded for
-    its g query heads, until about ``budget_s`` seconds of CPU work."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_worker(cfg, unit_q, deadline_s, barrier, out_q):
+    """One oracle worker process: after the start barrier, take (sequence,
+    kv-head) units from the shared queue and quantize them until the deadline
+    (seconds after the start); wait for every worker; decode the units it
+    quantized; wait again; then count the near-ties of its rows and report."""
     try:
         from threadpoolctl import threadpool_limits
+        _limits = threadpool_limits(limits=1)  # noqa: F841  (kept for the worker's life)
     except ImportError:
-        threadpool_limits = None
+        pass
+    import queue
+
     import workloads
-    from oracle import attention, paged
+    from oracle import attention, paged, tq4
     w = workloads.make(cfg)
     c = w.cfg
     g = c.num_q_heads // c.num_kv_heads
     lens = w.context_lens_at(0)
     q_all = workloads.bf16_bits_to_f32(w.query_bits(0))
-    tq = td = 0.0
-    toks = units = 0
-    ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx_mgr:
-        ctx_mgr.__enter__()
-    try:
-        for b in range(c.batch):
-            T = int(lens[b])
-            k, v = w.sequence_kv(b)
-            for h in range(c.num_kv_heads):
-                pool = paged.PagedPool(c.fmt, w.num_blocks, 1, c.head_dim)
-                t0 = time.perf_counter()
-                pool.append(workloads.bf16_bits_to_f32(k[:T, h:h + 1]), workloads.bf16_bits_to_f32(v[:T, h:h + 1]),
-                            w.slots(b, 0, T))
-                t1 = time.perf_counter()
-                attention.decode(pool, q_all[:, h * g:(h + 1) * g], w.block_table, lens, c.scale,
-                                 rows=[(b, j) for j in range(g)])
-                t2 = time.perf_counter()
-                tq += t1 - t0
-                td += t2 - t1
-                toks += T
-                units += 1
-                if tq + td >= budget_s:
-                    break
-            if tq + td >= budget_s:
-                break
-    finally:
-        if ctx_mgr:
-            ctx_mgr.__exit__(None, None, None)
+    res = {"tq": 0.0, "td": 0.0, "toks": 0, "units": 0, "kel": 0, "kties": 0, "kdiff": 0, "kfree": 0,
+           "vel": 0, "vties": 0, "vdiff": 0, "vfree": 0}
+    done = []
+    barrier.wait()
+    start = time.perf_counter()
+    while time.perf_counter() - start < deadline_s:
+        try:
+            b, h = unit_q.get_nowait()
+        except queue.Empty:
+            break
+        T = int(lens[b])
+        k, v = w.sequence_kv(b)
+        kf, vf = workloads.bf16_bits_to_f32(k[:T, h:h + 1]), workloads.bf16_bits_to_f32(v[:T, h:h + 1])
+        pool = paged.PagedPool(c.fmt, w.num_blocks, 1, c.head_dim)
+        pool.append(kf, vf, w.slots(b, 0, T))
+        done.append((b, h, pool, kf[:, 0], vf[:, 0]))
+        res["toks"] += T
+        res["units"] += 1
+    barrier.wait()
+    for b, h, pool, _, _ in done:
+        attention.decode(pool, q_all[:, h * g:(h + 1) * g], w.block_table, lens, c.scale,
+                         rows=[(b, j) for j in range(g)])
+    barrier.wait()
+    # near-ties of the sampled rows (after the timed phases): the fp32
+    # decision rule (the kernels' rule) against the exact fp64 rule and its
+    # near-tie flags; a difference away from a flagged near-tie would be a
+    # fault of the rules
+    if c.fmt in (0, 2):
+        levels = 15 if c.fmt == 0 else 3
+        for _, _, pool, kf, vf in done:
+            s = tq4.key_scale(kf)
+            kc = tq4.key_codes(kf, s, pool.table)
+            kx, knear = tq4.key_codes_exact(kf, s, pool.table)
+            vc, sc, mn = tq4.value_encode(vf, levels)
+            vx, vnear = tq4.value_codes_exact(vf, sc, mn, levels=levels)
+            res["kel"] += kc.size
+            res["kties"] += int(knear.sum())
+            res["kdiff"] += int((kc != kx).sum())
+            res["kfree"] += int(((kc != kx) & ~knear).sum())
+            res["vel"] += vc.size
+            res["vties"] += int(vnear.sum())
+            res["vdiff"] += int((vc != vx).sum())
+            res["vfree"] += int(((vc != vx) & ~vnear).sum())
+    out_q.put(res)
+
+
+def cpu_baseline(cfg, deadline_s=10.0):
+    """The CPU oracle, as it stands, on a bounded sample of the workload, run
+    in worker processes over this host's cores (at most 16; BLAS limited to
+    one thread each).  Phase 1: the workers take (sequence, kv-head) units in
+    order from a shared queue and quantize each unit's tokens, until
+    ``deadline_s`` seconds have passed; phase 2: each worker decodes the g
+    query heads of its units.  Each phase is timed on the wall clock between
+    barriers.  Run before the GPU is initialised (the workers are forked).
+    Also returns the near-tie counts of the sampled rows."""
+    import multiprocessing as mp
+
+    import workloads
+    c = cfg
+    units = [(b, h) for b in range(c.batch) for h in range(c.num_kv_heads)]
+    ncores = max(1, min(len(os.sched_getaffinity(0)), 16, len(units)))
+    ctx = mp.get_context("fork")
+    unit_q = ctx.Queue()
+    for u in units:
+        unit_q.put(u)
+    time.sleep(0.2)                      # the queue's feeder thread has flushed
+    barrier = ctx.Barrier(ncores + 1)
+    out_q = ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker, args=(cfg, unit_q, deadline_s, barrier, out_q)) for _ in range(ncores)]
+    for p in procs:
+        p.start()
+    barrier.wait()                       # workers ready: phase 1 starts
+    t0 = time.perf_counter()
+    barrier.wait()                       # phase 1 (quantize) done
+    t1 = time.perf_counter()
+    barrier.wait()                       # phase 2 (decode) done
+    t2 = time.perf_counter()
+    parts = [out_q.get() for _ in procs]
+    for p in procs:
+        p.join()
+    tot = {k: sum(r[k] for r in parts) for k in parts[0]}
     d = c.head_dim
     row = {0: d + 2 + d // 8, 1: d + d // 16, 2: 3 * d // 4 + 2 + d // 8}[c.fmt]   # bytes per token-head
-    return {
-        "value": toks * row / td / 1e9,
+    toks = tot["toks"]
+    g = c.num_q_heads // c.num_kv_heads
+    res = {
+        "value": toks * row / (t2 - t1) / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": ncores,
         "kind": "oracle",
-        "sample": f"{c.name}: {units} (sequence, kv-head) units, {toks} token-heads: quantize {tq:.2f} s, "
-                  f"decode of their {g} query heads each {td:.2f} s (numpy fp64, BLAS limited to 1 thread)",
-        "quantize_tokens_per_s": toks / tq / c.num_kv_heads,
+        "cpu_model": _cpu_model(),
+        "sample": f"{c.name}: the first {tot['units']} of {len(units)} (sequence, kv-head) units, {toks} token-heads, "
+                  f"on {ncores} worker processes: quantize {t1 - t0:.2f} s, decode of their {g} query heads each "
+                  f"{t2 - t1:.2f} s wall (numpy fp64, BLAS limited to 1 thread per worker)",
+        "quantize_tokens_per_s": toks / (t1 - t0) / c.num_kv_heads,
     }
+    if c.fmt in (0, 2):
+        res["near_ties"] = {
+            "key_codes": tot["kel"], "key_near_ties": tot["kties"], "key_rule_differences": tot["kdiff"],
+            "key_differences_not_flagged": tot["kfree"],
+            "value_codes": tot["vel"], "value_near_ties": tot["vties"], "value_rule_differences": tot["vdiff"],
+            "value_differences_not_flagged": tot["vfree"],
+            "rule": "codes of the sampled rows by the fp32 decision rule (the kernels' rule; the GPU's codes are "
+                    "bit-identical to it) against the exact fp64 rule; near-tie = gap below 1e-5 code units",
+        }
+    return res
 
 
 def traffic_from_profiles(cfg_name, kernel):
@@ -656,9 +736,7 @@ def main():
     if args.config in ("verify", "prefill"):
         bench_multitoken(args)
         return
-    import torch
     import workloads
-    torch.cuda.set_device(0)
     cascade = args.config == "cascade"
     cfg_name = "agentic" if cascade else args.config
     if args.config == "tq4v2":
@@ -666,6 +744,10 @@ def main():
         cfg = dataclasses.replace(workloads.CONFIGS["llama8b"], name="tq4v2", fmt=2)
     else:
         cfg = workloads.CONFIGS[cfg_name]
+    # the CPU oracle first: its worker processes are forked before any GPU use
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+    import torch
+    torch.cuda.set_device(0)
     bench = Bench(cfg, args.copies, cascade=cascade, group_blocks=args.cascade_group_blocks,
                   group_members=args.cascade_group_members)
     c = bench.cfg
@@ -738,8 +820,10 @@ def main():
     if a_ms is not None:
         res["append_1tok_us"] = round(a_ms * 1e3, 2)
         res["append_1tok_GBps"] = round(bench.append_bytes() / (a_ms * 1e-3) / 1e9, 1)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+        if "near_ties" in cpu:
+            res["near_ties"] = cpu["near_ties"]
     print(json.dumps(res))
 
 

@@ -36,4 +36,4 @@ def test_report_fields(config):
     assert r["bound"] in ("hbm", "mfma", "alu") and r["unit"] in ("GB/s", "TFLOP/s")
     assert 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     if config is None:
-        assert d["unit"] == "GB/s" and d["config"]["workload"].startswith("llama8b")
+        assert d["unit"] == "GB/s" and d["config"]["workload"].startswith("agentic")
