@@ -173,7 +173,11 @@ tq_status tq_decode_workspace_bytes(const tq_cache *cache, int32_t batch, int32_
  * [0, max_context_len] with ceil(len/16) <= max_blocks (trusted); a zero
  * length gives a zero row.  num_q_heads must be num_kv_heads * g with
  * g in {1, 2, 4, 8}.  max_context_len is the host's bound, used to size the
- * split.  softmax_scale > 0 (e.g. 1/sqrt(head_dim)).  workspace: device buffer
+ * split.  softmax_scale > 0 (e.g. 1/sqrt(head_dim)).  TQ4 formats: the
+ * rotated query times softmax_scale * log2(e) / sqrt(head_dim) is carried as
+ * two fp16 parts, so each of its elements must stay within 65504 (at
+ * head_dim 128 with the default scale: query elements below 4.5e4; not
+ * checked, the values are on the device).  workspace: device buffer
  * of at least tq_decode_workspace_bytes (may be NULL when that is 0).
  * Asynchronous. */
 tq_status tq_decode_attention(tq_cache *cache, const void *q, void *out, int32_t out_dtype,
