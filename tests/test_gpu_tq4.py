@@ -135,12 +135,37 @@ def test_both_quantize_loops(_loop_env, loop, fmt, d, hkv, seed):
     one task or a pair at a time) writes the oracle's bytes, for TQ4/4 and
     TQ4/2 at both head sizes."""
     os.environ["TQ_QUANT_LOOP"] = loop
-    # about 15000 tokens: the balanced loop's 256 work-groups take 10 to 30
-    # tasks each, so waves ask the counter more than once
+    # about 15000 tokens: the balanced loop's 256 work-groups take 3 to 30
+    # tasks each (the counter is asked in some of them; the long launches
+    # below make every wave ask it)
     cfg = workloads.small_config(batch=6, num_q_heads=4 * hkv, num_kv_heads=hkv, head_dim=d, ctx_range=(1500, 3000),
                                  seed=seed, fmt=fmt)
     say(f"case: quantize loop {loop}, format {fmt}, d={d}, hkv={hkv}, seed={seed}")
     _check_case(Case(cfg))
+
+
+@pytest.mark.parametrize("loop,fmt,d,hkv,seed", [("balanced", 0, 128, 2, 145), ("balanced-pairs", 0, 128, 2, 146),
+                                                 ("balanced-pairs", 2, 64, 4, 147)])
+def test_balanced_loop_hands_out_from_the_counter(_loop_env, loop, fmt, d, hkv, seed):
+    """A launch long enough that every work-group of the balanced loop takes
+    several times the 16 (one by one) or 32 (pairs) tasks its waves start
+    with, so that tasks and pairs of tasks come from the LDS counter; the
+    records match the oracle's byte for byte."""
+    os.environ["TQ_QUANT_LOOP"] = loop
+    cfg = workloads.small_config(batch=8, num_q_heads=4 * hkv, num_kv_heads=hkv, head_dim=d, ctx_range=(12000, 16000),
+                                 seed=seed, fmt=fmt)
+    case = Case(cfg)
+    tpw = 8 if d == 128 else 16
+    tasks_per_wg = int(case.w.total_lens.sum()) // tpw * hkv / 256
+    say(f"case: quantize loop {loop}, format {fmt}, d={d}, hkv={hkv}, seed={seed}, "
+        f"about {tasks_per_wg:.0f} tasks per work-group")
+    assert tasks_per_wg > 3 * 32
+    ranges = case.write_ranges()
+    case.quantize(ranges)
+    op = case.oracle_pool(ranges)
+    gpu = case.pool_np()
+    bad = np.nonzero(np.any(gpu != op.pool, axis=(1, 2)))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ from the oracle's, first {bad[:4]}"
 
 
 def test_pool_beyond_4_gib():
