@@ -343,6 +343,7 @@ hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s) {
                                             (const void *)mxfp4_quantize_kernel<true>, kD, a.num_tokens, a.hkv);
   QuantizeArgs b = a;
   b.grain = g.grain;
+  b.window = g.window;
   if (g.balanced) hipLaunchKernelGGL(mxfp4_quantize_kernel<true>, dim3(g.grid), dim3(g.threads), 0, s, b);
   else hipLaunchKernelGGL(mxfp4_quantize_kernel<false>, dim3(g.grid), dim3(g.threads), 0, s, b);
   return hipGetLastError();

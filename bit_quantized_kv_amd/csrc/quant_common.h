@@ -247,78 +247,201 @@ __device__ __forceinline__ void quantize_loop_static(const QuantizeArgs &a, int 
   }
 }
 
-// The balanced persistent loop (launches with many tasks per wave).  A wave
-// task is (chunk of TPW tokens, kv-head), numbered chunk * Hkv + head: the
-// wave codes tokens chunk * TPW + tw of that head.  One work-group of 16 waves
-// per compute unit takes an equal contiguous range of the tasks; inside it,
-// wave w starts with the range's first task (or pair of tasks) after w * grain,
-// and every later one goes to the wave that asks first (an LDS counter).  With four work-groups per unit and fixed
-// shares, the unit's arbiter favours the oldest: on long launches the first
-// ended at 0.6 of the run while the last ran its end on a partly idle unit;
-// here the waves of a unit end together.  Two row buffers, as above (past the
-// range, the range's first task is loaded again).
+// Rows of one task of the balanced loop: the item of `len` tokens starting at
+// token tb, whose first row sits at `lead` of its TPW-row span.  Lane token
+// index tw takes token tb + tw - lead, so each row lands on the lanes of its
+// own position in the span; the other lanes load a token of the item again
+// (every load is valid) and are not `valid`.
+template <int D>
+__device__ __forceinline__ void load_item_row(RowLoad<D> &o, const QuantizeArgs &a, int64_t tb, int lead, int len,
+                                              int h, int tw, int li) {
+  const int j = tw - lead;
+  const int t = j < 0 ? 0 : (j >= len ? len - 1 : j);
+  const int64_t ubase = (tb * a.hkv + h) * D;
+  const uint32_t loff = ((uint32_t)t * (uint32_t)a.hkv * D + (uint32_t)li * 16u) * 2u;
+  const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.k + ubase);
+  const uint8_t *vb = reinterpret_cast<const uint8_t *>(a.v + ubase);
+  o.k0 = *reinterpret_cast<const uint4 *>(kb + loff);
+  o.k1 = *reinterpret_cast<const uint4 *>(kb + loff + 16);
+  o.v0 = *reinterpret_cast<const uint4 *>(vb + loff);
+  o.v1 = *reinterpret_cast<const uint4 *>(vb + loff + 16);
+  o.slot = (a.slots + tb)[t];
+  o.valid = j >= 0 && j < len;
+}
+
+// Most tokens one pass of the balanced loop lists (6 bytes of LDS each).
+constexpr int kItemWindow = 8192;
+static_assert(3 * kQuantThreadsBal <= kItemWindow, "the first round's slots are parked in the item list");
+
+// The balanced persistent loop (launches with many tasks per wave).  One
+// work-group of 16 waves per compute unit takes an equal contiguous range of
+// the tokens and cuts it into items: the longest runs of tokens whose slots are
+// consecutive rows of one aligned TPW-row span of a block (half a block at
+// D = 128, the block at D = 64).  Tokens with a negative slot belong to no
+// item.  A task is (item, kv-head), numbered item * Hkv + head; wave w starts
+// with task w * grain and every later task (or pair of tasks) goes to the wave
+// that asks first (an LDS counter), so the waves of a unit end together (with
+// fixed shares per work-group, the unit's arbiter favours the oldest).  A
+// wave puts row r of a span on its lanes of token index r mod TPW, so the rows
+// of a whole item of four aligned rows sit where the record's four-row words
+// want them, however the launch's token order is cut into sequences.  The
+// range is listed in windows of at most a.window tokens (a work-group-wide
+// ballot scan; items are cut at window edges).  Two row buffers: every step
+// loads the next task into one (past the window's tasks, its first task again)
+// while coding the other.  `stage` runs once (table staging); `code(row, h)`
+// codes one row.
 template <int D, class Stage, class Code>
 __device__ __forceinline__ void quantize_loop_balanced(const QuantizeArgs &a, int wv, int tw, int li, Stage stage,
                                                        Code code) {
   constexpr int TPW = QLanes<D>::TPW;
+  constexpr int NWAVE = kQuantThreadsBal / 64;
+  __shared__ uint32_t s_first[kItemWindow];  // item k: window offset of its first token | its lead << 16
+  __shared__ uint16_t s_last[kItemWindow];   // item k: window offset of its last token
+  __shared__ int s_cnt[2][NWAVE];            // item starts and ends found by each wave in one round
   __shared__ int s_next;
-  const uint32_t hkv = (uint32_t)a.hkv;
-  const int64_t tasks = (a.num_tokens + TPW - 1) / TPW * hkv;
-  // this work-group's range [lo, lo + count) and its first task as (chunk c0,
-  // head h0); 32-bit arithmetic whenever the task count allows it.  count
-  // fits an int: a launch's K and V (512 B per token-head) lie in device
-  // memory, so it has well under 2^31 tasks per compute unit
-  int64_t c0;
-  int count, h0;
-  if (tasks <= 0x7FFFFFFF) {
-    const uint32_t t32 = (uint32_t)tasks, g = gridDim.x, b = blockIdx.x;
-    const uint32_t q = t32 / g, r = t32 % g;
-    const uint32_t lo = b * q + (b < r ? b : r);
-    count = (int)(q + (b < r ? 1u : 0u));
-    c0 = lo / hkv;
-    h0 = (int)(lo % hkv);
-  } else {
-    const int64_t g = gridDim.x, b = blockIdx.x, q = tasks / g, r = tasks % g;
-    const int64_t lo = b * q + (b < r ? b : r);
-    count = (int)(q + (b < r ? 1 : 0));
-    c0 = lo / hkv;
-    h0 = (int)(lo - c0 * hkv);
-  }
-  // task n of the range as (first token, head); n past the range: task 0
-  auto locate = [&](int n, int64_t &t0, int &h) {
-    const uint32_t m = (uint32_t)h0 + (uint32_t)(n < count ? n : 0);
-    t0 = (c0 + m / hkv) * TPW;
-    h = (int)(m % hkv);
-  };
-  // grain 2: tasks go out in pairs (2k, 2k + 1), one round trip per two
-  // tasks; grain 1: one by one
+  const int lane = (int)(threadIdx.x & 63);
+  const int hkv = a.hkv;
+  const int64_t n_tok = a.num_tokens, g = gridDim.x, b = blockIdx.x;
+  const int64_t t_lo = n_tok * b / g, t_hi = n_tok * (b + 1) / g;
+  const int win = a.window >= 1 && a.window <= kItemWindow ? a.window : kItemWindow;
   const int grain = a.grain;
   auto grab = [&]() {
     int x = 0;
-    if ((threadIdx.x & 63) == 0)
-      x = __hip_atomic_fetch_add(&s_next, grain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) x = __hip_atomic_fetch_add(&s_next, grain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return __builtin_amdgcn_readfirstlane(x);
   };
-  int n = grain * wv, h;
-  int64_t t0;
-  locate(n, t0, h);
-  RowLoad<D> ra, rb;
-  load_row<D>(ra, a, t0, h, tw, li);
-  if (threadIdx.x == 0) s_next = grain * (int)(blockDim.x >> 6);
-  stage();
-  __syncthreads();
-  while (n < count) {
-    const int n2 = grain == 2 ? n + 1 : grab();  // the pair's second task, or the next one
-    int h2;
-    int64_t t2;
-    locate(n2, t2, h2);
-    load_row<D>(rb, a, t2, h2, tw, li);
-    code(ra, h);
-    if (n2 >= count) break;
-    n = grab();
-    locate(n, t0, h);
-    load_row<D>(ra, a, t0, h, tw, li);
-    code(rb, h2);
+  // slots of window token i and of its neighbours (-1 past the window's
+  // ends); the three loads are independent and always in range (0 <= i < wn)
+  auto slots3 = [&](int64_t w0, int wn, int i, uint32_t &sl, uint32_t &sp, uint32_t &sn) {
+    const int32_t *p = a.slots + w0;
+    sl = (uint32_t)p[i];
+    const uint32_t lp = (uint32_t)p[i > 0 ? i - 1 : 0], ln1 = (uint32_t)p[i + 1 < wn ? i + 1 : i];
+    sp = i > 0 ? lp : 0xFFFFFFFFu;
+    sn = i + 1 < wn ? ln1 : 0xFFFFFFFFu;
+  };
+  // the first round's slots are loaded before the table staging (the two
+  // waits overlap) and parked in LDS, where each thread reads its own back
+  {
+    const int wn0 = (int)(t_hi - t_lo < win ? t_hi - t_lo : win);
+    const int t0 = (int)threadIdx.x;
+    uint32_t sl = 0, sp = 0, sn = 0;
+    if (t0 < wn0) slots3(t_lo, wn0, t0, sl, sp, sn);
+    stage();
+    if (t0 < wn0) {
+      s_first[3 * t0] = sl;
+      s_first[3 * t0 + 1] = sp;
+      s_first[3 * t0 + 2] = sn;
+    }
+  }
+  for (int64_t w0 = t_lo; w0 < t_hi; w0 += win) {
+    const int wn = (int)(t_hi - w0 < win ? t_hi - w0 : win);
+    __syncthreads();  // the previous window's lists and counter are no longer used
+    // ---- the window's items, in token order ------------------------------------
+    // the thread index through an opaque copy, so that nothing the listing
+    // derives from it is kept in registers through the task loop
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int ln = tid & 63;
+    // items listed so far: by their starts and by their ends (an item can
+    // start in one round and end in the next, so the two differ between rounds)
+    int items = 0, ended = 0;
+    for (int r0 = 0; r0 < wn; r0 += kQuantThreadsBal) {
+      const int i = r0 + tid;
+      bool st = false, en = false;
+      uint32_t lead = 0;
+      if (i < wn) {
+        uint32_t sl, sp, sn;
+        if (w0 == t_lo && r0 == 0) {  // parked above (i = this thread's index)
+          sl = s_first[3 * i];
+          sp = s_first[3 * i + 1];
+          sn = s_first[3 * i + 2];
+        } else {
+          slots3(w0, wn, i, sl, sp, sn);
+        }
+        if ((int)sl >= 0) {
+          // a row continues the item of the row before it when its slot is
+          // the next one and not the first of a span
+          st = (int)sp < 0 || sl != sp + 1u || (sl & (TPW - 1)) == 0;
+          en = (int)sn < 0 || sn != sl + 1u || (sn & (TPW - 1)) == 0;
+          lead = sl & (TPW - 1);
+        }
+      }
+      const uint64_t bs = __builtin_amdgcn_ballot_w64(st), be = __builtin_amdgcn_ballot_w64(en);
+      if (ln == 0) {
+        s_cnt[0][wv] = __builtin_popcountll(bs);
+        s_cnt[1][wv] = __builtin_popcountll(be);
+      }
+      __syncthreads();
+      // the starts (ends) of the waves before this one and of all waves: lane
+      // w < NWAVE holds wave w's counts, summed over lanes 0 .. NWAVE - 1
+      static_assert(NWAVE == 16, "the sums below cover 16 lanes");
+      const int cw = ln < NWAVE ? ln : 0;
+      const int c_s = ln < NWAVE ? s_cnt[0][cw] : 0, c_e = ln < NWAVE ? s_cnt[1][cw] : 0;
+      uint32_t pre_s = ln < wv ? c_s : 0, pre_e = ln < wv ? c_e : 0, tot_s = c_s, tot_e = c_e;
+      pre_s += swz_xor_u<1>(pre_s);
+      pre_e += swz_xor_u<1>(pre_e);
+      tot_s += swz_xor_u<1>(tot_s);
+      tot_e += swz_xor_u<1>(tot_e);
+      pre_s += swz_xor_u<2>(pre_s);
+      pre_e += swz_xor_u<2>(pre_e);
+      tot_s += swz_xor_u<2>(tot_s);
+      tot_e += swz_xor_u<2>(tot_e);
+      pre_s += swz_xor_u<4>(pre_s);
+      pre_e += swz_xor_u<4>(pre_e);
+      tot_s += swz_xor_u<4>(tot_s);
+      tot_e += swz_xor_u<4>(tot_e);
+      pre_s += swz_xor_u<8>(pre_s);
+      pre_e += swz_xor_u<8>(pre_e);
+      tot_s += swz_xor_u<8>(tot_s);
+      tot_e += swz_xor_u<8>(tot_e);
+      // item number of this lane's start (end): the starts (ends) listed
+      // before it.  Every item has one start and one end, so both lists end
+      // with the same count, at most wn <= kItemWindow
+      const int ps = items + __builtin_amdgcn_readfirstlane((int)pre_s) +
+                     (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u));
+      const int pe = ended + __builtin_amdgcn_readfirstlane((int)pre_e) +
+                     (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      if (st) s_first[ps] = (uint32_t)i | (lead << 16);
+      if (en) s_last[pe] = (uint16_t)i;
+      items += __builtin_amdgcn_readfirstlane((int)tot_s);
+      ended += __builtin_amdgcn_readfirstlane((int)tot_e);
+      __syncthreads();  // the counts are read before the next round writes them; the lists are complete
+    }
+    const int ntask = items * hkv;
+    if (ntask == 0) continue;  // work-group-uniform
+    if (tid == 0) s_next = grain * NWAVE;
+    __syncthreads();
+    // ---- the window's tasks ---------------------------------------------------------
+    // task n (past the window's tasks: task 0) as (first token, lead, length, head)
+    auto locate = [&](int n, int64_t &tb, int &lead, int &len, int &h) {
+      const int m = n < ntask ? n : 0;
+      const int k = m / hkv;
+      h = m - k * hkv;
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_first[k]);
+      const int i0 = (int)(e & 0xFFFFu);
+      lead = (int)(e >> 16);
+      const int l = __builtin_amdgcn_readfirstlane((int)s_last[k]) - i0 + 1;
+      len = l < 1 ? 1 : l;  // always >= 1 for a complete list; kept so for every load
+      tb = w0 + i0;
+    };
+    int n = grain * wv, h, lead, len;
+    int64_t tb;
+    locate(n, tb, lead, len, h);
+    RowLoad<D> ra, rb;
+    load_item_row<D>(ra, a, tb, lead, len, h, tw, li);
+    while (n < ntask) {
+      const int n2 = grain == 2 ? n + 1 : grab();  // the pair's second task, or the next one
+      int h2, lead2, len2;
+      int64_t tb2;
+      locate(n2, tb2, lead2, len2, h2);
+      load_item_row<D>(rb, a, tb2, lead2, len2, h2, tw, li);
+      code(ra, h);
+      if (n2 >= ntask) break;
+      n = grab();
+      locate(n, tb, lead, len, h);
+      load_item_row<D>(ra, a, tb, lead, len, h, tw, li);
+      code(rb, h2);
+    }
   }
 }
 
@@ -341,7 +464,8 @@ __device__ __forceinline__ void quantize_loop(const QuantizeArgs &a, int wv, int
 // off instead; pairs cost 1.5% on the long launches (coarser balance).
 struct QuantGeometry {
   bool balanced;
-  int grain;  // balanced loop: tasks per hand-out
+  int grain;   // balanced loop: tasks per hand-out
+  int window;  // balanced loop: tokens listed per pass
   int grid, threads;
 };
 QuantGeometry quantize_geometry(const void *kernel_static, const void *kernel_balanced, int d, int64_t num_tokens,

@@ -155,6 +155,14 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
   }
 
   // ---- placement ----------------------------------------------------------------------
+  {
+    // derived again from an opaque copy of the lane, so that the compiler
+    // does not hold the store-address terms in registers through the task loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    li = QLanes<D>::li(l);
+    tq = QLanes<D>::tw(l) & 3;
+  }
   const bool aligned = quad_aligned<D>(slot, tq);
   const uint32_t vt0 = quad_transpose<D>(vc0, tq), vt1 = quad_transpose<D>(vc1, tq);
   const uint32_t scmn = scb | ((uint32_t)h_bits(mn16) << 16);
@@ -208,9 +216,8 @@ __global__ __launch_bounds__(BAL ? kQuantThreadsBal : kQuantThreads) void tq4_qu
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = L::li(lane), tw = L::tw(lane), tq = tw & 3;
+  const int li = L::li(lane), tw = L::tw(lane);
   const float bin_a = a.bins.a, bin_b = a.bins.b - 0.5f;  // v_cvt_pk_u8 rounds: floor via -0.5
-  const float sigma = wht16_sign(li);
   quantize_loop<D, BAL>(a, wv, tw, li,
                    [&] {
                      constexpr int NT = BAL ? kQuantThreadsBal : kQuantThreads;
@@ -219,7 +226,14 @@ __global__ __launch_bounds__(BAL ? kQuantThreadsBal : kQuantThreads) void tq4_qu
                      __syncthreads();
                    },
                    [&](const RowLoad<D> &row, int h) {
-                     quantize_row<D, VB>(a, row, h, lane, li, tq, s_bins, s_recip, bin_a, bin_b, sigma);
+                     // the lane's indices through an opaque copy, derived
+                     // again per row: held through the loop they would push
+                     // the balanced loop's registers into spills
+                     int l = lane;
+                     asm volatile("" : "+v"(l));
+                     const int li_r = L::li(l);
+                     quantize_row<D, VB>(a, row, h, l, li_r, L::tw(l) & 3, s_bins, s_recip, bin_a, bin_b,
+                                         wht16_sign(li_r));
                    });
 }
 
@@ -280,6 +294,13 @@ QuantGeometry quantize_geometry(const void *kernel_static, const void *kernel_ba
   QuantGeometry g;
   g.balanced = balanced;
   g.grain = grain;
+  // override for tests: TQ_ITEM_WINDOW = tokens listed per pass of the
+  // balanced loop (several passes per work-group at test sizes)
+  g.window = kItemWindow;
+  if (const char *env = std::getenv("TQ_ITEM_WINDOW")) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v >= 1 && v <= kItemWindow) g.window = (int)v;
+  }
   if (balanced) {
     g.threads = kQuantThreadsBal;
     g.grid = occ.cus * resident_per_cu(occ, kernel_balanced, kQuantThreadsBal, 1);
@@ -298,6 +319,7 @@ void launch_q(const QuantizeArgs &a, hipStream_t s) {
                                             (const void *)tq4_quantize_kernel<D, VB, true>, D, a.num_tokens, a.hkv);
   QuantizeArgs b = a;
   b.grain = g.grain;
+  b.window = g.window;
   if (g.balanced) hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, true>), dim3(g.grid), dim3(g.threads), 0, s, b);
   else hipLaunchKernelGGL((tq4_quantize_kernel<D, VB, false>), dim3(g.grid), dim3(g.threads), 0, s, b);
 }

@@ -34,6 +34,7 @@ struct QuantizeArgs {
   BinParams bins;
   float rsqrt_d;                 // fp32(1/sqrt(d))
   int32_t grain;                 // balanced quantize loop: tasks per hand-out (1 or 2)
+  int32_t window;                // balanced quantize loop: tokens listed per pass (1 .. kItemWindow)
 };
 
 struct DecodeArgs {

@@ -120,11 +120,12 @@ def test_unaligned_skipped_and_single_token_slots():
 
 @pytest.fixture
 def _loop_env():
-    saved = os.environ.pop("TQ_QUANT_LOOP", None)
+    saved = {k: os.environ.pop(k, None) for k in ("TQ_QUANT_LOOP", "TQ_ITEM_WINDOW")}
     yield
-    os.environ.pop("TQ_QUANT_LOOP", None)
-    if saved is not None:
-        os.environ["TQ_QUANT_LOOP"] = saved
+    for k, v in saved.items():
+        os.environ.pop(k, None)
+        if v is not None:
+            os.environ[k] = v
 
 
 @pytest.mark.parametrize("loop", ["static", "balanced", "balanced-pairs"])
@@ -164,6 +165,93 @@ def test_balanced_loop_hands_out_from_the_counter(_loop_env, loop, fmt, d, hkv, 
     case.quantize(ranges)
     op = case.oracle_pool(ranges)
     gpu = case.pool_np()
+    bad = np.nonzero(np.any(gpu != op.pool, axis=(1, 2)))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ from the oracle's, first {bad[:4]}"
+
+
+def _scattered_launch(rng, num_blocks, n_seq):
+    """Slots of one launch: sequences that start at arbitrary rows of fresh
+    blocks and run 1 to 300 rows (so the launch's token order cuts them
+    anywhere), a stretch of single rows at scattered slots, and skipped
+    tokens (-1) sprinkled over both."""
+    parts, blk = [], 0
+    for _ in range(n_seq):
+        off, length = int(rng.integers(0, 16)), int(rng.integers(1, 301))
+        parts.append(np.arange(blk * 16 + off, blk * 16 + off + length))
+        blk += (off + length + 15) // 16
+    used = np.concatenate(parts)
+    free = np.setdiff1d(np.arange(num_blocks * 16), np.arange(blk * 16))
+    scattered = rng.permutation(free)[:600]
+    slots = np.concatenate(parts[:n_seq // 2] + [scattered] + parts[n_seq // 2:]).astype(np.int32)
+    slots[rng.choice(slots.size, slots.size // 50, replace=False)] = -1
+    assert used.max() < num_blocks * 16
+    return slots
+
+
+@pytest.mark.parametrize("fmt,d,window,seed", [(0, 128, 97, 151), (0, 64, 61, 152), (2, 128, 8192, 153),
+                                               (2, 64, 200, 154), (1, 128, 113, 155)])
+def test_balanced_loop_items_and_windows(_loop_env, fmt, d, window, seed):
+    """The balanced loop cuts each work-group's token range into items (runs of
+    rows inside one aligned span of a block, placed on the lanes of their rows)
+    and lists them in windows.  Sequences starting at any row, scattered single
+    rows and skipped tokens, listed in windows of a few dozen tokens (several
+    per work-group) or in one, give the oracle's bytes for TQ4/4, TQ4/2 and
+    MX-FP4."""
+    from bit_quantized_kv_amd import Cache
+    from gpu_common import to_dev_bf16, to_dev_i32
+    from oracle import paged
+    os.environ["TQ_QUANT_LOOP"] = "balanced"
+    os.environ["TQ_ITEM_WINDOW"] = str(window)
+    rng = np.random.default_rng(seed)
+    hkv, num_blocks = 2, 2048
+    slots = _scattered_launch(rng, num_blocks, 120)
+    n = slots.size
+    kf = rng.standard_normal((n, hkv, d)).astype(np.float32) * np.float32(2.0)
+    vf = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    kb, vb = workloads.f32_to_bf16_bits(kf), workloads.f32_to_bf16_bits(vf)
+    say(f"case: balanced-loop items, format {fmt}, d={d}, window {window}, seed {seed}, {n} tokens")
+    cache = Cache(fmt, d, hkv, num_blocks)
+    cache.quantize_append(to_dev_bf16(kb), to_dev_bf16(vb), to_dev_i32(slots))
+    torch.cuda.synchronize()
+    gpu = cache.pool.cpu().numpy().reshape(num_blocks, hkv, -1)
+    op = paged.PagedPool(fmt, num_blocks, hkv, d)
+    op.append(workloads.bf16_bits_to_f32(kb), workloads.bf16_bits_to_f32(vb), slots)
+    bad = np.nonzero(np.any(gpu != op.pool, axis=(1, 2)))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ from the oracle's, first {bad[:4]}"
+
+
+@pytest.mark.parametrize("d,window,seed", [(64, 8192, 161), (128, 1100, 162)])
+def test_balanced_loop_listing_rounds(_loop_env, d, window, seed):
+    """Work-group ranges of more than 1024 tokens are listed in several rounds
+    of the work-group's threads, and items (runs of rows in one span of a
+    block) start in one round and end in the next.  About 300000 tokens of
+    sequences that start at any row of a block: the records match the
+    oracle's byte for byte (regression: the round-crossing items once got the
+    wrong last row)."""
+    from bit_quantized_kv_amd import Cache
+    from gpu_common import to_dev_bf16, to_dev_i32
+    from oracle import paged
+    os.environ["TQ_QUANT_LOOP"] = "balanced"
+    os.environ["TQ_ITEM_WINDOW"] = str(window)
+    rng = np.random.default_rng(seed)
+    parts, blk = [], 0
+    while sum(p.size for p in parts) < 300000:
+        off, length = int(rng.integers(0, 16)), int(rng.integers(1, 2000))
+        parts.append(np.arange(blk * 16 + off, blk * 16 + off + length))
+        blk += (off + length + 15) // 16
+    slots = np.concatenate(parts).astype(np.int32)
+    n, num_blocks = slots.size, blk
+    assert n // 256 > 1024  # every work-group lists its range in two rounds or more
+    kf = rng.standard_normal((n, 1, d)).astype(np.float32)
+    vf = rng.standard_normal((n, 1, d)).astype(np.float32) * np.float32(0.5)
+    kb, vb = workloads.f32_to_bf16_bits(kf), workloads.f32_to_bf16_bits(vf)
+    say(f"case: balanced-loop listing rounds, d={d}, window {window}, seed {seed}, {n} tokens")
+    cache = Cache(0, d, 1, num_blocks)
+    cache.quantize_append(to_dev_bf16(kb), to_dev_bf16(vb), to_dev_i32(slots))
+    torch.cuda.synchronize()
+    gpu = cache.pool.cpu().numpy().reshape(num_blocks, 1, -1)
+    op = paged.PagedPool(0, num_blocks, 1, d)
+    op.append(workloads.bf16_bits_to_f32(kb), workloads.bf16_bits_to_f32(vb), slots)
     bad = np.nonzero(np.any(gpu != op.pool, axis=(1, 2)))[0]
     assert bad.size == 0, f"{bad.size} blocks differ from the oracle's, first {bad[:4]}"
 
