@@ -61,6 +61,16 @@ def parse():
     return p.parse_args()
 
 
+def payload_row_bytes(fmt, d):
+    """Bytes of the record sections per (token, kv-head), the padding of a
+    record to whole 128-byte lines excluded (algorithmic bytes)."""
+    g = d // 32
+    if fmt == 1:
+        return d // 2 + d // 2 + g + g           # MX-FP4: codes, exponent bytes
+    vcode = d // 2 if fmt == 0 else d // 4       # TQ4/4 or TQ4/2 value codes
+    return d // 2 + vcode + 4 * g + 2            # key codes, value codes, (scale, min), key scale
+
+
 def kernel_source_hash():
     """Hash of the native sources with comments and whitespace taken out, so
     that stored counters stay valid across edits of comments only."""
@@ -121,7 +131,7 @@ class Bench:
                 sa = np.array([w.slots(b, int(t[b]), int(t[b]) + 1)[0] for b in range(c.batch)])
                 self.appends.append((dev(ka), dev(va), i32(sa)))
         rec_bytes = Cache(c.fmt, c.head_dim, c.num_kv_heads, 1).record_bytes
-        self.row_bytes = rec_bytes // 16
+        self.row_bytes = payload_row_bytes(c.fmt, c.head_dim)
         pool_bytes = rec_bytes * c.num_kv_heads * w.num_blocks
         in_bytes = k0.numel() * 4
         # rotating copies so that no launch finds its data in the 256 MB
@@ -553,7 +563,7 @@ class MtBench:
         self.max_ctx = int(self.ctx_np.max())
         self.table = i32(w.block_table)
         rec = Cache(c.fmt, c.head_dim, c.num_kv_heads, 1).record_bytes
-        self.row_bytes = rec // 16
+        self.row_bytes = payload_row_bytes(c.fmt, c.head_dim)
         pool_bytes = rec * c.num_kv_heads * w.num_blocks
         self.copies = copies if copies > 0 else max(3, -(-2 * 256 * 2 ** 20 // pool_bytes))
         self.caches = [Cache(c.fmt, c.head_dim, c.num_kv_heads, w.num_blocks) for _ in range(self.copies)]

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64) void tq4_debug_dequant_kernel(const uint8_t *po
                                                                 const int32_t *ids, const DeviceTables *tables,
                                                                 float *k_out, float *v_out) {
   constexpr int G = D / 32, KS = D / 32;
-  constexpr int REC = 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * G;
+  constexpr int REC = TqRec<D, VB>::BYTES;
   __shared__ uint32_t s_lut[256];
   __shared__ __attribute__((aligned(16))) uint32_t s_vm[64];
   const int lane = threadIdx.x;
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64) void tq4_debug_dequant_kernel(const uint8_t *po
   // keys: lane l holds token l % 16, channels (D / 4) (l / 16) + 8 s + (0..7)
   // in word s
   const int kt = lane & 15;
-  const float s = (float)h_from(reinterpret_cast<const uint16_t *>(rec + 16 * (D / 2))[kt]);
+  const float s = (float)h_from(reinterpret_cast<const uint16_t *>(rec + TqRec<D, VB>::KS)[kt]);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint4 e = key_entries(s_lut, word(bk.kq, ks));
@@ -96,14 +96,14 @@ __global__ __launch_bounds__(64) void tq4_debug_dequant_kernel(const uint8_t *po
 // applies the same exponent bytes), values through the decode's bf16 path.
 __global__ __launch_bounds__(64) void mxfp4_debug_dequant_kernel(const uint8_t *pool, int64_t num_blocks, int hkv,
                                                                   const int32_t *ids, float *k_out, float *v_out) {
-  constexpr int D = 128, G = 4, REC = 2176, OFF_KS = 1024, OFF_VC = 1088, OFF_VS = 2112;
+  constexpr int D = 128, G = 4, REC = MxRec::BYTES, OFF_KS = MxRec::KS, OFF_VC = MxRec::VC, OFF_VS = MxRec::VS;
   const int lane = threadIdx.x;
   const int64_t i = blockIdx.x / hkv;
   const int h = blockIdx.x % hkv;
   const int64_t id = ids[i];
   const bool ok = id >= 0 && id < num_blocks;
   const uint8_t *rec = pool + ((ok ? id : 0) * hkv + h) * REC;
-  const uint4 kq = *reinterpret_cast<const uint4 *>(rec + lane * 16);
+  const uint4 kq = *reinterpret_cast<const uint4 *>(rec + MxRec::KC + lane * 16);
   const uint32_t kx = rec[OFF_KS + lane];  // (token lane % 16, group lane / 16)
   const uint4 vq = *reinterpret_cast<const uint4 *>(rec + OFF_VC + lane * 16);
   const int r = lane >> 4, c = lane & 15, kt = lane & 15;

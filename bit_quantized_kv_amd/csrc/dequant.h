@@ -25,6 +25,7 @@
 #pragma once
 
 #include "tq_device.h"
+#include "tq_internal.h"
 
 namespace tq {
 
@@ -89,11 +90,11 @@ struct Blk {
 
 template <int D, int VB>
 __device__ __forceinline__ void load_blk(Blk<D, VB> &o, const uint8_t *rec, int lane) {
-  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
+  constexpr int G = D / 32, Q = D / 8;
   constexpr int VW = VB == 4 ? G : G / 2;  // value-code words per lane
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + 64 * 4 * VW;
+  constexpr int OFF_KS = TqRec<D, VB>::KS, OFF_VC = TqRec<D, VB>::VC, OFF_VM = TqRec<D, VB>::VM;
   const int r = lane >> 4, c = lane & 15;
-  o.kq = *reinterpret_cast<const typename KTile<D>::T *>(rec + lane * Q);
+  o.kq = *reinterpret_cast<const typename KTile<D>::T *>(rec + TqRec<D, VB>::KC + lane * Q);
   o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
   o.vq = *reinterpret_cast<const typename VTile<D, VB>::T *>(rec + OFF_VC + lane * (4 * VW));
   o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];

@@ -25,8 +25,8 @@
 namespace tq {
 namespace {
 
-constexpr int kD = 128, kG = 4, kRec = 2176;
-constexpr int kOffKs = 1024, kOffVc = 1088, kOffVs = 2112;
+constexpr int kD = 128, kG = 4, kRec = MxRec::BYTES;
+constexpr int kOffKc = MxRec::KC, kOffKs = MxRec::KS, kOffVc = MxRec::VC, kOffVs = MxRec::VS;
 
 // ---- quantize -----------------------------------------------------------------
 
@@ -101,7 +101,7 @@ __device__ __forceinline__ void mx_quantize_row(const QuantizeArgs &a, const Row
   const int t = slot & 15;
   uint8_t *rec = a.pool + ((int64_t)blk * a.hkv + h) * kRec;
   const int p0 = 8 * li;
-  *reinterpret_cast<uint2 *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = kc;
+  *reinterpret_cast<uint2 *>(rec + kOffKc + ((p0 / Q) * 16 + t) * Q + p0 % Q) = kc;
   const int r = t >> 2, gp = li >> 1, j0 = 8 * (li & 1);
   if ((li & 1) == 0) rec[kOffKs + gp * 16 + t] = (uint8_t)(kx + 127);
   if (aligned) {
@@ -163,7 +163,7 @@ struct Blk4 {
 
 __device__ __forceinline__ void load_blk4(Blk4 &o, const uint8_t *rec, int lane) {
   const int r = lane >> 4, c = lane & 15;
-  o.kq = *reinterpret_cast<const uint4 *>(rec + lane * 16);
+  o.kq = *reinterpret_cast<const uint4 *>(rec + kOffKc + lane * 16);
   o.ksb = rec[kOffKs + lane];
   o.vq = *reinterpret_cast<const uint4 *>(rec + kOffVc + lane * 16);
   o.vsw = reinterpret_cast<const uint32_t *>(rec + kOffVs)[4 * r + (c & 3)];

@@ -165,7 +165,7 @@ template <int D, int GQ, bool CASCADE, int VB = 4>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void tq4_decode_kernel(
     DecodeArgs a) {
   constexpr int G = D / 32, KS = D / 32;
-  constexpr int REC = 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * G;
+  constexpr int REC = TqRec<D, VB>::BYTES;
   constexpr int NW = kWaves;
   constexpr int SL = decode_slots<GQ>();  // block slots per logit tile
   constexpr int CW = 2 * GQ;              // columns per slot

@@ -76,7 +76,7 @@ struct MtVTile<64, 2> {
 // Record bytes of one (block, kv-head).
 template <int D, int VB>
 constexpr int mt_rec_bytes() {
-  return 16 * (D / 2) + 32 + (VB == 4 ? 16 * (D / 2) : 16 * (D / 4)) + 64 * (D / 32);
+  return TqRec<D, VB>::BYTES;
 }
 
 template <int D, int VB>
@@ -89,11 +89,11 @@ struct MtBlk {
 
 template <int D, int VB>
 __device__ __forceinline__ void mt_load_blk(MtBlk<D, VB> &o, const uint8_t *rec, int lane) {
-  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
+  constexpr int G = D / 32, Q = D / 8;
   constexpr int VW = VB == 4 ? G : G / 2;  // value-code words per lane
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + 64 * 4 * VW;
+  constexpr int OFF_KS = TqRec<D, VB>::KS, OFF_VC = TqRec<D, VB>::VC, OFF_VM = TqRec<D, VB>::VM;
   const int r = lane >> 4, c = lane & 15;
-  o.kq = *reinterpret_cast<const typename MtTile<D>::T *>(rec + lane * Q);
+  o.kq = *reinterpret_cast<const typename MtTile<D>::T *>(rec + TqRec<D, VB>::KC + lane * Q);
   o.ks = *reinterpret_cast<const uint2 *>(rec + OFF_KS + 8 * r);
   o.vq = *reinterpret_cast<const typename MtVTile<D, VB>::T *>(rec + OFF_VC + lane * (4 * VW));
   o.vmw = reinterpret_cast<const uint32_t *>(rec + OFF_VM)[r * (4 * G) + (c & (4 * G - 1))];

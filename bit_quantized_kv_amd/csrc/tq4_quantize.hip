@@ -55,9 +55,9 @@ template <int D, int VB>
 __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoad<D> &cur, int h, int lane,
                                              int li, int tq, const float2 *s_bins,
                                              const float *s_recip, float bin_a, float bin_b, float sigma) {
-  constexpr int G = D / 32, Q = D / 8, P16 = 16 * (D / 2);
-  constexpr int OFF_KS = P16, OFF_VC = OFF_KS + 32, OFF_VM = OFF_VC + (VB == 4 ? P16 : P16 / 2);
-  constexpr int REC = OFF_VM + 64 * G;
+  constexpr int G = D / 32, Q = D / 8;
+  constexpr int OFF_KC = TqRec<D, VB>::KC, OFF_KS = TqRec<D, VB>::KS, OFF_VC = TqRec<D, VB>::VC;
+  constexpr int OFF_VM = TqRec<D, VB>::VM, REC = TqRec<D, VB>::BYTES;
   constexpr float LEVELS = VB == 4 ? 15.f : 3.f;
   const int slot = cur.valid ? cur.slot : -1;
   // ---- key scale: fp32 sum of squares, exact fp16 RMS -------------------------
@@ -173,7 +173,7 @@ __device__ __forceinline__ void quantize_row(const QuantizeArgs &a, const RowLoa
     uint8_t *rec = a.pool + ((int64_t)blk * a.hkv + h) * REC;
     // key codes: pairs 8*li .. 8*li+7 are contiguous in the key section
     const int p0 = 8 * li;
-    *reinterpret_cast<uint2 *>(rec + ((p0 / Q) * 16 + t) * Q + p0 % Q) = make_uint2(kc0, kc1);
+    *reinterpret_cast<uint2 *>(rec + OFF_KC + ((p0 / Q) * 16 + t) * Q + p0 % Q) = make_uint2(kc0, kc1);
     if (li == 0) *reinterpret_cast<uint16_t *>(rec + OFF_KS + 2 * t) = (uint16_t)sb;
     const int r = t >> 2, gp = li >> 1, j0 = 8 * (li & 1);
     // value-code word of pair j: 4-bit, one per group; 2-bit, one per group pair

@@ -122,10 +122,30 @@ double f16_to_f64(uint16_t h);
 // false if the table's midpoints are too close for kMaxBins bins.
 bool build_key_tables(const uint16_t table_f16[16], DeviceTables *t, BinParams *bp);
 
+// Byte offsets of the sections of one (16-token block, kv-head) record (the
+// layout tq.h states).  TQ4/4 and TQ4/2 (VB = value bits): key codes, value
+// codes, value (scale, min), key scales; at D = 128 the record is padded to
+// whole 128-byte lines, so that records and their large sections start on a
+// line and the quantize writes whole lines.
+template <int D, int VB>
+struct TqRec {
+  static constexpr int KC = 0;
+  static constexpr int VC = KC + 16 * (D / 2);
+  static constexpr int VM = VC + 16 * (D / 2) * VB / 4;
+  static constexpr int KS = VM + 16 * (D / 32) * 4;
+  static constexpr int END = KS + 32;
+  static constexpr int BYTES = D == 128 ? (END + 127) / 128 * 128 : END;
+};
+// MX-FP4 (D = 128): key codes, value codes, key exponents, value exponents
+// (2176 bytes: whole lines).
+struct MxRec {
+  static constexpr int KC = 0, VC = 1024, KS = 2048, VS = 2112, BYTES = 2176;
+};
+
 // Record sizes.
-inline size_t tq4_record_bytes(int d) { return (size_t)16 * (d / 2 + 2 + d / 2 + (d / 32) * 4); }
-inline size_t tq4v2_record_bytes(int d) { return (size_t)16 * (d / 2 + 2 + d / 4 + (d / 32) * 4); }
-inline size_t mxfp4_record_bytes(int d) { return (size_t)16 * (d / 2 + d / 32 + d / 2 + d / 32); }
+inline size_t tq4_record_bytes(int d) { return d == 128 ? TqRec<128, 4>::BYTES : TqRec<64, 4>::BYTES; }
+inline size_t tq4v2_record_bytes(int d) { return d == 128 ? TqRec<128, 2>::BYTES : TqRec<64, 2>::BYTES; }
+inline size_t mxfp4_record_bytes(int) { return MxRec::BYTES; }
 
 // Split-K plan shared by the workspace query and the launch.
 struct SplitPlan {

@@ -26,6 +26,10 @@
  * of a block, t = 4r + tt.  A pool is [num_blocks][num_kv_heads][record];
  * a record holds one 16-token block of one kv-head.  A byte holds two 4-bit
  * codes: the even channel in the low nibble.  fp16 values are little-endian.
+ * Sections follow each other in the order listed; the large ones start on
+ * 128-byte boundaries of the record, and at D = 128 every record is padded
+ * to whole 128-byte lines (unused bytes, never written or read), so that a
+ * block's records are written as whole lines.
  *
  * TQ4/4 (format 0, D = 64 or 128).  Per (token, kv-head):
  *   key scale  s = fp16_RNE(sqrt(sum_i k_i^2 / D)) (exact; saturates at 65504)
@@ -38,21 +42,25 @@
  *   values     per 32-channel group: sc = fp16_sat(fp32(fp32(max - min) / 15)),
  *              mn = fp16_sat(min), code = clamp(RNE(fp32(fp32(v - mn) *
  *              fp32(1/sc))), 0, 15) (0 if sc = 0); v_hat = code * sc + mn.
- *   record (2336 B at D = 128, 1184 B at D = 64):
+ *   record (2432 B at D = 128: 2336 B of sections and 96 B of padding;
+ *   1184 B at D = 64):
  *     Kc  16*P B   pair p of token t at ((p / Q) * 16 + t) * Q + p % Q
- *     Ks  32 B     fp16 s of token t at 2t
  *     Vc  16*P B   pair p = 16*gp + j of token t at ((r*16 + j)*G + gp)*4 + tt
  *     Vm  64*G B   sc(t,gp) at 2*((r*G + gp)*8 + tt),
  *                  mn(t,gp) at 2*((r*G + gp)*8 + 4 + tt)
+ *     Ks  32 B     fp16 s of token t at 2t
  *
  * TQ4/2 (format 2, D = 64 or 128; [TQ-AMD] section 2 names 2-bit variants as
  * feasible): keys as TQ4/4; values by the same per-group rule with 2-bit codes:
  *   sc = fp16_sat(fp32(fp32(max - min) / 3)), code = clamp(RNE(fp32(fp32(v -
  *   mn) * fp32(1/sc))), 0, 3); v_hat = code * sc + mn.
- *   record (1824 B at D = 128, 928 B at D = 64): Kc, Ks as TQ4/4, then
+ *   record (1920 B at D = 128: 1824 B of sections and 96 B of padding;
+ *   928 B at D = 64):
+ *     Kc  16*P B   as TQ4/4
  *     Vc2 8*P B    channel 2p + par, p = 16*gp + j, of token t: byte
  *                  ((r*16 + j)*(G/2) + gp/2)*4 + tt, bits 4*(gp%2) + 2*par
  *     Vm  64*G B   as TQ4/4
+ *     Ks  32 B     as TQ4/4
  *   Supported by every call: quantize-append, decode, multi-token and cascade
  *   attention.
  *
@@ -63,10 +71,10 @@
  *   the byte X + 127; element code = e2m1_RNE(value / 2^X) saturating at +-6,
  *   sign bit = the value's sign bit.  Queries: rotated the same way, cast to
  *   FP8 e4m3 (OCP e4m3fn, RNE, saturating), unit scale.
- *   record (2176 B):
+ *   record (2176 B, whole 128-byte lines):
  *     Kc4 1024 B   e2m1 key codes, placed as Kc
- *     Ks4 64 B     key exponent byte of (t, gp) at gp*16 + t
  *     Vc4 1024 B   e2m1 value codes, placed as Vc
+ *     Ks4 64 B     key exponent byte of (t, gp) at gp*16 + t
  *     Vs4 64 B     value exponent byte of (t, gp) at (r*G + gp)*4 + tt
  *
  * Paging: token n of a quantize call goes to slot s = slot_mapping[n], block
@@ -113,7 +121,8 @@ typedef struct tq_cache_desc {
 
 typedef struct tq_cache tq_cache;  /* opaque handle */
 
-/* Bytes of one (block, kv-head) record (2336 / 1184 / 2176, see above). */
+/* Bytes of one (block, kv-head) record, padding included (TQ4/4: 2432 at
+ * D = 128, 1184 at D = 64; TQ4/2: 1920 / 928; MX-FP4: 2176; see above). */
 tq_status tq_record_bytes(const tq_cache_desc *desc, size_t *bytes);
 
 /* Bytes of the whole pool: num_blocks * num_kv_heads * record bytes. */

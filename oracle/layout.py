@@ -15,26 +15,32 @@ token row t in [0, 16), t = 4r + tt.
 
 TQ4/4 record (D = 64 or 128), sections in this order:
   Kc  16*P bytes  key codes:     pair p of token t at  ((p // Q) * 16 + t) * Q + p % Q
-  Ks  16*2 bytes  key scales:    fp16 s_t at byte 2t
   Vc  16*P bytes  value codes:   pair p = 16*gp + j of token t at ((r*16 + j)*G + gp)*4 + tt
   Vm  16*G*4 B    value scale/min:
                    sc(t, gp) at 2*((r*G + gp)*8 + tt),  mn(t, gp) at 2*((r*G + gp)*8 + 4 + tt)
-  Record bytes: 2336 (D=128), 1184 (D=64)  = 16 * (D/2 + 2 + D/2 + G*4).
+  Ks  16*2 bytes  key scales:    fp16 s_t at byte 2t
+  Payload 16 * (D/2 + D/2 + G*4 + 2) bytes: 2336 (D=128), 1184 (D=64).  At
+  D = 128 the record is padded with unused bytes to whole 128-byte lines: 2432.
 
 TQ4/2 record (D = 64 or 128; 2-bit values), sections in this order:
   Kc  16*P bytes  as TQ4/4
-  Ks  16*2 bytes  as TQ4/4
   Vc2 16*P/2 B    2-bit value codes: channel 2p + par, p = 16*gp + j, of token
                   t in byte ((r*16 + j)*(G/2) + gp//2)*4 + tt at bit 4*(gp%2) + 2*par
   Vm  16*G*4 B    as TQ4/4
-  Record bytes: 1824 (D=128), 928 (D=64)  = 16 * (D/2 + 2 + D/4 + G*4).
+  Ks  16*2 bytes  as TQ4/4
+  Payload 16 * (D/2 + D/4 + G*4 + 2) bytes: 1824 (D=128), 928 (D=64); padded
+  to 1920 at D = 128.
 
 MX-FP4 record (D = 128 only), sections in this order:
   Kc4 16*P bytes  e2m1 key codes (rotated keys), same placement as Kc
-  Ks4 16*G bytes  UE8M0 key exponents: group gp of token t at gp*16 + t
   Vc4 16*P bytes  e2m1 value codes, same placement as Vc
+  Ks4 16*G bytes  UE8M0 key exponents: group gp of token t at gp*16 + t
   Vs4 16*G bytes  UE8M0 value exponents: group gp of token t at (r*G + gp)*4 + tt
-  Record bytes: 2176 (D=128) = 16 * (D/2 + G + D/2 + G).
+  Record bytes: 2176 (D=128) = 16 * (D/2 + D/2 + G + G), whole 128-byte lines.
+
+The large sections start on 128-byte boundaries of a record, and at D = 128
+the records themselves do (an implementation choice of this format: writes of
+whole lines).
 
 Pinned by tests/test_oracle_layout.py: hand-written byte examples, every
 section offset map is a bijection onto its section, nibble pack/unpack over all
@@ -45,20 +51,21 @@ import numpy as np
 BLOCK = 16
 
 
+def _lines(n):
+    """n rounded up to whole 128-byte lines."""
+    return (n + 127) // 128 * 128
+
+
 def tq4_record_bytes(d):
-    _check_dim(d)
-    return BLOCK * (d // 2 + 2 + d // 2 + (d // 32) * 4)
+    return tq4_sections(d)["bytes"]
 
 
 def tq4v2_record_bytes(d):
-    _check_dim(d)
-    return BLOCK * (d // 2 + 2 + d // 4 + (d // 32) * 4)
+    return tq4v2_sections(d)["bytes"]
 
 
 def mxfp4_record_bytes(d):
-    if d != 128:
-        raise ValueError("the MX-FP4 record is defined for head_dim 128")
-    return BLOCK * (d // 2 + d // 32 + d // 2 + d // 32)
+    return mxfp4_sections(d)["bytes"]
 
 
 def _check_dim(d):
@@ -117,33 +124,41 @@ def vs4_offset(t, gp, d):
 
 
 def tq4_sections(d):
-    """Start byte of each section of a TQ4 record."""
+    """Start byte of each section of a TQ4 record; "end": end of the payload,
+    "bytes": the record size (D = 128: whole 128-byte lines)."""
+    _check_dim(d)
     p16 = BLOCK * (d // 2)
     kc = 0
-    ks = kc + p16
-    vc = ks + 2 * BLOCK
+    vc = kc + p16
     vm = vc + p16
-    return {"kc": kc, "ks": ks, "vc": vc, "vm": vm, "end": vm + BLOCK * (d // 32) * 4}
+    ks = vm + BLOCK * (d // 32) * 4
+    end = ks + 2 * BLOCK
+    return {"kc": kc, "vc": vc, "vm": vm, "ks": ks, "end": end, "bytes": _lines(end) if d == 128 else end}
 
 
 def tq4v2_sections(d):
-    """Start byte of each section of a TQ4/2 record."""
+    """Start byte of each section of a TQ4/2 record (keys as in TQ4/4)."""
+    _check_dim(d)
     p16 = BLOCK * (d // 2)
     kc = 0
-    ks = kc + p16
-    vc = ks + 2 * BLOCK
+    vc = kc + p16
     vm = vc + p16 // 2
-    return {"kc": kc, "ks": ks, "vc": vc, "vm": vm, "end": vm + BLOCK * (d // 32) * 4}
+    ks = vm + BLOCK * (d // 32) * 4
+    end = ks + 2 * BLOCK
+    return {"kc": kc, "vc": vc, "vm": vm, "ks": ks, "end": end, "bytes": _lines(end) if d == 128 else end}
 
 
 def mxfp4_sections(d):
+    if d != 128:
+        raise ValueError("the MX-FP4 record is defined for head_dim 128")
     p16 = BLOCK * (d // 2)
     g16 = BLOCK * (d // 32)
     kc = 0
-    ks = kc + p16
-    vc = ks + g16
-    vs = vc + p16
-    return {"kc": kc, "ks": ks, "vc": vc, "vs": vs, "end": vs + g16}
+    vc = kc + p16
+    ks = vc + p16
+    vs = ks + g16
+    end = vs + g16
+    return {"kc": kc, "vc": vc, "ks": ks, "vs": vs, "end": end, "bytes": end}
 
 
 # --- nibbles -----------------------------------------------------------------

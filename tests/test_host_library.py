@@ -40,10 +40,12 @@ def test_library_exports_every_declared_entry_point():
 def test_record_and_pool_sizes():
     _ensure_built()
     import bit_quantized_kv_amd as T
-    assert T.tq_record_bytes(T.TQ_FORMAT_TQ4, 128) == 2336
+    assert T.tq_record_bytes(T.TQ_FORMAT_TQ4, 128) == 2432
     assert T.tq_record_bytes(T.TQ_FORMAT_TQ4, 64) == 1184
+    assert T.tq_record_bytes(T.TQ_FORMAT_TQ4V2, 128) == 1920
+    assert T.tq_record_bytes(T.TQ_FORMAT_TQ4V2, 64) == 928
     assert T.tq_record_bytes(T.TQ_FORMAT_MXFP4, 128) == 2176
-    assert T.tq_pool_bytes(T.TQ_FORMAT_TQ4, 128, 8, 2048) == 2336 * 8 * 2048
+    assert T.tq_pool_bytes(T.TQ_FORMAT_TQ4, 128, 8, 2048) == 2432 * 8 * 2048
 
 
 def test_default_key_table_matches_oracle():

@@ -26,8 +26,23 @@ def test_record_sizes():
     assert layout.tq4_record_bytes(64) == rb["tq4_64"]
     assert layout.tq4_record_bytes(128) == rb["tq4_128"]
     assert layout.mxfp4_record_bytes(128) == rb["mxfp4_128"]
-    assert layout.tq4_sections(128)["end"] == rb["tq4_128"]
-    assert layout.mxfp4_sections(128)["end"] == rb["mxfp4_128"]
+    assert layout.tq4_sections(128)["bytes"] == rb["tq4_128"]
+    assert layout.mxfp4_sections(128)["bytes"] == rb["mxfp4_128"]
+
+
+def test_hand_sections():
+    sec = G["sections"]
+    assert layout.tq4_sections(128) == sec["tq4_128"]
+    assert layout.tq4_sections(64) == sec["tq4_64"]
+    assert layout.tq4v2_sections(128) == sec["tq4v2_128"]
+    assert layout.tq4v2_sections(64) == sec["tq4v2_64"]
+    assert layout.mxfp4_sections(128) == sec["mxfp4_128"]
+    # the large sections start on 128-byte lines; D = 128 records are whole lines
+    for d in (64, 128):
+        for s in (layout.tq4_sections(d), layout.tq4v2_sections(d)):
+            assert s["vc"] % 128 == 0 and s["vm"] % 128 == 0
+    for s in (layout.tq4_sections(128), layout.tq4v2_sections(128), layout.mxfp4_sections(128)):
+        assert s["bytes"] % 128 == 0
 
 
 def test_hand_offsets():
@@ -100,9 +115,9 @@ def test_mxfp4_write_read_round_trip():
 
 
 def test_tq4v2_sizes_and_hand_positions():
-    assert layout.tq4v2_record_bytes(128) == 1824 and layout.tq4v2_record_bytes(64) == 928
+    assert layout.tq4v2_record_bytes(128) == 1920 and layout.tq4v2_record_bytes(64) == 928
     sec = layout.tq4v2_sections(128)
-    assert (sec["kc"], sec["ks"], sec["vc"], sec["vm"], sec["end"]) == (0, 1024, 1056, 1568, 1824)
+    assert (sec["kc"], sec["vc"], sec["vm"], sec["ks"], sec["end"]) == (0, 1024, 1536, 1792, 1824)
     # worked by hand (D = 128, G = 4): channel 0 of token 0 -> byte 0, bit 0;
     # channel 1 -> bit 2; channel 64 (pair 32: gp 2, j 0) -> word 1 -> byte 4;
     # token 5 (r 1, tt 1), channel 35 (pair 17: gp 1, j 1, odd) -> byte
