@@ -146,12 +146,12 @@ def test_both_quantize_loops(_loop_env, loop, fmt, d, hkv, seed):
 
 
 @pytest.mark.parametrize("loop,fmt,d,hkv,seed", [("balanced", 0, 128, 2, 145), ("balanced-pairs", 0, 128, 2, 146),
-                                                 ("balanced-pairs", 2, 64, 4, 147)])
+                                                 ("balanced-pairs", 2, 64, 4, 147), ("balanced-pairs", 1, 128, 2, 148)])
 def test_balanced_loop_hands_out_from_the_counter(_loop_env, loop, fmt, d, hkv, seed):
     """A launch long enough that every work-group of the balanced loop takes
     several times the 16 (one by one) or 32 (pairs) tasks its waves start
     with, so that tasks and pairs of tasks come from the LDS counter; the
-    records match the oracle's byte for byte."""
+    records match the oracle's byte for byte (TQ4/4, TQ4/2 and MX-FP4)."""
     os.environ["TQ_QUANT_LOOP"] = loop
     cfg = workloads.small_config(batch=8, num_q_heads=4 * hkv, num_kv_heads=hkv, head_dim=d, ctx_range=(12000, 16000),
                                  seed=seed, fmt=fmt)
