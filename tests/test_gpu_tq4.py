@@ -256,6 +256,35 @@ def test_balanced_loop_listing_rounds(_loop_env, d, window, seed):
     assert bad.size == 0, f"{bad.size} blocks differ from the oracle's, first {bad[:4]}"
 
 
+@pytest.mark.parametrize("fmt,d,hkv,n,seed", [(0, 128, 1, 1, 171), (0, 64, 8, 5, 172), (2, 128, 8, 300, 173),
+                                               (1, 128, 3, 77, 174)])
+def test_balanced_loop_short_launches(_loop_env, fmt, d, hkv, n, seed):
+    """The balanced loop forced on launches shorter than its grid: most
+    work-groups get an empty token range, the others one or a few items;
+    slots are scattered (every row its own item) with skips.  The records
+    match the oracle's byte for byte."""
+    from bit_quantized_kv_amd import Cache
+    from gpu_common import to_dev_bf16, to_dev_i32
+    from oracle import paged
+    os.environ["TQ_QUANT_LOOP"] = "balanced"
+    rng = np.random.default_rng(seed)
+    num_blocks = 64
+    slots = rng.permutation(num_blocks * 16)[:n].astype(np.int32)
+    if n > 2:
+        slots[rng.choice(n, max(1, n // 10), replace=False)] = -1
+    kf = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    vf = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    kb, vb = workloads.f32_to_bf16_bits(kf), workloads.f32_to_bf16_bits(vf)
+    say(f"case: balanced loop, short launch of {n} tokens, format {fmt}, d={d}, hkv={hkv}, seed {seed}")
+    cache = Cache(fmt, d, hkv, num_blocks)
+    cache.quantize_append(to_dev_bf16(kb), to_dev_bf16(vb), to_dev_i32(slots))
+    torch.cuda.synchronize()
+    gpu = cache.pool.cpu().numpy().reshape(num_blocks, hkv, -1)
+    op = paged.PagedPool(fmt, num_blocks, hkv, d)
+    op.append(workloads.bf16_bits_to_f32(kb), workloads.bf16_bits_to_f32(vb), slots)
+    assert np.array_equal(gpu, op.pool)
+
+
 def test_pool_beyond_4_gib():
     """A 4.7 GB pool (10^6 blocks x 2 kv-heads x 2336 B): records past byte
     2^32 are written and read through 64-bit offsets.  One sequence lives on
