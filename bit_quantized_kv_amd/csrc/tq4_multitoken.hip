@@ -14,17 +14,20 @@
 //     (sequence, kv-head) and one split of the key blocks, which are
 //     dequantized once per work-group and shared through LDS.  Stage k: wave w
 //     loads block 8k + w of the split (a ring of four blocks of 128-bit loads
-//     in flight per wave), dequantizes it into the work-group's stage buffer
-//     (keys: the fp16 table entries in the QK A-operand order; values: code *
-//     scale + min in fp16 in the PV A-operand order; key scales), and after
-//     one barrier every wave runs its rows against its pairs of blocks of the
-//     stage.  Two stage buffers alternate, so one barrier per stage suffices.
+//     in flight per wave), unpacks it into the work-group's stage buffer
+//     (keys: the fp16 table entries in the QK A-operand order; values: the
+//     codes as exact fp16 integers in the PV A-operand order and the block's
+//     (scale, min) tile; key scales), and after one barrier every wave runs
+//     its rows against its pairs of blocks of the stage.  Two stage buffers
+//     alternate, so one barrier per stage suffices.
 // Per pair of blocks and 16-row tile: logits = K_hat (16 tokens x D) times the
 // rotated query rows (D x 16 rows) on v_mfma_f32_16x16x32_f16, the query split
 // into fp16 high and low parts (two MFMAs into one accumulator); the key
 // scale; the causal mask; online softmax in log2 units with lazy rescale;
 // out^T (channels x rows) += V_hat^T P over the pair's 32 tokens on
-// v_mfma_f32_16x16x32_f16, P rounded once to fp16.
+// v_mfma_f32_16x16x32_f16: code * scale as two exact fp16 parts (one MFMA
+// each) and the minima through a separate product with P, so V_hat enters
+// exactly; P is rounded once to fp16.
 // With one split the rows are written directly; otherwise split partials
 // (max, sum, acc) go to the workspace and a merge kernel combines them per row.
 #include "decode_common.h"
