@@ -45,10 +45,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="agentic",
                    choices=["llama8b", "agentic", "longprefix", "fp4", "tq4v2", "calib", "verify", "prefill",
+                            "verify_fp4", "prefill_fp4", "agentic_fp4", "cascade_fp4",
                             "cascade"],
                    help="calib: the calibrated key-table fit of a 32-layer stack; verify / prefill: multi-token "
                         "attention over the cache; cascade: the agentic workload decoded with shared blocks "
-                        "read once per group; tq4v2: the llama8b shape with 2-bit values (each its own JSON line)")
+                        "read once per group; tq4v2: the llama8b shape with 2-bit values; *_fp4: the same workload over an "
+                        "MX-FP4 cache (each its own JSON line)")
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
     p.add_argument("--cascade-group-blocks", type=int, default=48,
                    help="cascade: shared ranges are cut into groups of at most this many blocks")
@@ -668,18 +670,20 @@ def bench_multitoken(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 codes; f16 MFMA, f32 softmax",
+        "dtype": ("e2m1 codes; fp8 x fp4 scaled MFMA (QK), bf16 MFMA (PV), f32 softmax" if c.fmt == 1
+                  else "u4 codes; f16 MFMA, f32 softmax"),
         "data": "synthetic (seeded; shapes of the pages' agentic workloads)",
         "config": {"workload": f"{c.name}: batch {c.batch}, {mb.m} query tokens per sequence, "
                                f"{c.num_q_heads}/{c.num_kv_heads} heads, head_dim {c.head_dim}, "
-                               f"context up to {mb.max_ctx}",
+                               f"context up to {mb.max_ctx}, format {['TQ4/4', 'MX-FP4', 'TQ4/2'][c.fmt]}",
                    "pool_copies": mb.copies},
         "attention_us": round(a_ms * 1e3, 2),
         "append_us": round(q_ms * 1e3, 2),
         "effective_kv_GBps": round(kv / (a_ms * 1e-3) / 1e9, 1),
         # the attention kernel's matrix-unit use (committed counters)
         "attention_mfma_busy": (mfma_busy_from_profiles(args.config, "tq::tq4_mt_direct_kernel")
-                                or mfma_busy_from_profiles(args.config, "tq::tq4_multitoken_kernel")),
+                                or mfma_busy_from_profiles(args.config, "tq::tq4_multitoken_kernel")
+                                or mfma_busy_from_profiles(args.config, "tq::mxfp4_mt_kernel")),
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -743,15 +747,18 @@ def main():
     if args.config == "calib":
         bench_calib(args)
         return
-    if args.config in ("verify", "prefill"):
+    if args.config in ("verify", "prefill", "verify_fp4", "prefill_fp4"):
         bench_multitoken(args)
         return
     import workloads
-    cascade = args.config == "cascade"
+    cascade = args.config in ("cascade", "cascade_fp4")
     cfg_name = "agentic" if cascade else args.config
+    import dataclasses
     if args.config == "tq4v2":
-        import dataclasses
         cfg = dataclasses.replace(workloads.CONFIGS["llama8b"], name="tq4v2", fmt=2)
+    elif args.config in ("agentic_fp4", "cascade_fp4"):
+        # the agentic workload over an MX-FP4 cache
+        cfg = dataclasses.replace(workloads.CONFIGS["agentic"], name="agentic_fp4", fmt=1)
     else:
         cfg = workloads.CONFIGS[cfg_name]
     # the CPU oracle first: its worker processes are forked before any GPU use
@@ -807,7 +814,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 codes; f16 MFMA, f32 softmax",
+        "dtype": ("e2m1 codes; fp8 x fp4 scaled MFMA (QK), bf16 MFMA (PV), f32 softmax" if c.fmt == 1
+                  else "u4 codes; f16 MFMA, f32 softmax"),
         "data": "synthetic (seeded; shapes of the pages' agentic workloads)",
         "config": {"workload": f"{c.name}: batch {c.batch}, {c.num_q_heads}/{c.num_kv_heads} heads, "
                                f"head_dim {c.head_dim}, context {int(bench.w.context_lens_at(0).max())}, "

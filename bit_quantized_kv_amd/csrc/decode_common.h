@@ -102,6 +102,29 @@ __device__ __forceinline__ WgTask decode_task(const DecodeArgs &a) {
   return t;
 }
 
+// A running maximum that starts finite, so that a column whose tokens are all
+// masked so far gets p = 2^(-inf - m) = 0 rather than 2^(-inf + inf).
+constexpr float kMtFloor = -1.0e30f;
+
+// Multi-token work-group -> (sequence or group, kv-head, row tile, split).
+struct MtTask {
+  int b, kvh, rt, sp;
+};
+
+__device__ __forceinline__ MtTask mt_task(const MultiTokenArgs &a) {
+  // row tiles fastest, then splits, sequences, kv-heads; each XCD gets a
+  // contiguous range, so the work-groups that read the same blocks share an L2
+  const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
+  MtTask t;
+  t.rt = (int)(wg % (uint32_t)a.row_tiles);
+  uint32_t rest = wg / (uint32_t)a.row_tiles;
+  t.sp = (int)(rest % (uint32_t)a.nsplit);
+  rest /= (uint32_t)a.nsplit;
+  t.b = (int)(rest % (uint32_t)a.batch);
+  t.kvh = (int)(rest / (uint32_t)a.batch);
+  return t;
+}
+
 // Per-wave online-softmax state for the 16 operand columns.  Column n < g is
 // query head n (high fp16 part), g <= n < 2g the same head's low part.
 template <int G2>  // number of PV accumulator tiles (2 * D / 32)

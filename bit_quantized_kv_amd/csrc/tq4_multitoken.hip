@@ -40,9 +40,6 @@ constexpr int kMtWaves = 8;
 // block ids of one split staged in LDS: split_blocks <= kMtMaxIds
 constexpr int kMtMaxIds = 4096;
 constexpr int kDirMaxIds = 1024;
-// A running maximum that starts finite, so that a column whose tokens are all
-// masked so far gets p = 2^(-inf - m) = 0 rather than 2^(-inf + inf).
-constexpr float kMtFloor = -1.0e30f;
 
 template <int D>
 struct MtTile;
@@ -117,24 +114,6 @@ struct MtPair {
   uint2 ks[2][4];          // fp16 key scales of tokens 4r .. 4r+3 of block h
   uint32_t big[2];         // block h holds a value scale >= 4096
 };
-
-struct MtTask {
-  int b, kvh, rt, sp;
-};
-
-__device__ __forceinline__ MtTask mt_task(const MultiTokenArgs &a) {
-  // row tiles fastest, then splits, sequences, kv-heads; each XCD gets a
-  // contiguous range, so the work-groups that read the same blocks share an L2
-  const uint32_t wg = xcd_logical_id(blockIdx.x, gridDim.x);
-  MtTask t;
-  t.rt = (int)(wg % (uint32_t)a.row_tiles);
-  uint32_t rest = wg / (uint32_t)a.row_tiles;
-  t.sp = (int)(rest % (uint32_t)a.nsplit);
-  rest /= (uint32_t)a.nsplit;
-  t.b = (int)(rest % (uint32_t)a.batch);
-  t.kvh = (int)(rest / (uint32_t)a.batch);
-  return t;
-}
 
 // Producer: this wave's loaded block into half `half` of its LDS pair: key
 // table entries, value codes as exact fp16, the (scale, min) tile (the scales
@@ -1136,6 +1115,13 @@ __global__ __launch_bounds__(256) void multitoken_merge_kernel(MultiTokenArgs a)
   }
 }
 
+template <int D>
+hipError_t launch_merge(const MultiTokenArgs &a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.max_query_len * a.hq;
+  hipLaunchKernelGGL(multitoken_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int VB>
 hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.hkv * a.row_tiles * a.nsplit;
@@ -1150,9 +1136,7 @@ hipError_t launch_mt(const MultiTokenArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  const int64_t rows = (int64_t)a.batch * a.max_query_len * a.hq;
-  hipLaunchKernelGGL(multitoken_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_merge<D>(a, s);
 }
 
 template <int D, int VB>
@@ -1179,6 +1163,12 @@ hipError_t launch_tq4_multitoken(int d, int vbits, const MultiTokenArgs &a, hipS
 hipError_t launch_prefix_attention(int d, int vbits, const MultiTokenArgs &a, hipStream_t s) {
   if (vbits == 2) return d == 128 ? launch_prefix<128, 2>(a, s) : launch_prefix<64, 2>(a, s);
   return d == 128 ? launch_prefix<128, 4>(a, s) : launch_prefix<64, 4>(a, s);
+}
+
+// The split merge of multi-token attention (any format: the partials have one
+// layout).
+hipError_t launch_multitoken_merge(int d, const MultiTokenArgs &a, hipStream_t s) {
+  return d == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
 }
 
 }  // namespace tq

@@ -327,8 +327,7 @@ struct MtPlan {
 tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads, int64_t num_tokens,
                           int32_t max_query_len, int32_t max_context_len, MtPlan *p) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
-  if (cache->desc.format == TQ_FORMAT_MXFP4)
-    return fail(TQ_ERR_UNSUPPORTED, "multi-token attention is built for the TQ4/4 and TQ4/2 formats");
+  const bool mx = cache->desc.format == TQ_FORMAT_MXFP4;
   const int hkv = cache->desc.num_kv_heads;
   if (batch < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0)
     return fail(TQ_ERR_INVALID_ARG, "batch, num_tokens, max_query_len and max_context_len must be >= 0");
@@ -343,17 +342,19 @@ tq_status multitoken_plan(const tq_cache *cache, int32_t batch, int32_t num_q_he
   // (every wave runs all rows against its own block pairs), up to 64 in a
   // staged work-group of 4 row groups x 2 block groups, up to 128 in 8 x 1,
   // more in tiles of 256 (8 x 1, two 16-row tiles per wave)
+  // MX-FP4: work-groups of 16 or 32 rows, more rows as more row tiles; a
+  // wave keeps at most 64 block ids (one per lane), 256 per work-group
   const int64_t rows = (int64_t)max_query_len * g;
-  const int rows_per_wg = rows <= 16 ? 16 : rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
+  const int rows_per_wg = rows <= 16 ? 16 : rows <= 32 || mx ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
   const int64_t row_tiles = (rows + rows_per_wg - 1) / rows_per_wg;
   // prefill-sized tiles (MFMA-heavy per block) walk whole contexts; smaller
   // ones split long contexts at 512 blocks so uneven lengths balance
-  const int max_split = rows_per_wg >= 256 ? 4096 : 512;
+  const int max_split = mx ? 256 : rows_per_wg >= 256 ? 4096 : 512;
   tq::SplitPlan sp = tq::plan_split_multitoken((int64_t)batch * hkv * std::max<int64_t>(1, row_tiles),
                                                max_context_len, max_split);
   // a work-group stages its split's block ids in LDS: at most 4096 (staged
   // kernel) or 1024 (direct kernel)
-  const int max_ids = rows_per_wg <= 32 ? 1024 : 4096;
+  const int max_ids = mx ? 256 : rows_per_wg <= 32 ? 1024 : 4096;
   if (sp.split_blocks > max_ids) {
     sp.split_blocks = max_ids;
     sp.nsplit = (int)std::max<int64_t>(1, (((int64_t)max_context_len + 15) / 16 + max_ids - 1) / max_ids);
@@ -416,7 +417,10 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
     a.part_acc = a.part_ml + (((size_t)num_tokens * num_q_heads * p.split.nsplit * 2 + 63) / 64) * 64;
   }
   const double log2e = 1.4426950408889634074;
-  a.qscale = (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)));
+  const bool mx = cache->desc.format == TQ_FORMAT_MXFP4;
+  // MX-FP4 queries carry 1/sqrt(d) before their e4m3 rounding
+  a.qscale = (float)((double)softmax_scale * log2e * (mx ? 1.0 : 1.0 / std::sqrt((double)d)));
+  a.rsqrt_d = (float)(1.0 / std::sqrt((double)d));
   a.max_blocks = max_blocks;
   a.batch = batch;
   a.hq = num_q_heads;
@@ -430,7 +434,9 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
   a.part_stride = p.split.nsplit;
   a.slot0 = 0;
   a.out_bf16 = out_dtype == TQ_OUT_BF16;
-  hipError_t e = tq::launch_tq4_multitoken(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, static_cast<hipStream_t>(stream));
+  hipError_t e = mx ? tq::launch_mxfp4_multitoken(a, static_cast<hipStream_t>(stream))
+                    : tq::launch_tq4_multitoken(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a,
+                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "multi-token attention launch");
   return TQ_OK;
 }
@@ -447,8 +453,7 @@ tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads
                        int32_t num_groups, int32_t max_group_size, int32_t max_group_blocks, int32_t max_depth,
                        CascadePlan *p) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
-  if (cache->desc.format == TQ_FORMAT_MXFP4)
-    return fail(TQ_ERR_UNSUPPORTED, "cascade decode is built for the TQ4/4 and TQ4/2 formats");
+  const bool mx = cache->desc.format == TQ_FORMAT_MXFP4;
   const int hkv = cache->desc.num_kv_heads;
   if (batch < 0 || max_context_len < 0 || num_groups < 0 || max_group_blocks < 0 || max_depth < 0)
     return fail(TQ_ERR_INVALID_ARG,
@@ -464,14 +469,18 @@ tq_status cascade_plan(const tq_cache *cache, int32_t batch, int32_t num_q_heads
     return fail(TQ_ERR_INVALID_ARG, "max_depth must be in [1, num_groups]");
   if ((int64_t)16 * max_group_blocks > max_context_len)
     return fail(TQ_ERR_INVALID_ARG, "16 * max_group_blocks must be <= max_context_len");
-  if (max_group_blocks > 4096)
-    return fail(TQ_ERR_UNSUPPORTED, "a group's shared range is at most 4096 blocks (cut longer ones into chained groups)");
+  if (max_group_blocks > (mx ? 256 : 4096))
+    return fail(TQ_ERR_UNSUPPORTED, mx ? "an MX-FP4 group's shared range is at most 256 blocks (cut longer ones into "
+                                         "chained groups)"
+                                       : "a group's shared range is at most 4096 blocks (cut longer ones into chained "
+                                         "groups)");
   p->own = tq::plan_split(batch, hkv, max_context_len);
   // groups of at most 32 rows take the direct kernel (every wave runs all rows
   // against its own blocks; the group's block ids, at most 1024, in LDS),
-  // larger ones the staged kernel
+  // larger ones the staged kernel; MX-FP4 groups take work-groups of 16 or 32
+  // rows (more rows: more row tiles)
   const int64_t rows = (int64_t)std::max(1, max_group_size) * g;
-  const bool direct = rows <= 32 && max_group_blocks <= 1024;
+  const bool direct = mx || (rows <= 32 && max_group_blocks <= 1024);
   p->rows_per_wg = direct ? (rows <= 16 ? 16 : 32) : rows <= 64 ? 64 : 128;
   p->row_tiles = (int)((rows + p->rows_per_wg - 1) / p->rows_per_wg);
   // one split per group: a group is the unit of parallel work (callers cut
@@ -533,7 +542,10 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
   float *part_ml = static_cast<float *>(workspace);
   float *part_acc = part_ml + (((size_t)batch * num_q_heads * p.part_stride * 2 + 63) / 64) * 64;
   const double log2e = 1.4426950408889634074;
-  const float qscale = (float)((double)softmax_scale * log2e * (1.0 / std::sqrt((double)d)));
+  const bool mx = cache->desc.format == TQ_FORMAT_MXFP4;
+  // MX-FP4 queries carry 1/sqrt(d) before their e4m3 rounding
+  const float qscale = (float)((double)softmax_scale * log2e * (mx ? 1.0 : 1.0 / std::sqrt((double)d)));
+  const float rsqrt_d = (float)(1.0 / std::sqrt((double)d));
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;
@@ -552,6 +564,7 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
     m.part_ml = part_ml;
     m.part_acc = part_acc;
     m.qscale = qscale;
+    m.rsqrt_d = rsqrt_d;
     m.max_blocks = max_blocks;
     m.batch = num_groups;
     m.hq = num_q_heads;
@@ -571,7 +584,8 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
     e = hipEventRecord(cache->fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(cache->aux, cache->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "cascade fork");
-    e = tq::launch_prefix_attention(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, m, cache->aux);
+    e = mx ? tq::launch_mxfp4_prefix_attention(m, cache->aux)
+           : tq::launch_prefix_attention(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, m, cache->aux);
     if (e != hipSuccess) return hip_fail(e, "shared-block attention launch");
     e = hipEventRecord(cache->join, cache->aux);
     if (e != hipSuccess) return hip_fail(e, "cascade join record");
@@ -586,7 +600,7 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
   a.part_ml = part_ml;
   a.part_acc = part_acc;
   a.qscale = qscale;
-  a.rsqrt_d = (float)(1.0 / std::sqrt((double)d));
+  a.rsqrt_d = rsqrt_d;
   a.max_blocks = max_blocks;
   a.batch = batch;
   a.hq = num_q_heads;
@@ -598,7 +612,8 @@ tq_status tq_cascade_decode_attention(tq_cache *cache, const void *q, void *out,
   a.first_blk = seq_prefix_blocks;
   a.depth = seq_depth;
   a.part_stride = p.part_stride;
-  e = tq::launch_tq4_cascade_decode(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, s);
+  e = mx ? tq::launch_mxfp4_cascade_decode(a, s)
+         : tq::launch_tq4_cascade_decode(d, cache->desc.format == TQ_FORMAT_TQ4 ? 4 : 2, a, s);
   if (e != hipSuccess) return hip_fail(e, "cascade decode launch");
   if (num_groups > 0) {
     e = hipStreamWaitEvent(s, cache->join, 0);

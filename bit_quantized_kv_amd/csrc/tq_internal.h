@@ -69,7 +69,8 @@ struct MultiTokenArgs {
   const DeviceTables *tables;
   float *part_ml;                // [num_tokens][hq][nsplit][2]
   float *part_acc;               // [num_tokens][hq][nsplit][d]
-  float qscale;                  // softmax_scale * log2(e) * fp32(1/sqrt(d))
+  float qscale;                  // TQ4: softmax_scale * log2(e) * fp32(1/sqrt(d)); MX-FP4: softmax_scale * log2(e)
+  float rsqrt_d;                 // fp32(1/sqrt(d)) (MX-FP4: the query's scale before e4m3)
   int32_t max_blocks, batch, hq, hkv, g;
   int32_t max_query_len;         // bound on q_start[b+1] - q_start[b]
   int32_t rows_per_wg;           // 16 or 32 (direct kernel), 64, 128 or 256 query rows per work-group
@@ -101,9 +102,13 @@ hipError_t launch_tq4_quantize(int d, int vbits, const QuantizeArgs &a, hipStrea
 hipError_t launch_tq4_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_mxfp4_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_mxfp4_cascade_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_mxfp4_multitoken(const MultiTokenArgs &a, hipStream_t s);
+hipError_t launch_mxfp4_prefix_attention(const MultiTokenArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int d, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_tq4_multitoken(int d, int vbits, const MultiTokenArgs &a, hipStream_t s);
 hipError_t launch_prefix_attention(int d, int vbits, const MultiTokenArgs &a, hipStream_t s);
+hipError_t launch_multitoken_merge(int d, const MultiTokenArgs &a, hipStream_t s);
 hipError_t launch_tq4_cascade_decode(int d, int vbits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_cascade_merge(int d, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_debug_dequant(int format, int d, const uint8_t *pool, int64_t num_blocks, int hkv,

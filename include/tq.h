@@ -210,8 +210,8 @@ tq_status tq_decode_attention_noalloc(tq_cache *cache, const void *q, void *out,
                                       float softmax_scale, void *stream);
 
 /* ---------------------------------------------------------------------------
- * Multi-token attention over the compressed cache (TQ4/4): chunked prefill of
- * new tokens, or the verification of several proposed tokens.  The time to
+ * Multi-token attention over the compressed cache (every format): chunked
+ * prefill of new tokens, or the verification of several proposed tokens.  The time to
  * first token that the pages report ([TQ-AMD] section 1; [UQ] "它實際證明了
  * 什麼") comes from prefilling over the cache; the operation is the causal
  * reading of attention over the cached context:
@@ -219,7 +219,8 @@ tq_status tq_decode_attention_noalloc(tq_cache *cache, const void *q, void *out,
  *                            <q~, k_hat_t>) v_hat_t,   i < M_b,
  * with M_b = q_start[b+1] - q_start[b] query tokens of sequence b, the last
  * M_b tokens of its context of T_b = context_lens[b] tokens (their keys and
- * values already appended), q~ = H_D q, kv-head h / g as in decode.
+ * values already appended), q~ = H_D q (MX-FP4: its e4m3 code values, as in
+ * decode), kv-head h / g as in decode.
  * q: device bf16 [num_tokens][num_q_heads][head_dim]; out: device fp32 or
  * bf16 (out_dtype) of the same shape; q_start: device int32 [batch + 1],
  * nondecreasing, q_start[0] = 0, q_start[batch] = num_tokens, each M_b in
@@ -228,8 +229,8 @@ tq_status tq_decode_attention_noalloc(tq_cache *cache, const void *q, void *out,
  * on the device).  num_q_heads a multiple of num_kv_heads (any ratio).
  * Host-checked: max_query_len <= max_context_len, num_tokens <= batch *
  * max_query_len.  workspace: device buffer of at least
- * tq_multitoken_workspace_bytes (NULL allowed when that is 0).  TQ4/4 and
- * TQ4/2 caches; MX-FP4 caches return TQ_ERR_UNSUPPORTED.  Asynchronous. */
+ * tq_multitoken_workspace_bytes (NULL allowed when that is 0).
+ * Asynchronous. */
 tq_status tq_multitoken_workspace_bytes(const tq_cache *cache, int32_t batch, int32_t num_q_heads,
                                         int64_t num_tokens, int32_t max_query_len, int32_t max_context_len,
                                         size_t *bytes);
@@ -240,7 +241,7 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
                                   float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
- * Shared-prefix (cascade) decode attention (TQ4/4).  The same result as
+ * Shared-prefix (cascade) decode attention (every format).  The same result as
  * tq_decode_attention, computed so that blocks shared by several sequences
  * are read once: the pages' agentic workloads keep long prefixes resident and
  * shared between sessions ([TQ-AMD] spec table; [UQ] "它實際證明了什麼"), and
@@ -269,11 +270,10 @@ tq_status tq_multitoken_attention(tq_cache *cache, const void *q, void *out, int
  *   group_depth        int32 [num_groups]: the group's depth (< max_depth)
  *   host: num_groups >= 0; when > 0, max_group_size in [1, batch] and
  *   max_depth in [1, num_groups]; 16 * max_group_blocks <= max_context_len;
- *   max_group_blocks <= 4096 (TQ_ERR_UNSUPPORTED beyond: cut longer shared
- *   ranges into chained groups).
+ *   max_group_blocks <= 4096, MX-FP4: <= 256 (TQ_ERR_UNSUPPORTED beyond: cut
+ *   longer shared ranges into chained groups).
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8.  workspace: device buffer
- * of at least tq_cascade_workspace_bytes (always needed).  TQ4/4 and TQ4/2
- * caches; MX-FP4 caches return TQ_ERR_UNSUPPORTED.  Asynchronous: the
+ * of at least tq_cascade_workspace_bytes (always needed).  Asynchronous: the
  * shared-block pass runs on a second stream of the handle (created on first
  * use, default priority), forked from `stream` and joined back to it by events
  * before the merge, so the call is ordered on `stream` like the others; calls

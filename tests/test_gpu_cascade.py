@@ -80,6 +80,19 @@ def test_two_bit_values(d, g, hkv, seed, split):
     _run(Case(cfg), [([0, 1, 2, 3, 4, 5], 0, 4), ([0, 2, 4], 4, 10), ([6], 0, 3)])
 
 
+@pytest.mark.parametrize("g,hkv,seed,split", [(4, 2, 321, None), (8, 1, 322, 4), (1, 2, 323, 8)])
+def test_mxfp4(g, hkv, seed, split):
+    """MX-FP4 caches with nested groups: the own-token pass on the MX-FP4
+    decode kernel, the shared blocks on its multi-token kernel in prefix mode
+    (at g = 8 the 6-sequence group's 48 rows take two 32-row tiles)."""
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=7, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=128,
+                                 ctx_range=(200, 600), shared_seqs=6, shared_tokens=160, seed=seed, fmt=1)
+    say(f"case: cascade MX-FP4 g={g} hkv={hkv} seed={seed} split={split}")
+    _run(Case(cfg), [([0, 1, 2, 3, 4, 5], 0, 4), ([0, 2, 4], 4, 10), ([6], 0, 3)])
+
+
 def test_context_ending_at_the_prefix_and_no_groups():
     cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(200, 400),
                                  shared_seqs=2, shared_tokens=192, seed=306)
@@ -128,3 +141,16 @@ def test_shared_range_longer_than_the_block_id_table_is_refused():
     assert tq_cascade_workspace_bytes(cache.handle, 2, 8, 16 * 4097, 1, 2, 4096, 1) > 0
     with pytest.raises(TqError):
         tq_cascade_workspace_bytes(cache.handle, 2, 8, 16 * 4097, 1, 2, 4097, 1)
+
+
+def test_mxfp4_shared_range_longer_than_one_work_group_is_refused():
+    """An MX-FP4 group's shared range is at most 256 blocks (its work-group's
+    four waves hold 64 block ids each); the host refuses longer ones before
+    any launch, and accepts exactly 256."""
+    from bit_quantized_kv_amd import Cache
+    from bit_quantized_kv_amd.binding import TqError, tq_cascade_workspace_bytes
+    cache = Cache(1, 128, 2, 16)
+    say("case: MX-FP4 cascade workspace query with 256 and 257 shared blocks")
+    assert tq_cascade_workspace_bytes(cache.handle, 2, 8, 16 * 257, 1, 2, 256, 1) > 0
+    with pytest.raises(TqError):
+        tq_cascade_workspace_bytes(cache.handle, 2, 8, 16 * 257, 1, 2, 257, 1)

@@ -1,5 +1,5 @@
-"""GPU parity of multi-token attention over the TQ4/4 and TQ4/2 caches (chunked
-prefill, verification) against the CPU oracle, through the C ABI: max over rows of
+"""GPU parity of multi-token attention over the TQ4/4, TQ4/2 and MX-FP4 caches
+(chunked prefill, verification) against the CPU oracle, through the C ABI: max over rows of
 ||o - o_ref||_inf / ||o_ref||_inf within 2e-3, rows computed by the oracle's
 exact fp64 causal attention over the same (byte-identical) cache."""
 import os
@@ -88,6 +88,41 @@ def test_two_bit_values(d, g, hkv, seed, m, split):
                                  ctx_range=(60, 700), seed=seed, fmt=2)
     say(f"case: multi-token TQ4/2 d={d} g={g} hkv={hkv} seed={seed} m={m} split={split}")
     _run(Case(cfg), np.array(m))
+
+
+@pytest.mark.parametrize("g,hkv,seed,m,split", [
+    (4, 2, 231, [3, 8, 1, 5, 8], None),       # at most 32 rows: one 32-row tile
+    (8, 1, 232, [2, 1, 2, 0, 2], None),       # at most 16 rows: one 16-row tile
+    (8, 1, 233, [8, 3, 5, 7, 1], 8),          # 64 rows: two 32-row tiles, 8-block splits
+    (4, 2, 234, [30, 12, 1, 25, 9], None),    # 120 rows: four row tiles
+    (1, 3, 235, [40, 3, 17, 1, 26], 5),       # g = 1, 40 rows, splits ending inside a wave's blocks
+    (2, 2, 236, [16, 4, 0, 1, 12], 3),        # 32 rows, a sequence without query tokens
+])
+def test_mxfp4(g, hkv, seed, m, split):
+    """MX-FP4 caches: the scaled-MFMA multi-token kernel with 16- and 32-row
+    tiles, several row tiles per (sequence, kv-head), split merges."""
+    if split:
+        os.environ["TQ_SPLIT_BLOCKS"] = str(split)
+    cfg = workloads.small_config(batch=5, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=128,
+                                 ctx_range=(60, 700), seed=seed, fmt=1)
+    say(f"case: multi-token MX-FP4 g={g} hkv={hkv} seed={seed} m={m} split={split}")
+    _run(Case(cfg), np.array(m))
+
+
+def test_mxfp4_whole_contexts_and_longest_split():
+    """MX-FP4: query tokens that are whole contexts (the first row sees one
+    key), then 256-block splits of 9000- to 12000-token contexts, where each
+    of a work-group's four waves walks 64 blocks (the most one wave-wide id
+    load holds)."""
+    cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(1, 40),
+                                 seed=237, fmt=1)
+    say("case: multi-token MX-FP4, whole short contexts")
+    _run(Case(cfg), np.array([10 ** 6, 10 ** 6, 3, 10 ** 6]))
+    os.environ["TQ_SPLIT_BLOCKS"] = "256"
+    cfg = workloads.small_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(9000, 12000),
+                                 seed=238, fmt=1)
+    say("case: multi-token MX-FP4 with 256-block splits")
+    _run(Case(cfg), 20)
 
 
 def test_prefill_from_the_first_token_and_empty_sequences():

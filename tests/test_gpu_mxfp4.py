@@ -115,18 +115,20 @@ def test_full_fp4_sampled():
     _check(Case(workloads.CONFIGS["fp4"]), seqs=[0, 77, 127], rows=[(b, h) for b in (0, 77, 127) for h in range(64)])
 
 
-def test_multi_token_and_cascade_refuse_mxfp4():
-    """Multi-token and cascade attention are built for the TQ4 formats; an
-    MX-FP4 cache is refused (status TQ_ERR_UNSUPPORTED) before any launch."""
-    from bit_quantized_kv_amd import Cache, TqError
-    from bit_quantized_kv_amd.binding import tq_cascade_workspace_bytes
-    cache = Cache(1, 128, 2, 4)
-    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
-    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
-    say("case: multi-token and cascade calls on an MX-FP4 cache")
-    with pytest.raises(TqError) as e:
-        cache.multitoken(q, i32([0, 1]), 1, i32([[0]]), i32([16]), 16, 0.1)
-    assert e.value.status == 2
-    with pytest.raises(TqError) as e:
-        tq_cascade_workspace_bytes(cache.handle, 1, 8, 16, 1, 1, 1, 1)
-    assert e.value.status == 2
+def test_one_query_token_multi_token_matches_decode():
+    """One query token per sequence through the MX-FP4 multi-token kernel
+    equals the MX-FP4 decode kernel up to summation order: both take the
+    logits from the same scaled MFMA and P as bf16 high + low parts."""
+    cfg = workloads.small_config(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(50, 900),
+                                 fmt=1, seed=141)
+    case = Case(cfg)
+    case.quantize(case.write_ranges())
+    w = case.w
+    qbits, q_start = w.multi_queries(1)
+    ctx = w.total_lens.astype(np.int32)
+    say("case: MX-FP4 multi-token with one query token per sequence against decode")
+    mt = case.cache.multitoken(to_dev_bf16(qbits), to_dev_i32(q_start), 1, case.table_dev, to_dev_i32(ctx),
+                               int(ctx.max()), cfg.scale)
+    dec = case.cache.decode(to_dev_bf16(qbits), case.table_dev, to_dev_i32(ctx), int(ctx.max()), cfg.scale)
+    torch.cuda.synchronize()
+    assert row_rel_err(mt.cpu().numpy(), dec.cpu().numpy()) <= 1e-4

@@ -85,8 +85,14 @@ MT_CONFIGS = {
     # a 512-token prefill chunk per sequence on top of a 25088-token cached prefix
     "prefill": Config("prefill", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, context=25600,
                       outliers=4, bias_std=0.5, seed=1008),
+    # the same two steps over an MX-FP4 cache
+    "verify_fp4": Config("verify_fp4", batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         ctx_range=(4096, 25600), shared_seqs=16, shared_tokens=24576,
+                         outliers=4, fmt=1, seed=1009),
+    "prefill_fp4": Config("prefill_fp4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, context=25600,
+                          outliers=4, fmt=1, seed=1010),
 }
-MT_QUERY_TOKENS = {"verify": 8, "prefill": 512}
+MT_QUERY_TOKENS = {"verify": 8, "prefill": 512, "verify_fp4": 8, "prefill_fp4": 512}
 
 
 def f32_to_bf16_bits(x):
