@@ -43,14 +43,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="agentic",
+    p.add_argument("--config", default="cascade",
                    choices=["llama8b", "agentic", "longprefix", "fp4", "tq4v2", "calib", "verify", "prefill",
                             "verify_fp4", "prefill_fp4", "agentic_fp4", "cascade_fp4",
                             "cascade"],
-                   help="calib: the calibrated key-table fit of a 32-layer stack; verify / prefill: multi-token "
-                        "attention over the cache; cascade: the agentic workload decoded with shared blocks "
-                        "read once per group; tq4v2: the llama8b shape with 2-bit values; *_fp4: the same workload over an "
-                        "MX-FP4 cache (each its own JSON line)")
+                   help="cascade (the default): the agentic workload, decoded with its shared prefix blocks read "
+                        "once per group of sequences (the per-sequence decode is timed beside it); agentic: the same "
+                        "workload with the per-sequence decode; calib: the calibrated key-table fit of a 32-layer "
+                        "stack; verify / prefill: multi-token attention over the cache; tq4v2: the llama8b shape "
+                        "with 2-bit values; *_fp4: the same workload over an MX-FP4 cache (each its own JSON line)")
     p.add_argument("--copies", type=int, default=0, help="rotating input/pool copies (0 = automatic)")
     p.add_argument("--cascade-group-blocks", type=int, default=48,
                    help="cascade: shared ranges are cut into groups of at most this many blocks")
@@ -195,9 +196,9 @@ class Bench:
         k, v = self.kv[i % self.in_copies]
         self.caches[i % self.pool_copies].quantize_append(k, v, self.slots)
 
-    def decode(self, i, s):
+    def decode(self, i, s, plain=False):
         c = self.cfg
-        if self.cascade is not None:
+        if self.cascade is not None and not plain:
             self.caches[i % self.pool_copies].cascade_decode(self.q[s], self.table, self.ctx[s], self.max_ctx[s],
                                                              c.scale, self.cascade, out=self.out)
             return
@@ -382,9 +383,13 @@ def traffic_from_profiles(cfg_name, kernel):
         if kernel == "multitoken":
             # the attention launch: the direct or staged kernel and its merge
             parts = [e for k, e in ents.items() if "multitoken" in k or "mt_direct" in k]
+        elif cfg_name.startswith("cascade"):
+            # the cascade launch: the own-token pass, the shared-block pass and
+            # their merge (not the per-sequence decode timed beside it)
+            parts = [e for k, e in ents.items()
+                     if "quantize_kernel" not in k and ("cascade_merge" in k or "true" in k.split("|")[0])]
         else:
-            # the decode launch: decode kernel and merge, and for cascade decode
-            # the shared-block pass too
+            # the decode launch: decode kernel and merge
             parts = [e for k, e in ents.items() if "quantize_kernel" not in k]
         return round(sum(hbm(e) for e in parts)) if parts else None
     except Exception:
@@ -781,6 +786,9 @@ def main():
     q_ms = timed_median(torch, stream, args.steps, lambda j: bench.quantize(base + j))
     nd = args.steps * c.decode_steps
     d_ms = timed_median(torch, stream, nd, lambda j: bench.decode(j, j % c.decode_steps))
+    # cascade: the per-sequence decode of the same pools, for comparison
+    p_ms = (timed_median(torch, stream, nd, lambda j: bench.decode(j, j % c.decode_steps, plain=True))
+            if cascade else None)
     # the single-token appends of the decode steps (one token per sequence), alone
     a_ms = (timed_median(torch, stream, nd, lambda j: bench.append(j, j % c.decode_steps)) if bench.appends else None)
 
@@ -832,6 +840,11 @@ def main():
         "roofline_other": roof("decode" if dominant == "quantize" else "quantize"),
         "kernel_source_hash": kernel_source_hash(),
     }
+    if p_ms is not None:
+        # the per-sequence decode over the same cache (every sharer reads the
+        # shared blocks itself)
+        res["plain_decode_us"] = round(p_ms * 1e3, 2)
+        res["plain_value"] = round(kv_logical / (p_ms * 1e-3) / 1e9, 1)
     if c.fmt == 1:
         # the FP4 decode's matrix-unit use (committed counters)
         res["decode_mfma_busy"] = mfma_busy_from_profiles(args.config, "tq::mxfp4_decode_kernel")

@@ -44,3 +44,21 @@ def test_traffic_is_dropped_when_the_sources_changed(tmp_path, monkeypatch):
     d["kernel_source_hash"] = "0" * 16
     (prof / "traffic.json").write_text(json.dumps(d))
     assert bench.traffic_from_profiles("llama8b", "quantize") is None
+
+
+def test_cascade_traffic_counts_the_cascade_launch_only(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    one = {"fetch_kib_per_dispatch": 1.0, "write_kib_per_dispatch": 0.0}
+    d = {"kernel_source_hash": bench.kernel_source_hash(), "fetch_scale": 1.0, "write_scale": 1.0,
+         "workloads": {"cascade": {"tq::tq4_quantize_kernel<128, 4, true>|262144": one,
+                                   "tq::tq4_decode_kernel<128, 4, true, 4>|917504": one,
+                                   "tq::tq4_mt_direct_kernel<128, 2, true, 4>|129024": one,
+                                   "tq::cascade_merge_kernel<128>|262144": one,
+                                   # the per-sequence decode timed beside the cascade
+                                   "tq::tq4_decode_kernel<128, 4, false, 4>|917504": one,
+                                   "tq::decode_merge_kernel<128>|262144": one}}}
+    (prof / "traffic.json").write_text(json.dumps(d))
+    monkeypatch.setattr(bench, "PROFILES", str(prof))
+    assert bench.traffic_from_profiles("cascade", "decode") == 3 * 1024
+    assert bench.traffic_from_profiles("cascade", "quantize") == 1024

@@ -36,4 +36,8 @@ def test_report_fields(config):
     assert r["bound"] in ("hbm", "mfma", "alu") and r["unit"] in ("GB/s", "TFLOP/s")
     assert 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     if config is None:
+        # the default: the agentic workload with the shared-prefix (cascade)
+        # decode, the per-sequence decode timed beside it
         assert d["unit"] == "GB/s" and d["config"]["workload"].startswith("agentic")
+        assert "cascade decode" in d["config"]["workload"]
+        assert d["plain_decode_us"] > 0 and d["plain_value"] > 0
