@@ -59,6 +59,9 @@ def parse():
                    help="cascade: groups are cut into groups of at most this many sequences "
                         "(default: 32 rows' worth, the direct kernel's tile)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ceilings", action="store_true",
+                   help="print the measured bandwidth ceilings of this GPU (stream read, record gather, copy, fill) "
+                        "and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for counter calibration)")
     return p.parse_args()
@@ -88,6 +91,68 @@ def kernel_source_hash():
         h.update(name.encode())
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def ceilings():
+    """Bandwidth ceilings of this GPU for the path's access patterns, from the
+    probe kernels of libtqprobe.so (no arithmetic on the data): a streaming
+    read of 4 GiB, and a gather of whole TQ4/4 records (2336 of every 2432
+    bytes, D = 128) of a 2 GiB pool in random order, the decode's pattern;
+    each the best over a few grid sizes of the median of five launches.  A
+    torch device copy and fill of 1 GiB are given beside them."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_kv_amd", "libtqprobe.so"))
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.tqprobe_stream_read.argtypes = [P, I64, P, I32, P]
+    lib.tqprobe_record_gather.argtypes = [P, P, I64, I64, I32, P, I32, P]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def med(fn, reps=5):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            assert rc == 0
+            out.append(a.elapsed_time(b) * 1e-3)
+        return sorted(out)[reps // 2]
+
+    res = {}
+    n = 4 << 30
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")   # equal words: every fold is 0
+    rates = {g: n / med(lambda g=g: lib.tqprobe_stream_read(buf.data_ptr(), n, sink.data_ptr(), g, sp)) / 1e9
+             for g in (2048, 4096, 8192, 16384, 32768)}
+    g_best = max(rates, key=rates.get)
+    res["stream_read_GBps"], res["stream_read_grid"] = round(rates[g_best], 1), g_best
+    del buf
+    from bit_quantized_kv_amd import Cache
+    stride = Cache(0, 128, 1, 1).record_bytes
+    rec = 16 * payload_row_bytes(0, 128)
+    nrec = (2 << 30) // stride
+    pool = torch.ones(nrec * stride // 4, dtype=torch.float32, device="cuda")
+    ids = torch.from_numpy(np.random.default_rng(7).permutation(nrec).astype(np.int32)).cuda()
+    rates = {g: nrec * rec / med(lambda g=g: lib.tqprobe_record_gather(pool.data_ptr(), ids.data_ptr(), nrec, stride,
+                                                                       rec, sink.data_ptr(), g, sp)) / 1e9
+             for g in (1024, 2048, 4096, 8192, 16384)}
+    g_best = max(rates, key=rates.get)
+    res["record_gather_GBps"], res["record_gather_grid"] = round(rates[g_best], 1), g_best
+    res["record_bytes"], res["record_stride"], res["records"] = rec, stride, nrec
+    del pool, ids
+    m = 1 << 30
+    a = torch.ones(m // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    res["torch_copy_GBps"] = round(2 * m / med(lambda: (b.copy_(a), 0)[1]) / 1e9, 1)
+    res["torch_fill_GBps"] = round(m / med(lambda: (b.fill_(2.0), 0)[1]) / 1e9, 1)
+    res["peak_GBps"] = HBM_PEAK_GBPS
+    print(json.dumps({"ceilings": res, "device": torch.cuda.get_device_name(0)}))
 
 
 def copy_calibration():
@@ -746,6 +811,9 @@ def main():
         print("bench.py measures one GPU only: there is no multi-GPU path "
               "(the decode shards by sequence or kv-head with no exchange).", file=sys.stderr)
         sys.exit(2)
+    if args.ceilings:
+        ceilings()
+        return
     if args.copy_calibration:
         copy_calibration()
         return

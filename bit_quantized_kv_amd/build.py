@@ -57,7 +57,24 @@ def build(verbose=False):
     if p.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
     shutil.move(tmp, OUT)
+    build_probe()
     return OUT
+
+
+PROBE_SRC = os.path.join(HERE, "probe", "ceiling.hip")
+PROBE_OUT = os.path.join(HERE, "libtqprobe.so")
+
+
+def build_probe():
+    """The bench's bandwidth probes (stream read, record gather), a library of
+    their own: no entry point of libtq.so uses them."""
+    tmp = PROBE_OUT + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", "-x", "hip", PROBE_SRC, "-o", tmp]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
+    shutil.move(tmp, PROBE_OUT)
+    return PROBE_OUT
 
 
 if __name__ == "__main__":
