@@ -96,10 +96,13 @@ def kernel_source_hash():
 def ceilings():
     """Bandwidth ceilings of this GPU for the path's access patterns, from the
     probe kernels of libtqprobe.so (no arithmetic on the data): a streaming
-    read of 4 GiB, and a gather of whole TQ4/4 records (2336 of every 2432
-    bytes, D = 128) of a 2 GiB pool in random order, the decode's pattern;
-    each the best over a few grid sizes of the median of five launches.  A
-    torch device copy and fill of 1 GiB are given beside them."""
+    read of 4 GiB, a gather of whole TQ4/4 records (2336 of every 2432 bytes,
+    D = 128) of a 2 GiB pool in random order, the decode's pattern,
+    and the quantize's mix of traffic (7 words read, 2 written per item; 1.1 GB
+    read per launch), its output written in order or as 2 KB pieces at
+    scattered places; each the best over a few grid sizes of the median of
+    five launches.  A torch device copy and fill of 1 GiB are given beside
+    them."""
     import ctypes
 
     import torch
@@ -107,6 +110,7 @@ def ceilings():
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.tqprobe_stream_read.argtypes = [P, I64, P, I32, P]
     lib.tqprobe_record_gather.argtypes = [P, P, I64, I64, I32, P, I32, P]
+    lib.tqprobe_mixed_stream.argtypes = [P, P, P, I64, I32, P]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
@@ -146,6 +150,21 @@ def ceilings():
     res["record_gather_GBps"], res["record_gather_grid"] = round(rates[g_best], 1), g_best
     res["record_bytes"], res["record_stride"], res["records"] = rec, stride, nrec
     del pool, ids
+    # the quantize's 7 : 2 mix: 1.1 GB read and 0.31 GB written per launch
+    chunks = (1100 << 20) // (7 * 1024)
+    src = torch.ones(chunks * 7 * 256, dtype=torch.float32, device="cuda")
+    dst = torch.empty(chunks * 2 * 256, dtype=torch.float32, device="cuda")
+    moved = chunks * 9 * 1024
+    perm = torch.from_numpy(np.random.default_rng(8).permutation(chunks).astype(np.int32)).cuda()
+    for key, pp in (("mixed_7r2w", None), ("mixed_7r2w_scattered", perm)):
+        pptr = pp.data_ptr() if pp is not None else None
+        rates = {g: moved / med(lambda g=g: lib.tqprobe_mixed_stream(src.data_ptr(), dst.data_ptr(), pptr, chunks, g,
+                                                                     sp)) / 1e9
+                 for g in (2048, 4096, 8192, 16384)}
+        g_best = max(rates, key=rates.get)
+        res[key + "_GBps"], res[key + "_grid"] = round(rates[g_best], 1), g_best
+    res["mixed_7r2w_bytes"] = moved
+    del src, dst, perm
     m = 1 << 30
     a = torch.ones(m // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)

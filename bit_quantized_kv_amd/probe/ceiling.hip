@@ -1,6 +1,7 @@
-// Measurement probes for bench.py: how fast this GPU streams plain reads and
-// how fast it gathers whole records at random positions (the decode's access
-// pattern), with no arithmetic on the data.  Built into libtqprobe.so beside
+// Measurement probes for bench.py: how fast this GPU streams plain reads, how
+// fast it gathers whole records at random positions (the decode's access
+// pattern) and how fast it streams the quantize's mix of reads and writes,
+// with no arithmetic on the data beyond folding the words read.  Built into libtqprobe.so beside
 // the library; no entry point of libtq.so uses it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -53,9 +54,49 @@ __global__ __launch_bounds__(256) void record_gather_kernel(const uint8_t *pool,
   if (acc == kNever) sink[0] = acc;
 }
 
+// The quantize's mix of HBM traffic: per item 7 16-byte words read and 2
+// written (its 78 : 22 split of read and written bytes).  Wave w takes chunks
+// of 64 items: lane l reads words j * 64 + l (j < 7) of the chunk and writes
+// the folds of its words 0-3 and 4-6 to words l and 64 + l of the chunk's
+// output, so that every load and store is coalesced and every store depends on
+// loads.  With `perm`, chunk c's output goes to output chunk perm[c] (a
+// permutation): whole 2 KB pieces written at scattered places, as the
+// quantize writes its records into the paged pool.
+__device__ __forceinline__ uint4 xor4(uint4 a, uint4 b) {
+  return make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w);
+}
+__global__ __launch_bounds__(256) void mixed_stream_kernel(const uint4 *src, uint4 *dst, const int32_t *perm,
+                                                           int64_t chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t c = wave; c < chunks; c += nwaves) {
+    const uint4 *s = src + c * (7 * 64) + lane;
+    uint4 a[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) a[j] = s[j * 64];
+    uint4 *d = dst + (perm ? (int64_t)perm[c] : c) * (2 * 64) + lane;
+    d[0] = xor4(xor4(a[0], a[1]), xor4(a[2], a[3]));
+    d[64] = xor4(xor4(a[4], a[5]), a[6]);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads 7 * 1024 * chunks bytes of `src` and writes 2 * 1024 * chunks bytes of
+// `dst` (chunks of 64 items of 7 read and 2 written 16-byte words), with
+// `grid` work-groups of 256 threads, on `stream`.  `perm`: NULL (chunk c
+// writes output chunk c), or a device int32 permutation of [0, chunks) (the
+// caller's; not checked).  Returns as tqprobe_stream_read.
+int tqprobe_mixed_stream(const void *src, void *dst, const int32_t *perm, int64_t chunks, int grid,
+                         void *stream) {
+  if (!src || !dst || chunks <= 0 || grid < 1) return 1;
+  hipLaunchKernelGGL(mixed_stream_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), perm, chunks);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Reads `bytes` bytes (a multiple of 16) of device buffer `buf` once, with
 // `grid` work-groups of 256 threads, on `stream`.  `sink`: one device word,
