@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--ceilings", action="store_true",
                    help="print the measured bandwidth ceilings of this GPU (stream read, record gather, copy, fill) "
                         "and exit")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="leave the measured bandwidth ceilings out of the line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for counter calibration)")
     return p.parse_args()
@@ -94,6 +96,11 @@ def kernel_source_hash():
 
 
 def ceilings():
+    import torch
+    print(json.dumps({"ceilings": measure_ceilings(), "device": torch.cuda.get_device_name(0)}))
+
+
+def measure_ceilings():
     """Bandwidth ceilings of this GPU for the path's access patterns, from the
     probe kernels of libtqprobe.so (no arithmetic on the data): a streaming
     read of 4 GiB, a gather of whole TQ4/4 records (2336 of every 2432 bytes,
@@ -171,7 +178,9 @@ def ceilings():
     res["torch_copy_GBps"] = round(2 * m / med(lambda: (b.copy_(a), 0)[1]) / 1e9, 1)
     res["torch_fill_GBps"] = round(m / med(lambda: (b.fill_(2.0), 0)[1]) / 1e9, 1)
     res["peak_GBps"] = HBM_PEAK_GBPS
-    print(json.dumps({"ceilings": res, "device": torch.cuda.get_device_name(0)}))
+    del a, b, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration():
@@ -938,6 +947,18 @@ def main():
     if a_ms is not None:
         res["append_1tok_us"] = round(a_ms * 1e3, 2)
         res["append_1tok_GBps"] = round(bench.append_bytes() / (a_ms * 1e-3) / 1e9, 1)
+    if not args.no_ceilings and os.path.exists(os.path.join(ROOT, "bit_quantized_kv_amd", "libtqprobe.so")):
+        # this GPU's measured ceilings for the two kernels' access patterns,
+        # taken after the timed regions, and where the kernels stand against them
+        try:
+            ceil = measure_ceilings()
+            q_rate = bench.quantize_bytes() / (q_ms * 1e-3) / 1e9
+            d_rate = kv_unique / (d_ms * 1e-3) / 1e9
+            ceil["quantize_frac_of_mixed_scattered"] = round(q_rate / ceil["mixed_7r2w_scattered_GBps"], 4)
+            ceil["decode_unique_frac_of_record_gather"] = round(d_rate / ceil["record_gather_GBps"], 4)
+            res["ceilings"] = ceil
+        except Exception as e:  # the probes are context, not the measurement
+            res["ceilings"] = {"error": str(e)[:200]}
     if cpu is not None:
         res["cpu_baseline"] = cpu
         if "near_ties" in cpu:

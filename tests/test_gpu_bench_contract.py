@@ -41,3 +41,10 @@ def test_report_fields(config):
         assert d["unit"] == "GB/s" and d["config"]["workload"].startswith("agentic")
         assert "cascade decode" in d["config"]["workload"]
         assert d["plain_decode_us"] > 0 and d["plain_value"] > 0
+        # the measured ceilings of the same GPU and where the kernels stand
+        c = d["ceilings"]
+        assert "error" not in c, c
+        for k in ("stream_read_GBps", "record_gather_GBps", "mixed_7r2w_GBps", "mixed_7r2w_scattered_GBps"):
+            assert 0 < c[k] < c["peak_GBps"], k
+        assert 0 < c["quantize_frac_of_mixed_scattered"] < 1.5
+        assert 0 < c["decode_unique_frac_of_record_gather"] < 1.5
